@@ -1,0 +1,134 @@
+/*
+ * qr.h -- C ABI of the MI355X (gfx950) quantized-actor W8A8 linear library, libqr.so.
+ *
+ * The layer that quantized rollout runs at every decode step, from the pages
+ *   [QuRL] "QuRL: Efficient Reinforcement Learning with Quantized Rollout"
+ *   [QaRL] "QaRL: Rollout-Aligned Quantization-Aware RL for Fast and Stable Training under Training-Inference
+ *          Mismatch"
+ * in four calls: weight quantization (once per RL step, [QuRL] section 4), per-token activation
+ * quantization, the W8A8 linear with its dequantization epilogue, and a grouped variant for MoE experts
+ * ([QuRL] section 5; [QaRL] sections 2.2 and 3.1).
+ *
+ * Common contract
+ *  - Layouts: W[n,k], X[m,k], Y[m,n] row-major with the last index contiguous. Codes are one byte per element:
+ *    INT8 two's complement, or the OCP E4M3FN bit pattern for FP8. Scales are fp32, one per row of the
+ *    quantized tensor. Codes and scales are a canonical, bit-exact format ([QaRL] 3.1: the learner publishes
+ *    the low-bit tensors themselves to the inference engine), so no call reorders or pre-shuffles them.
+ *  - Pointers are device pointers unless stated otherwise. The caller owns every buffer; the library keeps no
+ *    pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call only enqueues work on it
+ *    and never synchronizes; device faults surface at the caller's next synchronization.
+ *  - k must be a positive multiple of 16; code and activation pointers must be 16-byte aligned; scale
+ *    pointers 4-byte aligned; y and accumulator outputs 16-byte aligned.
+ *  - m == 0, n == 0 or total_rows == 0: QR_OK, nothing is launched.
+ *  - Arguments are validated on the host before anything is launched; a failed check returns its status
+ *    and qr_last_error() (thread-local) explains it. A failed launch returns QR_ERR_HIP with the HIP error
+ *    text. Inputs must be finite (NaN/Inf give unspecified codes).
+ *  - Calls on different streams must not share a workspace buffer.
+ */
+#ifndef QR_H
+#define QR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qr_status {
+    QR_OK = 0,
+    QR_ERR_ARG = 1,         /* null pointer, negative or inconsistent size, bad enum          */
+    QR_ERR_UNSUPPORTED = 2, /* k not a multiple of 16, or a size beyond the supported range     */
+    QR_ERR_ALIGN = 3,       /* pointer alignment                                                */
+    QR_ERR_WORKSPACE = 4,   /* workspace missing or smaller than qr_workspace_bytes()           */
+    QR_ERR_HIP = 5          /* the HIP runtime refused a launch                                 */
+} qr_status;
+
+typedef enum qr_dtype { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
+
+/* INT8: symmetric, codes in [-127, 127], scale = max|row| / 127.
+ * FP8:  E4M3FN (bias 7, largest finite 448, no infinity), scale = max|row| / 448. */
+typedef enum qr_qtype { QR_INT8 = 0, QR_FP8_E4M3 = 1 } qr_qtype;
+
+/*
+ * Weight quantization, one scale per output channel ([QuRL] 5: channel-wise weight scales; [QaRL] 2.2: the
+ * integer and floating-point Quant equations with zero point 0 and s = max|W| / alpha; [QuRL] 4.3: the
+ * invariant scaling W X = (W / s)(s X), here with the per-input-channel vector folded as W diag(s)).
+ *
+ * For every row r of w[n,k] (fp32 or bfloat16, selected by w_type):
+ *   w'_j = w[r,j] * s[j] rounded to fp32 (or w[r,j] when s == NULL)
+ *   S    = max_j |w'_j| / qmax rounded to fp32 (S = 1 for an all-zero row), qmax = 127 or 448
+ *   code = INT8: round-half-even(clamp(w'_j / S, -127, 127)); FP8: E4M3 nearest-even of clamp(w'_j / S, +-448)
+ * with IEEE fp32 division and the sign of zero kept in FP8 (a negative value that rounds to 0 gives 0x80).
+ * Writes w_codes[n,k] and w_scales[n]. s: device fp32 [k] or NULL.
+ */
+qr_status qr_quantize_weights(const void *w, qr_dtype w_type, int64_t n, int64_t k, const float *s, qr_qtype q,
+                              void *w_codes, float *w_scales, void *stream);
+
+/*
+ * Per-token dynamic activation quantization ([QuRL] 5: token-wise activation scales). Identical to
+ * qr_quantize_weights row by row, with x'_j = x[r,j] * (1 / s[j]) (the reciprocal rounded to fp32 first,
+ * then the product rounded to fp32), the X diag(1/s) side of the invariant scaling of [QuRL] 4.3.
+ * Writes x_codes[m,k] and x_scales[m].
+ */
+qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k, const float *s, qr_qtype q,
+                           void *x_codes, float *x_scales, void *stream);
+
+/*
+ * W8A8 linear with dequantization epilogue ([QuRL] 5 and [QaRL] 3.1: W8A8 rollout; [QaRL] 2.2 Dequant):
+ *   acc[i,c] = sum_j xq[i,j] * wq[c,j]   (INT8: exact int32; FP8: fp32 accumulation of exact products)
+ *   y[i,c]   = acc[i,c] * x_scales[i] * w_scales[c], stored as y_type (bfloat16 rounded to nearest even).
+ * acc_out: optional [m,n] int32 (INT8) or fp32 (FP8) copy of the accumulators, or NULL.
+ * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes (NULL allowed when that is
+ * 0). It must be zero-filled before its first use; every completed call leaves it zero-filled again.
+ * INT8 results are bitwise independent of m (row i depends only on row i of the inputs) and deterministic;
+ * FP8 results are deterministic for a given (m, n, k).
+ * Limits: k <= 131072 (INT8 accumulators stay below 2^31).
+ */
+qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes, const float *x_scales,
+                         const void *w_codes, const float *w_scales, void *y, qr_dtype y_type, void *acc_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped (MoE) W8A8 linear over per-expert token lists (the expert FFNs of the Qwen3-30B-A3B model in the
+ * [QaRL] abstract, run in W8A8 as in [QaRL] 3.1). Output rows are grouped by expert in CSR form:
+ *   for e in [0, num_experts), j in [expert_offsets[e], expert_offsets[e+1]):
+ *     r = row_ids ? row_ids[j] : j;    y[j,:] = (x_codes[r,:] . w_codes[e]^T) * x_scales[r] * w_scales[e,:]
+ * expert_offsets: device int32 [num_experts+1], non-decreasing, expert_offsets[0] == 0,
+ *                 expert_offsets[num_experts] == total_rows (the host passes total_rows).
+ * row_ids: device int32 [total_rows] with values in [0, x_rows), or NULL for the identity.
+ * w_codes: [num_experts, n, k]; w_scales: [num_experts, n]; y: [total_rows, n].
+ * The device trusts the token lists; out-of-range rows are skipped, never read.
+ * workspace: as for qr_w8a8_linear, qr_workspace_bytes(q, total_rows, n, k, num_experts) bytes.
+ */
+qr_status qr_w8a8_grouped_linear(qr_qtype q, int64_t num_experts, int64_t n, int64_t k,
+                                 const int32_t *expert_offsets, const int32_t *row_ids, int64_t total_rows,
+                                 int64_t x_rows, const void *x_codes, const float *x_scales, const void *w_codes,
+                                 const float *w_scales, void *y, qr_dtype y_type, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
+ * Changed-code count between two published code sets of the same tensor ([QuRL] 4.3: weight updates between
+ * RL steps are much smaller than the quantization error, so most codes do not change).
+ *   out3[0] = #{i : a[i] != b[i]}                         (bytes)
+ *   out3[1] = #{i : value(a[i]) != value(b[i])}           (FP8 +0 and -0 are one value)
+ *   out3[2] = #{r : bits(sa[r]) != bits(sb[r])}           (scales; sa/sb may be NULL with n_scales == 0)
+ * out3: device int64 [3], overwritten. a, b: device codes [count], 16-byte aligned.
+ */
+qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_qtype q, const float *sa,
+                                const float *sb, int64_t n_scales, int64_t *out3, void *stream);
+
+/* Device bytes of workspace a linear (num_experts == 1, m rows) or grouped call (m = total_rows) needs. */
+size_t qr_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k, int64_t num_experts);
+
+/* Text of the last error on the calling thread ("" when none). */
+const char *qr_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *qr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QR_H */

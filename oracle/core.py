@@ -1,0 +1,169 @@
+"""ctypes wrapper of the C oracle ``libqr_oracle.so`` (test infrastructure only).
+
+Arrays are numpy: bfloat16 data travels as ``uint16`` bit patterns, codes as ``uint8`` (INT8 codes are the
+two's-complement bytes), scales as ``float32``. Functions allocate and return their outputs.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+INT8, FP8 = 0, 1
+S_NONE, S_MUL, S_MUL_RECIP = 0, 1, 2
+QMAX = {INT8: 127.0, FP8: 448.0}
+
+_lib = None
+
+
+def lib():
+    """Load (building first if needed) the oracle library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build_oracle()
+        L = ctypes.CDLL(_build.LIB)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.or_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.or_bf16_to_f32.restype = ctypes.c_float
+        L.or_rne.argtypes = [ctypes.c_double]
+        L.or_rne.restype = ctypes.c_double
+        L.or_e4m3_encode.argtypes = [ctypes.c_float]
+        L.or_e4m3_encode.restype = ctypes.c_uint8
+        L.or_e4m3_encode_search.argtypes = [ctypes.c_float]
+        L.or_e4m3_encode_search.restype = ctypes.c_uint8
+        L.or_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.or_e4m3_decode.restype = ctypes.c_double
+        L.or_e4m3_decode_units.argtypes = [ctypes.c_uint8]
+        L.or_e4m3_decode_units.restype = ctypes.c_int32
+        L.or_round_to_bf16.argtypes = [ctypes.c_double]
+        L.or_round_to_bf16.restype = ctypes.c_uint16
+        L.or_e4m3_encode_array.argtypes = [vp, i64, vp]
+        L.or_e4m3_encode_array.restype = None
+        L.or_e4m3_encode_search_array.argtypes = [vp, i64, vp]
+        L.or_e4m3_encode_search_array.restype = None
+        L.or_quantize_rows.argtypes = [vp, i32, i64, i64, vp, i32, i32, vp, vp]
+        L.or_quantize_rows.restype = None
+        L.or_linear.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.or_linear.restype = ctypes.c_int
+        L.or_grouped_linear.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp, vp, i32, vp]
+        L.or_grouped_linear.restype = ctypes.c_int
+        L.or_count_code_changes.argtypes = [vp, vp, i64, i32, vp, vp, i64, vp]
+        L.or_count_code_changes.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def e4m3_encode(v):
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().or_e4m3_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_encode_search(v):
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().or_e4m3_encode_search_array(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_decode(codes):
+    L = lib()
+    return np.array([L.or_e4m3_decode(int(c)) for c in np.asarray(codes, np.uint8).ravel()],
+                    np.float64).reshape(np.shape(codes))
+
+
+def e4m3_decode_units(codes):
+    L = lib()
+    return np.array([L.or_e4m3_decode_units(int(c)) for c in np.asarray(codes, np.uint8).ravel()],
+                    np.int64).reshape(np.shape(codes))
+
+
+def rne(x):
+    return lib().or_rne(float(x))
+
+
+def round_to_bf16(x):
+    return lib().or_round_to_bf16(float(x))
+
+
+def bf16_to_f32(bits):
+    bits = np.asarray(bits, np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_rows(x, qtype, s=None, s_mode=None, in_type=None):
+    """Per-row absmax quantization. ``x``: [rows, k] float32, or uint16 bfloat16 bits.
+    ``s_mode`` defaults to S_MUL when ``s`` is given (weights); pass S_MUL_RECIP for activations."""
+    if in_type is None:
+        in_type = BF16 if np.asarray(x).dtype == np.uint16 else F32
+    x = _c(x, np.uint16 if in_type == BF16 else np.float32)
+    rows, k = x.shape
+    if s is None:
+        s_mode = S_NONE
+    else:
+        s = _c(s, np.float32)
+        assert s.shape == (k,)
+        if s_mode is None:
+            s_mode = S_MUL
+    codes = np.empty((rows, k), np.uint8)
+    scales = np.empty((rows,), np.float32)
+    lib().or_quantize_rows(_p(x), in_type, rows, k, _p(s), s_mode, qtype, _p(codes), _p(scales))
+    return codes, scales
+
+
+def linear(qtype, x_codes, x_scales, w_codes, w_scales, y_type=BF16):
+    """Returns (y, acc_i32 or None, acc_f64). y is uint16 bfloat16 bits or float32."""
+    x_codes, w_codes = _c(x_codes, np.uint8), _c(w_codes, np.uint8)
+    x_scales, w_scales = _c(x_scales, np.float32), _c(w_scales, np.float32)
+    m, k = x_codes.shape
+    n, k2 = w_codes.shape
+    assert k == k2
+    y = np.empty((m, n), np.uint16 if y_type == BF16 else np.float32)
+    acc_i32 = np.empty((m, n), np.int32) if qtype == INT8 else None
+    acc_f64 = np.empty((m, n), np.float64)
+    rc = lib().or_linear(qtype, m, n, k, _p(x_codes), _p(x_scales), _p(w_codes), _p(w_scales), y_type,
+                         _p(y), _p(acc_i32), _p(acc_f64))
+    if rc != 0:
+        raise ValueError("oracle linear: k too large for exact accumulation")
+    return y, acc_i32, acc_f64
+
+
+def grouped_linear(qtype, expert_offsets, row_ids, x_codes, x_scales, w_codes, w_scales, y_type=BF16):
+    x_codes, w_codes = _c(x_codes, np.uint8), _c(w_codes, np.uint8)
+    x_scales, w_scales = _c(x_scales, np.float32), _c(w_scales, np.float32)
+    expert_offsets = _c(expert_offsets, np.int32)
+    row_ids = None if row_ids is None else _c(row_ids, np.int32)
+    x_rows, k = x_codes.shape
+    E, n, k2 = w_codes.shape
+    assert k == k2 and expert_offsets.shape == (E + 1,)
+    total = int(expert_offsets[-1])
+    y = np.zeros((total, n), np.uint16 if y_type == BF16 else np.float32)
+    rc = lib().or_grouped_linear(qtype, E, n, k, _p(expert_offsets), _p(row_ids), x_rows, _p(x_codes),
+                                 _p(x_scales), _p(w_codes), _p(w_scales), y_type, _p(y))
+    if rc != 0:
+        raise ValueError("oracle grouped linear: inconsistent token lists")
+    return y
+
+
+def count_code_changes(a, b, qtype, sa=None, sb=None):
+    a, b = _c(a, np.uint8), _c(b, np.uint8)
+    assert a.size == b.size
+    ns = 0
+    if sa is not None:
+        sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+        ns = sa.size
+    out = np.zeros(3, np.int64)
+    lib().or_count_code_changes(_p(a), _p(b), a.size, qtype, _p(sa), _p(sb), ns, _p(out))
+    return out

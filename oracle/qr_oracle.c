@@ -1,0 +1,324 @@
+/*
+ * qr_oracle.c -- plain, slow CPU oracle for the quantized-actor W8A8 linear.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test-suite, the smoke check and the benchmark's CPU-baseline leg,
+ * never by the product path. Scalar loops, no intrinsics, single-threaded, built with -O2 -ffp-contract=off
+ * and no fast-math so that every fp32 operation below is one IEEE binary32 operation with round-to-nearest-
+ * even (x86-64 SSE arithmetic, FLT_EVAL_METHOD == 0).
+ *
+ * Page references are given as [QuRL] / [QaRL] plus the section or equation; see qr_oracle.h for the titles.
+ *
+ * Precision choices:
+ *  - every floating-point step that decides an integer code or produces a published scale (the invariant-
+ *    scale product, the absmax scale, the division by the scale) is done in fp32, the precision of the
+ *    kernels, so that codes and scales can be compared bit for bit;
+ *  - accumulators are exact (64-bit integers);
+ *  - the dequantized output is computed in fp64 from the exact accumulator and rounded once to fp32 or
+ *    bfloat16.
+ */
+#include "qr_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------------------------------------
+ * Codecs
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* bfloat16 is the upper half of an fp32 bit pattern, so widening is exact. */
+float or_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round to the nearest integer, halfway cases to the even neighbour ([QaRL] 2.2 writes the rounding as
+ * the nearest-integer bracket; the tie rule is not stated, ties-to-even is the IEEE default). Inputs come
+ * from fp32 values, so x - floor(x) is exact in double. */
+double or_rne(double x) {
+    double f = floor(x);
+    double d = x - f;
+    if (d > 0.5) return f + 1.0;
+    if (d < 0.5) return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* [QuRL] 3, Eq. (2): a floating-point code is (-1)^sign * 2^d * (1 + sum_i m_i / 2^i); with b = 8 bits and
+ * e = 4 exponent bits there are 3 mantissa bits. The FP8 variant is OCP E4M3FN: exponent bias 7, exponent
+ * field 0 holds the subnormals 2^-6 * F/8, no infinity, and S.1111.111 is NaN, so the largest finite
+ * magnitude is 2^8 * 1.75 = 448 -- the alpha of the FP8 absmax scale max|w| / 448. */
+double or_e4m3_decode(uint8_t c) {
+    int sgn = (c >> 7) & 1;
+    int E = (c >> 3) & 15;
+    int F = c & 7;
+    double mag;
+    if (E == 15 && F == 7) return NAN;
+    if (E == 0)
+        mag = ldexp((double)F / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)F / 8.0, E - 7);
+    return sgn ? -mag : mag;
+}
+
+/* Every finite E4M3 value is an integer multiple of the smallest subnormal 2^-9. */
+int32_t or_e4m3_decode_units(uint8_t c) {
+    int sgn = (c >> 7) & 1;
+    int E = (c >> 3) & 15;
+    int F = c & 7;
+    int32_t mag;
+    if (E == 0)
+        mag = F;                       /* F/8 * 2^-6 = F * 2^-9 */
+    else
+        mag = (8 + F) << (E - 1);      /* (1 + F/8) * 2^(E-7) = (8+F) * 2^(E-10) = (8+F) * 2^(E-1) * 2^-9 */
+    return sgn ? -mag : mag;
+}
+
+/* [QaRL] 2.2, W_q = [W / s]_FPk: the nearest value of the E4M3 set, ties to the even mantissa, sign kept
+ * (a negative value that rounds to zero gives the -0 code 0x80). Requires finite |v| <= 448 (the caller
+ * clamps). Arithmetic form: split |v| into exponent and significand and round the significand to 3 bits. */
+uint8_t or_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    int e;
+    double m, frac, r;
+    int d;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9; rounding up to 8 units gives 0x08, the smallest normal */
+        r = or_rne(a * 512.0);
+        return (uint8_t)(sign | (uint8_t)r);
+    }
+    m = frexp(a, &e);            /* a = m * 2^e, m in [0.5, 1) */
+    d = e - 1;                   /* a = (2m) * 2^d, 2m in [1, 2) */
+    frac = (2.0 * m - 1.0) * 8.0;
+    r = or_rne(frac);
+    if (r == 8.0) {              /* significand rounded up to the next binade */
+        d += 1;
+        r = 0.0;
+    }
+    return (uint8_t)(sign | (uint8_t)(((d + 7) << 3) | (int)r));
+}
+
+/* The same encoder written a second, independent way: search the 127 non-negative finite magnitudes
+ * (codes 0x00..0x7E, which decode in increasing order) for the two neighbours of |v| and take the nearer,
+ * the even code on a tie. */
+uint8_t or_e4m3_encode_search(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    int lo = 0, hi = 126;
+    double dl, dh;
+    if (a >= or_e4m3_decode(126)) return (uint8_t)(sign | 126);
+    /* invariant: decode(lo) <= a < decode(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (or_e4m3_decode((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    dl = a - or_e4m3_decode((uint8_t)lo);
+    dh = or_e4m3_decode((uint8_t)hi) - a;
+    if (dl < dh) return (uint8_t)(sign | lo);
+    if (dh < dl) return (uint8_t)(sign | hi);
+    return (uint8_t)(sign | ((lo % 2 == 0) ? lo : hi));
+}
+
+void or_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = or_e4m3_encode(v[i]);
+}
+
+void or_e4m3_encode_search_array(const float *v, int64_t n, uint8_t *out) {
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = or_e4m3_encode_search(v[i]);
+}
+
+/* One rounding from double to bfloat16 (8 significant bits), ties to even. Output values of the path are
+ * far from the bfloat16 overflow and subnormal ranges; both are handled plainly anyway. */
+uint16_t or_round_to_bf16(double v) {
+    int e;
+    double m, r;
+    float f;
+    uint32_t u;
+    if (v == 0.0 || isnan(v) || isinf(v)) {
+        f = (float)v;
+        memcpy(&u, &f, sizeof u);
+        return (uint16_t)(u >> 16);
+    }
+    m = frexp(fabs(v), &e);      /* |v| = m * 2^e, m in [0.5, 1): 8 significant bits have quantum 2^(e-8) */
+    (void)m;
+    if (e < -125) e = -125;      /* below the normal range (|v| < 2^-126) the quantum stays 2^-133 */
+    r = or_rne(ldexp(fabs(v), 8 - e));
+    r = ldexp(r, e - 8);
+    if (r > 3.3895313892515355e38) r = INFINITY;
+    f = (float)(v < 0 ? -r : r); /* exact: r has at most 8 significant bits */
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------------------------------------------
+ * a1 / a2: per-row absmax quantization
+ * ---------------------------------------------------------------------------------------------------- */
+
+static float or_load(const void *in, int in_type, int64_t idx) {
+    if (in_type == OR_BF16) return or_bf16_to_f32(((const uint16_t *)in)[idx]);
+    return ((const float *)in)[idx];
+}
+
+/* For every row independently ([QuRL] 5: weight scales per output channel, activation scales per token):
+ *  1. w'_k = w_k, or fl32(w_k * s_k) for W diag(s), or fl32(w_k * fl32(1/s_k)) for X diag(1/s)
+ *     ([QuRL] 4.3, invariant scaling);
+ *  2. a = max_k |w'_k|;
+ *  3. S = fl32(a / qmax), qmax = 127 (INT8) or 448 (FP8) ([QaRL] 2.2, s = max|W| / alpha); an all-zero row
+ *     gets S = 1 so that its codes are all zero;
+ *  4. v_k = fl32(w'_k / S) (IEEE division);
+ *  5. INT8: q = round-to-nearest-even of v clamped to [-127, 127] ([QaRL] 2.2 integer Quant with z = 0);
+ *     FP8: q = E4M3 encoding of v clamped to [-448, 448] ([QaRL] 2.2 floating-point Quant). */
+void or_quantize_rows(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int s_mode,
+                      int qtype, uint8_t *codes, float *scales) {
+    int64_t r, j;
+    const float qmax = (qtype == OR_INT8) ? 127.0f : 448.0f;
+    float *wp = (float *)malloc((size_t)(k > 0 ? k : 1) * sizeof(float));
+    if (!wp) abort();
+    for (r = 0; r < rows; ++r) {
+        float a = 0.0f;
+        float S;
+        for (j = 0; j < k; ++j) {
+            float w = or_load(in, in_type, r * k + j);
+            if (s_mode == OR_S_MUL) {
+                w = w * s[j];
+            } else if (s_mode == OR_S_MUL_RECIP) {
+                float rs = 1.0f / s[j];
+                w = w * rs;
+            }
+            wp[j] = w;
+            if (fabsf(w) > a) a = fabsf(w);
+        }
+        S = (a > 0.0f) ? a / qmax : 1.0f;
+        scales[r] = S;
+        for (j = 0; j < k; ++j) {
+            float v = wp[j] / S;
+            if (v > qmax) v = qmax;
+            if (v < -qmax) v = -qmax;
+            if (qtype == OR_INT8) {
+                int q = (int)or_rne((double)v);
+                codes[r * k + j] = (uint8_t)(int8_t)q;
+            } else {
+                codes[r * k + j] = or_e4m3_encode(v);
+            }
+        }
+    }
+    free(wp);
+}
+
+/* ------------------------------------------------------------------------------------------------------
+ * a3: W8A8 linear with dequant epilogue
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* Exact dot product of one activation row and one weight row. INT8: the plain integer sum. FP8: each code
+ * is an integer number of 2^-9 units, so the product of two codes is an integer number of 2^-18 units and
+ * the whole sum is exact in 64-bit integers (|sum| <= k * 229376^2 < 2^63). Returns the count in units. */
+static int64_t or_dot_units(int qtype, const uint8_t *xr, const uint8_t *wr, int64_t k) {
+    int64_t acc = 0, j;
+    if (qtype == OR_INT8) {
+        for (j = 0; j < k; ++j) acc += (int64_t)(int8_t)xr[j] * (int64_t)(int8_t)wr[j];
+    } else {
+        for (j = 0; j < k; ++j)
+            acc += (int64_t)or_e4m3_decode_units(xr[j]) * (int64_t)or_e4m3_decode_units(wr[j]);
+    }
+    return acc;
+}
+
+static void or_store_y(int y_type, void *y, int64_t idx, double v) {
+    if (y_type == OR_BF16)
+        ((uint16_t *)y)[idx] = or_round_to_bf16(v);
+    else
+        ((float *)y)[idx] = (float)v;
+}
+
+/* Y[m,n] = acc[m,n] * S_x[m] * S_w[n]: the dequantization of [QaRL] 2.2 (W_hat = s * W_q) applied to both
+ * operands of the product, with one activation scale per token and one weight scale per output channel
+ * ([QuRL] 5). Returns 0, or -1 when the sizes could overflow the exact accumulators. */
+int or_linear(int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *x_codes, const float *x_scales,
+              const uint8_t *w_codes, const float *w_scales, int y_type, void *y, int32_t *acc_i32,
+              double *acc_f64) {
+    int64_t i, c;
+    /* INT8 sums stay within int32 for k * 127^2 < 2^31; FP8 sums within 2^53 (exact double) */
+    if (qtype == OR_INT8 && k > 133143) return -1;
+    if (qtype == OR_FP8 && k > 171196) return -1;
+    for (i = 0; i < m; ++i) {
+        for (c = 0; c < n; ++c) {
+            int64_t units = or_dot_units(qtype, x_codes + i * k, w_codes + c * k, k);
+            double acc = (qtype == OR_INT8) ? (double)units : ldexp((double)units, -18);
+            if (acc_i32 && qtype == OR_INT8) acc_i32[i * n + c] = (int32_t)units;
+            if (acc_f64) acc_f64[i * n + c] = acc;
+            or_store_y(y_type, y, i * n + c, acc * (double)x_scales[i] * (double)w_scales[c]);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------------
+ * a4: grouped (MoE) linear
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* For each expert e and each output row j of its token list, the a3 product of activation row row_ids[j]
+ * with expert e's weights. Returns -1 on an inconsistent token list. */
+int or_grouped_linear(int qtype, int64_t num_experts, int64_t n, int64_t k, const int32_t *expert_offsets,
+                      const int32_t *row_ids, int64_t x_rows, const uint8_t *x_codes, const float *x_scales,
+                      const uint8_t *w_codes, const float *w_scales, int y_type, void *y) {
+    int64_t e, j, c;
+    if (qtype == OR_INT8 && k > 133143) return -1;
+    if (qtype == OR_FP8 && k > 171196) return -1;
+    if (num_experts > 0 && expert_offsets[0] != 0) return -1;
+    for (e = 0; e < num_experts; ++e) {
+        const uint8_t *we = w_codes + e * n * k;
+        const float *se = w_scales + e * n;
+        if (expert_offsets[e + 1] < expert_offsets[e]) return -1;
+        for (j = expert_offsets[e]; j < expert_offsets[e + 1]; ++j) {
+            int64_t r = row_ids ? (int64_t)row_ids[j] : j;
+            if (r < 0 || r >= x_rows) return -1;
+            for (c = 0; c < n; ++c) {
+                int64_t units = or_dot_units(qtype, x_codes + r * k, we + c * k, k);
+                double acc = (qtype == OR_INT8) ? (double)units : ldexp((double)units, -18);
+                or_store_y(y_type, y, j * n + c, acc * (double)x_scales[r] * (double)se[c]);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------------
+ * a5: changed-code count between two published code sets
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* How many codes (and scales) a weight update changes ([QuRL] 4.3: the update between RL steps is much
+ * smaller than the quantization error, so most codes stay the same). Values are compared after decoding, so
+ * the FP8 codes 0x00 and 0x80 (+0 and -0) count as one value; scales are compared bit for bit. */
+void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
+                           const float *sb, int64_t n_scales, int64_t *out3) {
+    int64_t i, nb = 0, nv = 0, ns = 0;
+    for (i = 0; i < count; ++i) {
+        if (a[i] != b[i]) {
+            nb++;
+            if (qtype == OR_INT8) {
+                nv++;
+            } else {
+                double va = or_e4m3_decode(a[i]), vb = or_e4m3_decode(b[i]);
+                if (!(va == vb)) nv++;
+            }
+        }
+    }
+    for (i = 0; i < n_scales; ++i) {
+        uint32_t ua, ub;
+        memcpy(&ua, &sa[i], sizeof ua);
+        memcpy(&ub, &sb[i], sizeof ub);
+        if (ua != ub) ns++;
+    }
+    out3[0] = nb;
+    out3[1] = nv;
+    out3[2] = ns;
+}
