@@ -94,7 +94,9 @@ def quantize_row(row, qtype, s=None, recip=False):
         wp.append(v)
         neg.append(is_neg if v == 0 else v < 0)
     a = max((abs(v) for v in wp), default=Fraction(0))
-    S = round_f32(a / qmax) if a > 0 else Fraction(1)
+    S = round_f32(a / qmax)
+    if S == 0:  # all-zero row, or a scale that underflows: replaced by 1
+        S = Fraction(1)
     codes = []
     for v, is_neg in zip(wp, neg):
         q = round_f32(v / S)

@@ -172,8 +172,8 @@ static float or_load(const void *in, int in_type, int64_t idx) {
  *  1. w'_k = w_k, or fl32(w_k * s_k) for W diag(s), or fl32(w_k * fl32(1/s_k)) for X diag(1/s)
  *     ([QuRL] 4.3, invariant scaling);
  *  2. a = max_k |w'_k|;
- *  3. S = fl32(a / qmax), qmax = 127 (INT8) or 448 (FP8) ([QaRL] 2.2, s = max|W| / alpha); an all-zero row
- *     gets S = 1 so that its codes are all zero;
+ *  3. S = fl32(a / qmax), qmax = 127 (INT8) or 448 (FP8) ([QaRL] 2.2, s = max|W| / alpha); a row whose S
+ *     is zero (all-zero, or so small that a / qmax underflows) gets S = 1, so its codes are all (signed) zero;
  *  4. v_k = fl32(w'_k / S) (IEEE division);
  *  5. INT8: q = round-to-nearest-even of v clamped to [-127, 127] ([QaRL] 2.2 integer Quant with z = 0);
  *     FP8: q = E4M3 encoding of v clamped to [-448, 448] ([QaRL] 2.2 floating-point Quant). */
@@ -197,7 +197,8 @@ void or_quantize_rows(const void *in, int in_type, int64_t rows, int64_t k, cons
             wp[j] = w;
             if (fabsf(w) > a) a = fabsf(w);
         }
-        S = (a > 0.0f) ? a / qmax : 1.0f;
+        S = a / qmax;
+        if (!(S > 0.0f)) S = 1.0f; /* all-zero row, or a row so small that its scale underflows to zero */
         scales[r] = S;
         for (j = 0; j < k; ++j) {
             float v = wp[j] / S;

@@ -141,6 +141,25 @@ def test_all_zero_row(qtype):
 
 
 @pytest.mark.parametrize("qtype", QT)
+def test_underflowing_scale_is_replaced_by_one(qtype):
+    """A row of fp32 subnormals whose max / qmax rounds to 0 gets S = 1: codes are signed zeros (FP8) or 0
+    (INT8), matching the exact brute force; a row just large enough for a nonzero S keeps it."""
+    tiny = np.float32(2.0 ** -149)
+    row = (np.array([3, -3, 1, -1, 0, 2, -2, 3] * 2, np.float32) * tiny)[None, :]
+    codes, scales = O.quantize_rows(row, qtype)
+    assert scales[0] == 1.0
+    if qtype == O.INT8:
+        assert np.all(codes == 0)
+    else:
+        assert list(codes[0][:8]) == [0x00, 0x80, 0x00, 0x80, 0x00, 0x00, 0x80, 0x00]
+    bc, bs = brute.quantize_row([float(v) for v in row[0]], qtype)
+    assert bs == 1 and list(codes[0]) == bc
+    big = (np.float32(2.0 ** -120) * np.arange(1, 17, dtype=np.float32))[None, :]
+    c2, s2 = O.quantize_rows(big, qtype)
+    assert s2[0] != 1.0 and s2[0] > 0
+
+
+@pytest.mark.parametrize("qtype", QT)
 @pytest.mark.parametrize("with_s", [False, True])
 def test_round_trip_error_bound(qtype, with_s):
     """INT8: |S q - w'| <= S/2 (plus fp32 slack); FP8: at most half an E4M3 step of v = w'/S, i.e.
