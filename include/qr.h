@@ -58,7 +58,8 @@ typedef enum qr_qtype { QR_INT8 = 0, QR_FP8_E4M3 = 1 } qr_qtype;
  *
  * For every row r of w[n,k] (fp32 or bfloat16, selected by w_type):
  *   w'_j = w[r,j] * s[j] rounded to fp32 (or w[r,j] when s == NULL)
- *   S    = max_j |w'_j| / qmax rounded to fp32 (S = 1 for an all-zero row), qmax = 127 or 448
+ *   S    = max_j |w'_j| / qmax rounded to fp32, qmax = 127 or 448 (S = 1 when that rounds to 0: an all-zero
+ *          row, or one whose largest magnitude is below qmax * 2^-150)
  *   code = INT8: round-half-even(clamp(w'_j / S, -127, 127)); FP8: E4M3 nearest-even of clamp(w'_j / S, +-448)
  * with IEEE fp32 division and the sign of zero kept in FP8 (a negative value that rounds to 0 gives 0x80).
  * Writes w_codes[n,k] and w_scales[n]. s: device fp32 [k] or NULL.
@@ -80,8 +81,10 @@ qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k,
  *   acc[i,c] = sum_j xq[i,j] * wq[c,j]   (INT8: exact int32; FP8: fp32 accumulation of exact products)
  *   y[i,c]   = acc[i,c] * x_scales[i] * w_scales[c], stored as y_type (bfloat16 rounded to nearest even).
  * acc_out: optional [m,n] int32 (INT8) or fp32 (FP8) copy of the accumulators, or NULL.
- * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes (NULL allowed when that is
- * 0). It must be zero-filled before its first use; every completed call leaves it zero-filled again.
+ * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes, 256-byte aligned (NULL allowed
+ * when that is 0). Zero-fill it once before its first use: its first 256 KiB hold split-K arrival counters
+ * that every completed call returns to zero, and the rest is scratch, so one buffer serves any sequence of
+ * shapes on one stream.
  * INT8 results are bitwise independent of m (row i depends only on row i of the inputs) and deterministic;
  * FP8 results are deterministic for a given (m, n, k).
  * Limits: k <= 131072 (INT8 accumulators stay below 2^31).
@@ -99,7 +102,8 @@ qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void
  *                 expert_offsets[num_experts] == total_rows (the host passes total_rows).
  * row_ids: device int32 [total_rows] with values in [0, x_rows), or NULL for the identity.
  * w_codes: [num_experts, n, k]; w_scales: [num_experts, n]; y: [total_rows, n].
- * The device trusts the token lists; out-of-range rows are skipped, never read.
+ * The device trusts the token lists but never reads outside them: a row whose row_ids entry is outside
+ * [0, x_rows) gets zeros, and offsets are clamped to [0, total_rows].
  * workspace: as for qr_w8a8_linear, qr_workspace_bytes(q, total_rows, n, k, num_experts) bytes.
  */
 qr_status qr_w8a8_grouped_linear(qr_qtype q, int64_t num_experts, int64_t n, int64_t k,

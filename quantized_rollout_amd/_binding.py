@@ -1,0 +1,221 @@
+"""ctypes binding of libqr.so (the C ABI in include/qr.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels. PyTorch provides device
+memory (tensors) and the stream (``torch.cuda.current_stream()``). There is no fallback: if libqr.so is
+missing or fails to load, every call raises.
+
+The functions carry the C names (``qr_quantize_weights`` ...) and take torch CUDA tensors; outputs are
+allocated here with torch unless passed in.
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqr.so")
+
+# enums of qr.h
+QR_OK, QR_ERR_ARG, QR_ERR_UNSUPPORTED, QR_ERR_ALIGN, QR_ERR_WORKSPACE, QR_ERR_HIP = range(6)
+QR_F32, QR_BF16 = 0, 1
+QR_INT8, QR_FP8_E4M3 = 0, 1
+STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR_ALIGN", 4: "QR_ERR_WORKSPACE",
+                5: "QR_ERR_HIP"}
+
+# every symbol include/qr.h declares
+EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
+           "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version")
+
+
+class QRError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), text))
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libqr.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError("libqr.so is not built (run __graft_entry__.build() or "
+                                       "python -m quantized_rollout_amd.build); no fallback exists")
+                L = ctypes.CDLL(LIB_PATH)
+                vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+                L.qr_quantize_weights.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp]
+                L.qr_quantize_acts.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp]
+                L.qr_w8a8_linear.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+                L.qr_w8a8_grouped_linear.argtypes = [i32, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, vp, i32,
+                                                     vp, sz, vp]
+                L.qr_count_code_changes.argtypes = [vp, vp, i64, i32, vp, vp, i64, vp, vp]
+                for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
+                          "qr_count_code_changes"):
+                    getattr(L, f).restype = ctypes.c_int
+                L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+                L.qr_workspace_bytes.restype = sz
+                L.qr_last_error.argtypes = []
+                L.qr_last_error.restype = ctypes.c_char_p
+                L.qr_version.argtypes = []
+                L.qr_version.restype = ctypes.c_char_p
+                _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != QR_OK:
+        raise QRError(status, lib().qr_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return QR_BF16
+    if t.dtype == torch.float32:
+        return QR_F32
+    raise TypeError("expected a bfloat16 or float32 tensor, got %s" % t.dtype)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def qr_version():
+    return lib().qr_version().decode()
+
+
+def qr_workspace_bytes(qtype, m, n, k, num_experts=1):
+    return int(lib().qr_workspace_bytes(int(qtype), int(m), int(n), int(k), int(num_experts)))
+
+
+class Workspace:
+    """Zero-filled device workspace, grown on demand. The library leaves it zero-filled after each call;
+    calls that may overlap (different streams) need separate workspaces."""
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+        self.buf = None
+
+    def get(self, nbytes):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def default_workspace(device):
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _default_ws:
+        _default_ws[idx] = Workspace(idx)
+    return _default_ws[idx]
+
+
+def _quantize(fn, t, qtype, s, codes, scales, stream):
+    _need(t.is_cuda and t.dim() == 2 and t.is_contiguous(), "input must be a contiguous 2-D CUDA tensor")
+    rows, k = t.shape
+    if codes is None:
+        codes = torch.empty((rows, k), dtype=torch.uint8, device=t.device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=t.device)
+    if s is not None:
+        _need(s.is_cuda and s.dtype == torch.float32 and s.shape == (k,) and s.is_contiguous(),
+              "s must be a contiguous float32 CUDA vector of length k")
+    _need(codes.dtype == torch.uint8 and codes.shape == (rows, k) and codes.is_contiguous(), "bad codes tensor")
+    _need(scales.dtype == torch.float32 and scales.shape == (rows,) and scales.is_contiguous(), "bad scales tensor")
+    _check(fn(_ptr(t), _dtype_code(t), rows, k, _ptr(s), int(qtype), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def qr_quantize_weights(w, qtype, s=None, codes=None, scales=None, stream=None):
+    """Per-output-channel codes [n,k] (uint8) and scales [n] of w [n,k] (optionally of W diag(s))."""
+    return _quantize(lib().qr_quantize_weights, w, qtype, s, codes, scales, stream)
+
+
+def qr_quantize_acts(x, qtype, s=None, codes=None, scales=None, stream=None):
+    """Per-token codes [m,k] and scales [m] of x [m,k] (optionally of X diag(1/s))."""
+    return _quantize(lib().qr_quantize_acts, x, qtype, s, codes, scales, stream)
+
+
+def qr_w8a8_linear(qtype, x_codes, x_scales, w_codes, w_scales, y=None, y_dtype=torch.bfloat16, acc_out=None,
+                   workspace=None, stream=None):
+    """y [m,n] = (x_codes . w_codes^T) * x_scales[:,None] * w_scales[None,:]. ``acc_out`` True allocates the
+    accumulator copy (int32 for INT8, float32 for FP8); a tensor is filled in place. Returns y or (y, acc)."""
+    m, k = x_codes.shape
+    n, k2 = w_codes.shape
+    _need(k == k2, "k mismatch")
+    dev = x_codes.device
+    for t in (x_codes, x_scales, w_codes, w_scales):
+        _need(t.is_cuda and t.is_contiguous(), "operands must be contiguous CUDA tensors")
+    _need(x_codes.dtype == torch.uint8 and w_codes.dtype == torch.uint8, "codes must be uint8")
+    _need(x_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
+    _need(x_scales.shape == (m,) and w_scales.shape == (n,), "scale shapes")
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype, device=dev)
+    _need(y.shape == (m, n) and y.is_contiguous(), "bad y")
+    want_acc = acc_out is not None and acc_out is not False
+    if acc_out is True:
+        acc_out = torch.empty((m, n), dtype=torch.int32 if qtype == QR_INT8 else torch.float32, device=dev)
+    elif acc_out is False:
+        acc_out = None
+    nbytes = qr_workspace_bytes(qtype, m, n, k)
+    ws = (workspace if workspace is not None else default_workspace(dev)).get(nbytes)
+    _check(lib().qr_w8a8_linear(int(qtype), m, n, k, _ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales),
+                                _ptr(y), _dtype_code(y), _ptr(acc_out), _ptr(ws), nbytes, _stream(stream)))
+    return (y, acc_out) if want_acc else y
+
+
+def qr_w8a8_grouped_linear(qtype, expert_offsets, row_ids, total_rows, x_codes, x_scales, w_codes, w_scales, y=None,
+                           y_dtype=torch.bfloat16, workspace=None, stream=None):
+    """Grouped (MoE) linear. expert_offsets [E+1] int32 (device), row_ids [total_rows] int32 or None,
+    w_codes [E,n,k], w_scales [E,n]. Returns y [total_rows, n]."""
+    E, n, k = w_codes.shape
+    x_rows, k2 = x_codes.shape
+    _need(k == k2, "k mismatch")
+    dev = x_codes.device
+    _need(expert_offsets.dtype == torch.int32 and expert_offsets.shape == (E + 1,) and expert_offsets.is_cuda,
+          "expert_offsets must be int32 [E+1] on the GPU")
+    if row_ids is not None:
+        _need(row_ids.dtype == torch.int32 and row_ids.shape == (total_rows,) and row_ids.is_cuda, "bad row_ids")
+    _need(w_scales.shape == (E, n) and x_scales.shape == (x_rows,), "scale shapes")
+    if y is None:
+        y = torch.empty((total_rows, n), dtype=y_dtype, device=dev)
+    nbytes = qr_workspace_bytes(qtype, total_rows, n, k, E) if E > 1 else 0
+    ws = (workspace if workspace is not None else default_workspace(dev)).get(nbytes)
+    _check(lib().qr_w8a8_grouped_linear(int(qtype), E, n, k, _ptr(expert_offsets), _ptr(row_ids), int(total_rows),
+                                        x_rows, _ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales),
+                                        _ptr(y), _dtype_code(y), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def qr_count_code_changes(a, b, qtype, sa=None, sb=None, out3=None, stream=None):
+    """Device int64 [3]: bytes, decoded values and scales that differ between two code sets."""
+    _need(a.dtype == torch.uint8 and b.dtype == torch.uint8 and a.numel() == b.numel(), "codes must match")
+    ns = 0
+    if sa is not None:
+        _need(sb is not None and sa.numel() == sb.numel(), "scale vectors must match")
+        ns = sa.numel()
+    if out3 is None:
+        out3 = torch.empty(3, dtype=torch.int64, device=a.device)
+    _check(lib().qr_count_code_changes(_ptr(a), _ptr(b), a.numel(), int(qtype), _ptr(sa), _ptr(sb), ns, _ptr(out3),
+                                       _stream(stream)))
+    return out3

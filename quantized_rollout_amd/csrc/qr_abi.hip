@@ -1,0 +1,192 @@
+// qr_abi.hip -- the extern "C" boundary of libqr.so (declared in include/qr.h).
+//
+// Host-side validation of every argument before anything is enqueued, dispatch to the gfx950 kernels,
+// thread-local error text. No call allocates, synchronizes or keeps a pointer.
+#include "qr.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "qr_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qr_status fail(qr_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qr_status ok() {
+    g_err[0] = '\0';
+    return QR_OK;
+}
+
+qr_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(QR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxK = 131072;           // INT8 accumulators: k * 127^2 < 2^31
+constexpr int64_t kMaxRows = 2147483647;    // grid dimension limit
+
+qr_status check_q(qr_qtype q) {
+    if (q != QR_INT8 && q != QR_FP8_E4M3) return fail(QR_ERR_ARG, "unknown qtype %d", (int)q);
+    return QR_OK;
+}
+
+qr_status check_dtype(qr_dtype t, const char *name) {
+    if (t != QR_F32 && t != QR_BF16) return fail(QR_ERR_ARG, "unknown %s %d", name, (int)t);
+    return QR_OK;
+}
+
+qr_status check_k(int64_t k) {
+    if (k <= 0) return fail(QR_ERR_ARG, "k must be positive (got %lld)", (long long)k);
+    if (k % 16 != 0) return fail(QR_ERR_UNSUPPORTED, "k must be a multiple of 16 (got %lld)", (long long)k);
+    if (k > kMaxK) return fail(QR_ERR_UNSUPPORTED, "k = %lld exceeds %lld", (long long)k, (long long)kMaxK);
+    return QR_OK;
+}
+
+qr_status quantize_common(const void *in, qr_dtype in_type, int64_t rows, int64_t k, const float *s, qr_qtype q,
+                          void *codes, float *scales, void *stream, int s_mode) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if ((st = check_dtype(in_type, "input dtype")) != QR_OK) return st;
+    if (rows < 0) return fail(QR_ERR_ARG, "negative row count %lld", (long long)rows);
+    if (rows > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "row count %lld too large", (long long)rows);
+    if (k <= 0 || k % 16 != 0) {
+        if (k <= 0) return fail(QR_ERR_ARG, "k must be positive (got %lld)", (long long)k);
+        return fail(QR_ERR_UNSUPPORTED, "k must be a multiple of 16 (got %lld)", (long long)k);
+    }
+    if (rows == 0) return ok();
+    if (in == nullptr || codes == nullptr || scales == nullptr)
+        return fail(QR_ERR_ARG, "null input, code or scale pointer");
+    if (!aligned(in, 16) || !aligned(codes, 16)) return fail(QR_ERR_ALIGN, "input and codes must be 16-byte aligned");
+    if (!aligned(scales, 4) || (s != nullptr && !aligned(s, 4)))
+        return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+    const hipError_t e =
+        qr::launch_quantize_rows(in, in_type == QR_BF16, rows, k, s, s == nullptr ? qr::kSNone : s_mode, (int)q,
+                                 static_cast<uint8_t *>(codes), scales, static_cast<hipStream_t>(stream));
+    return hip_status(e, "quantize launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+qr_status qr_quantize_weights(const void *w, qr_dtype w_type, int64_t n, int64_t k, const float *s, qr_qtype q,
+                              void *w_codes, float *w_scales, void *stream) {
+    return quantize_common(w, w_type, n, k, s, q, w_codes, w_scales, stream, qr::kSMul);
+}
+
+qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k, const float *s, qr_qtype q,
+                           void *x_codes, float *x_scales, void *stream) {
+    return quantize_common(x, x_type, m, k, s, q, x_codes, x_scales, stream, qr::kSMulRecip);
+}
+
+size_t qr_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k, int64_t num_experts) {
+    if ((q != QR_INT8 && q != QR_FP8_E4M3) || m <= 0 || n <= 0 || k <= 0) return 0;
+    if (num_experts > 1) return qr::grouped_workspace_bytes((int)q, m, n, k, num_experts);
+    return qr::plan_linear((int)q, m, n, k).ws_bytes;
+}
+
+qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes, const float *x_scales,
+                         const void *w_codes, const float *w_scales, void *y, qr_dtype y_type, void *acc_out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if ((st = check_dtype(y_type, "output dtype")) != QR_OK) return st;
+    if (m < 0 || n < 0) return fail(QR_ERR_ARG, "negative size m=%lld n=%lld", (long long)m, (long long)n);
+    if ((st = check_k(k)) != QR_OK) return st;
+    if (m > kMaxRows || n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "m or n too large");
+    if (m == 0 || n == 0) return ok();
+    if (x_codes == nullptr || x_scales == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
+        return fail(QR_ERR_ARG, "null operand pointer");
+    if (!aligned(x_codes, 16) || !aligned(w_codes, 16)) return fail(QR_ERR_ALIGN, "codes must be 16-byte aligned");
+    if (!aligned(x_scales, 4) || !aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    if (!aligned(y, 16) || (acc_out != nullptr && !aligned(acc_out, 16)))
+        return fail(QR_ERR_ALIGN, "y and acc_out must be 16-byte aligned");
+    const qr::LinearPlan p = qr::plan_linear((int)q, m, n, k);
+    if (p.ws_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < p.ws_bytes)
+            return fail(QR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                        workspace == nullptr ? (size_t)0 : workspace_bytes);
+        if (!aligned(workspace, 256)) return fail(QR_ERR_ALIGN, "workspace must be 256-byte aligned");
+    }
+    if (getenv("QR_TRACE") != nullptr)
+        fprintf(stderr, "[qr] linear q=%d m=%lld n=%lld k=%lld kind=%d mt=%d waves=%d splits=%d ws=%zu\n", (int)q,
+                (long long)m, (long long)n, (long long)k, p.kind, p.m_tiles, p.waves, p.splits, p.ws_bytes);
+    const hipError_t e = qr::launch_linear(p, (int)q, m, n, k, static_cast<const uint8_t *>(x_codes), x_scales,
+                                           static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
+                                           acc_out, workspace, static_cast<hipStream_t>(stream));
+    return hip_status(e, "linear launch");
+}
+
+qr_status qr_w8a8_grouped_linear(qr_qtype q, int64_t num_experts, int64_t n, int64_t k,
+                                 const int32_t *expert_offsets, const int32_t *row_ids, int64_t total_rows,
+                                 int64_t x_rows, const void *x_codes, const float *x_scales, const void *w_codes,
+                                 const float *w_scales, void *y, qr_dtype y_type, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    qr_status st;
+    (void)workspace;
+    (void)workspace_bytes;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if ((st = check_dtype(y_type, "output dtype")) != QR_OK) return st;
+    if (num_experts < 0 || n < 0 || total_rows < 0 || x_rows < 0)
+        return fail(QR_ERR_ARG, "negative size");
+    if ((st = check_k(k)) != QR_OK) return st;
+    if (num_experts > 65535) return fail(QR_ERR_UNSUPPORTED, "at most 65535 experts");
+    if (n > kMaxRows || total_rows > kMaxRows || x_rows > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "size too large");
+    if (num_experts == 0 || n == 0 || total_rows == 0) return ok();
+    if (expert_offsets == nullptr || x_codes == nullptr || x_scales == nullptr || w_codes == nullptr ||
+        w_scales == nullptr || y == nullptr)
+        return fail(QR_ERR_ARG, "null operand pointer");
+    if (x_rows == 0 && row_ids != nullptr) return fail(QR_ERR_ARG, "row_ids given but x has no rows");
+    if (row_ids == nullptr && x_rows < total_rows)
+        return fail(QR_ERR_ARG, "identity rows need x_rows >= total_rows (%lld < %lld)", (long long)x_rows,
+                    (long long)total_rows);
+    if (!aligned(x_codes, 16) || !aligned(w_codes, 16)) return fail(QR_ERR_ALIGN, "codes must be 16-byte aligned");
+    if (!aligned(x_scales, 4) || !aligned(w_scales, 4) || !aligned(expert_offsets, 4) ||
+        (row_ids != nullptr && !aligned(row_ids, 4)))
+        return fail(QR_ERR_ALIGN, "scales and index arrays must be 4-byte aligned");
+    if (!aligned(y, 16)) return fail(QR_ERR_ALIGN, "y must be 16-byte aligned");
+    const hipError_t e = qr::launch_grouped((int)q, num_experts, n, k, expert_offsets, row_ids, total_rows, x_rows,
+                                            static_cast<const uint8_t *>(x_codes), x_scales,
+                                            static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "grouped launch");
+}
+
+qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_qtype q, const float *sa,
+                                const float *sb, int64_t n_scales, int64_t *out3, void *stream) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if (count < 0 || n_scales < 0) return fail(QR_ERR_ARG, "negative count");
+    if (out3 == nullptr) return fail(QR_ERR_ARG, "null out3");
+    if (!aligned(out3, 8)) return fail(QR_ERR_ALIGN, "out3 must be 8-byte aligned");
+    if (count > 0 && (a == nullptr || b == nullptr)) return fail(QR_ERR_ARG, "null code pointer");
+    if (n_scales > 0 && (sa == nullptr || sb == nullptr)) return fail(QR_ERR_ARG, "null scale pointer");
+    if ((a != nullptr && !aligned(a, 16)) || (b != nullptr && !aligned(b, 16)))
+        return fail(QR_ERR_ALIGN, "codes must be 16-byte aligned");
+    if ((sa != nullptr && !aligned(sa, 4)) || (sb != nullptr && !aligned(sb, 4)))
+        return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    const hipError_t e = qr::launch_count_changes(static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(b),
+                                                  count, (int)q, sa, sb, n_scales, out3,
+                                                  static_cast<hipStream_t>(stream));
+    return hip_status(e, "count launch");
+}
+
+const char *qr_last_error(void) { return g_err; }
+
+const char *qr_version(void) { return "0.1.0"; }
+
+}  // extern "C"

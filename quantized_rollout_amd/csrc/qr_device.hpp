@@ -1,0 +1,155 @@
+// qr_device.hpp -- device-side helpers shared by the gfx950 kernels of libqr.so.
+//
+// Codecs, the per-row division, wavefront reductions and MFMA wrappers. gfx950 (CDNA4) only: wave64,
+// v_mfma_i32_16x16x64_i8 for INT8 and v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit scales) for FP8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qr {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kInt8 = 0;
+constexpr int kFp8 = 1;
+
+// ---------------------------------------------------------------------------------------------------------
+// bfloat16 <-> fp32
+// ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bfloat16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Correctly rounded w / S for a whole row with one reciprocal.
+//
+// r = RN(1/S) is computed once per row with IEEE division. Then q = RN(w*r) is within one ulp of w/S, the
+// remainder e = w - q*S is exact when formed by one fused multiply-add, and RN(q + e*r) is the correctly
+// rounded quotient (P. Markstein, "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990; also Muller et al., Handbook of Floating-Point Arithmetic,
+// section on division with an FMA). The theorem needs the remainder to stay in the normal range, so callers
+// use it only for rows whose scale S is at least 2^-90; smaller rows take the IEEE division.
+// For w = -0 the last step returns +0 (fma(+0, r, -0) = +0), so the quotient takes the sign of w, which is
+// the sign of w / S for S > 0 (FP8 codes keep the sign of zero).
+// ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float div_by_scale(float w, float S, float r) {
+    float q = w * r;
+    float e = __builtin_fmaf(-q, S, w);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q), w);
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Code encoders. Inputs are already clamped to [-qmax, qmax].
+// ---------------------------------------------------------------------------------------------------------
+
+// INT8: round half to even (v_rndne_f32), then the exact integer conversion.
+__device__ __forceinline__ uint32_t encode_int8(float v) {
+    return (uint32_t)(int32_t)__builtin_rintf(v) & 0xFFu;
+}
+
+// FP8 E4M3FN, nearest value with ties to the even mantissa, sign of zero kept. |v| <= 448.
+//  - |v| < 2^-6 (the subnormal range): adding 2^14 makes the fp32 ulp exactly 2^-9, so the fp32 addition
+//    itself rounds |v| to a multiple of 2^-9 (ties to an even multiple); the difference of the bit patterns
+//    counts those multiples (0..8; 8 is the code of 2^-6, the smallest normal).
+//  - otherwise: round the 23-bit fp32 mantissa to 3 bits (add half minus one plus the kept lsb), then move
+//    the exponent from bias 127 to bias 7 by subtracting 120 from the exponent field.
+__device__ __forceinline__ uint32_t encode_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t ua = u & 0x7FFFFFFFu;
+    float a = __uint_as_float(ua);
+    uint32_t sub = __float_as_uint(a + 16384.0f) - 0x46800000u;  // 0x46800000 = bits of 2^14
+    uint32_t nrm = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+    return sign | (ua < 0x3C800000u ? sub : nrm);                // 0x3C800000 = bits of 2^-6
+}
+
+template <int QT>
+__device__ __forceinline__ uint32_t encode_code(float v) {
+    if constexpr (QT == kInt8) {
+        return encode_int8(v);
+    } else {
+        return encode_e4m3(v);
+    }
+}
+
+template <int QT>
+struct QMax;
+template <>
+struct QMax<kInt8> {
+    static constexpr float value = 127.0f;
+};
+template <>
+struct QMax<kFp8> {
+    static constexpr float value = 448.0f;
+};
+
+// ---------------------------------------------------------------------------------------------------------
+// Wavefront reductions (wave64).
+// ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// MFMA on 64-byte K chunks.
+//
+// Both operands use the same lane map: lane l supplies row (l & 15) of its operand (an activation row for A,
+// a weight row = output channel for B) and 16 (INT8) or 32 (FP8) consecutive K bytes chosen by (l >> 4).
+// Because A and B are addressed identically, the K permutation inside one instruction does not change the
+// dot products. The 16x16 result C[i][j] sits in lane (j + 16 * (i / 4)), element (i % 4).
+//
+// mma_k64(acc, a[4], b[4]): acc += A(16 x 256) * B(256 x 16)^T using four 64-byte K sub-chunks per lane.
+// ---------------------------------------------------------------------------------------------------------
+template <int QT>
+struct Acc;
+template <>
+struct Acc<kInt8> {
+    typedef v4i type;
+};
+template <>
+struct Acc<kFp8> {
+    typedef v4f type;
+};
+
+__device__ __forceinline__ void mma_step(v4i &acc, const uint4 *a, const uint4 *b) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        v4i av = {(int)a[t].x, (int)a[t].y, (int)a[t].z, (int)a[t].w};
+        v4i bv = {(int)b[t].x, (int)b[t].y, (int)b[t].z, (int)b[t].w};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void mma_step(v4f &acc, const uint4 *a, const uint4 *b) {
+#pragma unroll
+    for (int t = 0; t < 4; t += 2) {
+        v8i av = {(int)a[t].x, (int)a[t].y, (int)a[t].z, (int)a[t].w,
+                  (int)a[t + 1].x, (int)a[t + 1].y, (int)a[t + 1].z, (int)a[t + 1].w};
+        v8i bv = {(int)b[t].x, (int)b[t].y, (int)b[t].z, (int)b[t].w,
+                  (int)b[t + 1].x, (int)b[t + 1].y, (int)b[t + 1].z, (int)b[t + 1].w};
+        // format 0 = E4M3 for both operands; scale exponents 127 = 2^0 (no block scaling)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+    }
+}
+
+__device__ __forceinline__ float acc_to_f32(int a) { return (float)a; }
+__device__ __forceinline__ float acc_to_f32(float a) { return a; }
+
+}  // namespace qr

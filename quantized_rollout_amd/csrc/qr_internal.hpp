@@ -1,0 +1,46 @@
+// qr_internal.hpp -- host-side declarations shared by the translation units of libqr.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qr {
+
+// invariant-scale modes of the row quantizer
+enum SMode { kSNone = 0, kSMul = 1, kSMulRecip = 2 };
+
+// Row quantizer: one absmax scale per row of in[rows, k] (k % 16 == 0).
+hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode,
+                                int qtype, uint8_t *codes, float *scales, hipStream_t stream);
+
+// Plan of a W8A8 linear (which kernel, its split of K and the workspace it needs).
+struct LinearPlan {
+    int kind;          // 0 = small-M MFMA GEMV with split-K, 1 = LDS-tiled MFMA GEMM
+    int m_tiles;       // GEMV: 16-row tiles per pass
+    int waves;         // GEMV: waves per block (intra-block split of K)
+    int splits;        // GEMV: blocks along K (inter-block split), 1 = none
+    int64_t n_tiles;   // GEMV: 16-column tiles
+    size_t ws_bytes;   // workspace bytes
+};
+
+LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k);
+
+hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
+                         const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                         void *workspace, hipStream_t stream);
+
+size_t grouped_workspace_bytes(int qtype, int64_t total_rows, int64_t n, int64_t k, int64_t num_experts);
+
+hipError_t launch_grouped(int qtype, int64_t num_experts, int64_t n, int64_t k, const int32_t *offsets,
+                          const int32_t *row_ids, int64_t total_rows, int64_t x_rows, const uint8_t *xq,
+                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16,
+                          hipStream_t stream);
+
+hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
+                                const float *sb, int64_t n_scales, int64_t *out3, hipStream_t stream);
+
+// Environment overrides used for tuning sweeps (0 / -1 = automatic).
+int env_int(const char *name, int dflt);
+
+}  // namespace qr

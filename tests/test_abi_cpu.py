@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: libqr.so loads, exports every symbol include/qr.h declares, and its host-side
+validation rejects bad arguments before anything is launched (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_rollout_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qr.h")
+
+# fake, 256-byte aligned device addresses: validation never dereferences them on the host and every call
+# below fails (or is a no-op) before a launch
+P = ctypes.c_void_p(0x7F0000000000)
+P2 = ctypes.c_void_p(0x7F0000100000)
+MIS = ctypes.c_void_p(0x7F0000000008)
+NULL = None
+S0 = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_auxiliaries():
+    names = declared_functions()
+    for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear"):
+        assert f in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert re.match(r"^\d+\.\d+\.\d+$", B.qr_version())
+
+
+def _err():
+    return B.lib().qr_last_error().decode()
+
+
+def test_linear_validation():
+    L = B.lib()
+    ws = B.qr_workspace_bytes(B.QR_INT8, 16, 1536, 8960)
+    assert ws > 0
+    base = dict(q=0, m=16, n=1536, k=8960, x=P, xs=P, w=P, wsc=P, y=P, yt=1, acc=NULL, wsp=P2, wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.qr_w8a8_linear(a["q"], a["m"], a["n"], a["k"], a["x"], a["xs"], a["w"], a["wsc"], a["y"], a["yt"],
+                                a["acc"], a["wsp"], a["wsb"], S0)
+
+    assert call(k=8968) == B.QR_ERR_UNSUPPORTED and "multiple of 16" in _err()
+    assert call(k=0) == B.QR_ERR_ARG
+    assert call(k=131072 + 16) == B.QR_ERR_UNSUPPORTED
+    assert call(m=-1) == B.QR_ERR_ARG
+    assert call(q=7) == B.QR_ERR_ARG and "qtype" in _err()
+    assert call(yt=9) == B.QR_ERR_ARG
+    assert call(x=NULL) == B.QR_ERR_ARG
+    assert call(w=MIS) == B.QR_ERR_ALIGN
+    assert call(y=MIS) == B.QR_ERR_ALIGN
+    assert call(wsp=NULL) == B.QR_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == B.QR_ERR_WORKSPACE
+    assert call(wsp=MIS) == B.QR_ERR_ALIGN
+    # empty problems are no-ops that launch nothing
+    assert call(m=0) == B.QR_OK and _err() == ""
+    assert call(n=0, x=NULL) == B.QR_OK
+
+
+def test_quantize_validation():
+    L = B.lib()
+    for fn in (L.qr_quantize_weights, L.qr_quantize_acts):
+        assert fn(P, 1, 8, 24, NULL, 0, P, P, S0) == B.QR_ERR_UNSUPPORTED
+        assert fn(P, 1, 8, -16, NULL, 0, P, P, S0) == B.QR_ERR_ARG
+        assert fn(P, 1, -8, 16, NULL, 0, P, P, S0) == B.QR_ERR_ARG
+        assert fn(P, 5, 8, 16, NULL, 0, P, P, S0) == B.QR_ERR_ARG
+        assert fn(P, 1, 8, 16, NULL, 3, P, P, S0) == B.QR_ERR_ARG
+        assert fn(NULL, 1, 8, 16, NULL, 0, P, P, S0) == B.QR_ERR_ARG
+        assert fn(MIS, 1, 8, 16, NULL, 0, P, P, S0) == B.QR_ERR_ALIGN
+        assert fn(P, 1, 8, 16, ctypes.c_void_p(0x7F0000000002), 0, P, P, S0) == B.QR_ERR_ALIGN
+        assert fn(P, 1, 0, 16, NULL, 0, NULL, NULL, S0) == B.QR_OK
+
+
+def test_grouped_validation():
+    L = B.lib()
+
+    def call(E=4, n=64, k=256, off=P, rows=P, total=32, xrows=8, x=P, xs=P, w=P, wsc=P, y=P, yt=1):
+        return L.qr_w8a8_grouped_linear(1, E, n, k, off, rows, total, xrows, x, xs, w, wsc, y, yt, NULL, 0, S0)
+
+    assert call(k=250) == B.QR_ERR_UNSUPPORTED
+    assert call(E=-1) == B.QR_ERR_ARG
+    assert call(E=70000) == B.QR_ERR_UNSUPPORTED
+    assert call(off=NULL) == B.QR_ERR_ARG
+    assert call(rows=NULL, xrows=8, total=32) == B.QR_ERR_ARG  # identity rows need x_rows >= total_rows
+    assert call(x=MIS) == B.QR_ERR_ALIGN
+    assert call(total=0) == B.QR_OK
+    assert call(E=0) == B.QR_OK
+
+
+def test_count_validation():
+    L = B.lib()
+    assert L.qr_count_code_changes(P, P, 64, 1, NULL, NULL, 0, NULL, S0) == B.QR_ERR_ARG
+    assert L.qr_count_code_changes(NULL, P, 64, 1, NULL, NULL, 0, P, S0) == B.QR_ERR_ARG
+    assert L.qr_count_code_changes(P, P, -1, 1, NULL, NULL, 0, P, S0) == B.QR_ERR_ARG
+    assert L.qr_count_code_changes(MIS, P, 64, 1, NULL, NULL, 0, P, S0) == B.QR_ERR_ALIGN
+    assert L.qr_count_code_changes(P, P, 64, 3, NULL, NULL, 0, P, S0) == B.QR_ERR_ARG
+
+
+def test_workspace_sizes():
+    # large batches use the tiled GEMM (no workspace); decode batches that split K need counters + partials
+    assert B.qr_workspace_bytes(B.QR_FP8_E4M3, 2048, 37888, 3584) == 0
+    assert B.qr_workspace_bytes(B.QR_INT8, 0, 10, 16) == 0
+    assert B.qr_workspace_bytes(B.QR_INT8, 1, 1536, 8960) > 0
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()

@@ -1,0 +1,132 @@
+"""GPU parity of the grouped (MoE) linear (a4) and the changed-code count (a5)."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_rollout_amd as qr
+from oracle import core as O
+from quantized_rollout_amd import synth
+
+from gpu_util import assert_y_close, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+QT = [(O.INT8, qr.QR_INT8), (O.FP8, qr.QR_FP8_E4M3)]
+
+
+def _expert_weights(E, n, k, oq, rng):
+    wc = np.empty((E, n, k), np.uint8)
+    ws = np.empty((E, n), np.float32)
+    for e in range(E):
+        wc[e], ws[e] = O.quantize_rows((rng.standard_normal((n, k)) * 0.02).astype(np.float32), oq)
+    return wc, ws
+
+
+@pytest.mark.parametrize("oq,gq", QT)
+def test_grouped_parity_small(oq, gq):
+    rng = np.random.default_rng(300)
+    T, E, n, k, top = 40, 8, 72, 528, 3
+    x = rng.standard_normal((T, k)).astype(np.float32)
+    xc, xs = O.quantize_rows(x, oq, s_mode=O.S_MUL_RECIP)
+    wc, ws = _expert_weights(E, n, k, oq, rng)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 5] = -100.0  # expert 5 gets no tokens
+    off, rows = synth.route_top_k(logits, top)
+    assert off[6] == off[5]
+    log("grouped small %s E=%d rows=%d" % (oq, E, rows.size))
+    y_ref = O.grouped_linear(oq, off, rows, xc, xs, wc, ws)
+    y = qr.qr_w8a8_grouped_linear(gq, dev(off), dev(rows), rows.size, dev(xc), dev(xs), dev(wc), dev(ws))
+    torch.cuda.synchronize()
+    assert_y_close(host(y), y_ref, "grouped small")
+    # INT8: outputs come from exact accumulators, so per-expert rows equal the plain linear's bitwise
+    if oq == O.INT8:
+        for e in range(E):
+            r = rows[off[e]:off[e + 1]]
+            if r.size == 0:
+                continue
+            ye = qr.qr_w8a8_linear(gq, dev(xc[r]), dev(xs[r]), dev(wc[e]), dev(ws[e]))
+            torch.cuda.synchronize()
+            assert np.array_equal(host(ye), host(y)[off[e]:off[e + 1]]), e
+
+
+@pytest.mark.parametrize("oq,gq", QT)
+def test_grouped_identity_rows_and_many_rows_per_expert(oq, gq):
+    rng = np.random.default_rng(301)
+    E, n, k = 3, 40, 272
+    counts = [70, 0, 33]  # more rows than two token tiles, an empty expert
+    total = sum(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xc, xs = O.quantize_rows(rng.standard_normal((total, k)).astype(np.float32), oq, s_mode=O.S_MUL_RECIP)
+    wc, ws = _expert_weights(E, n, k, oq, rng)
+    y_ref = O.grouped_linear(oq, off, None, xc, xs, wc, ws)
+    y = qr.qr_w8a8_grouped_linear(gq, dev(off), None, total, dev(xc), dev(xs), dev(wc), dev(ws))
+    torch.cuda.synchronize()
+    assert_y_close(host(y), y_ref, "grouped identity")
+
+
+def test_grouped_full_size_qwen3_moe_fp8_sampled():
+    """The Qwen3-30B-A3B-shaped MoE layer: 128 experts, top-8 of 256 tokens, gate/up 2048->2x768 and down
+    768->2048, FP8; every expert's full weights in one launch, the oracle checks sampled channels."""
+    inp = synth.make_moe()
+    rng = np.random.default_rng(302)
+    xc, xs = O.quantize_rows(inp.x, O.FP8, s_mode=O.S_MUL_RECIP)
+    hc, hs = O.quantize_rows(inp.h, O.FP8, s_mode=O.S_MUL_RECIP)
+    for name, w, acts, scales, rows in (("gate_up", inp.w_gate_up, xc, xs, inp.row_ids),
+                                        ("down", inp.w_down, hc, hs, None)):
+        E, n, k = w.shape
+        wc = np.empty((E, n, k), np.uint8)
+        ws = np.empty((E, n), np.float32)
+        for e in range(E):
+            wc[e], ws[e] = O.quantize_rows(w[e], O.FP8)
+        total = int(inp.expert_offsets[-1])
+        log("moe %s E=%d n=%d k=%d rows=%d" % (name, E, n, k, total))
+        y = qr.qr_w8a8_grouped_linear(qr.QR_FP8_E4M3, dev(inp.expert_offsets), None if rows is None else dev(rows),
+                                      total, dev(acts), dev(scales), dev(wc), dev(ws))
+        torch.cuda.synchronize()
+        cols = np.sort(rng.choice(n, 16, replace=False))
+        y_ref = O.grouped_linear(O.FP8, inp.expert_offsets, rows, acts, scales, wc[:, cols], ws[:, cols])
+        assert_y_close(host(y)[:, cols], y_ref, "moe " + name)
+
+
+@pytest.mark.parametrize("oq,gq", QT)
+def test_count_code_changes_parity(oq, gq):
+    inp = synth.make_requant(linears=["qkv"], row_limit=1024)
+    w, w2, s = inp.w["qkv"], inp.w2["qkv"], inp.s["qkv"]
+    for with_s in (False, True):
+        a, sa = O.quantize_rows(w, oq, s=s if with_s else None)
+        b, sb = O.quantize_rows(w2, oq, s=s if with_s else None)
+        ref = O.count_code_changes(a, b, oq, sa, sb)
+        got = qr.qr_count_code_changes(dev(a), dev(b), gq, dev(sa), dev(sb))
+        torch.cuda.synchronize()
+        assert list(host(got)) == list(ref), (with_s, host(got), ref)
+    # ragged byte count (not a multiple of 16), equal inputs, FP8 signed zeros
+    z = np.array([0x00, 0x80, 0x38, 0x38] * 9 + [0x80], np.uint8)
+    z2 = np.array([0x80, 0x00, 0x38, 0xB8] * 9 + [0x00], np.uint8)
+    for aa, bb in ((z, z2), (z, z)):
+        ref = O.count_code_changes(aa, bb, oq)
+        ta = torch.zeros(48, dtype=torch.uint8, device="cuda")
+        tb = torch.zeros(48, dtype=torch.uint8, device="cuda")
+        ta[:aa.size] = dev(aa)
+        tb[:bb.size] = dev(bb)
+        got = qr.qr_count_code_changes(ta[:aa.size], tb[:bb.size], gq)
+        torch.cuda.synchronize()
+        assert list(host(got)) == list(ref)
+
+
+@pytest.mark.parametrize("oq,gq", QT)
+def test_requant_full_size_on_gpu_matches_oracle_counts(oq, gq):
+    """The weight publish between RL steps on one 7B linear (o-proj, 3584x3584, fp32 masters): quantize W
+    and W + dW on the GPU, count changed codes on the GPU; the oracle does the same from the same inputs."""
+    inp = synth.make_requant(linears=["o"])
+    w, w2, s = inp.w["o"], inp.w2["o"], inp.s["o"]
+    for with_s in (False, True):
+        sd = dev(s) if with_s else None
+        a, sa = qr.qr_quantize_weights(dev(w), gq, s=sd)
+        b, sb = qr.qr_quantize_weights(dev(w2), gq, s=sd)
+        got = qr.qr_count_code_changes(a, b, gq, sa, sb)
+        torch.cuda.synchronize()
+        ra, rsa = O.quantize_rows(w, oq, s=s if with_s else None)
+        rb, rsb = O.quantize_rows(w2, oq, s=s if with_s else None)
+        ref = O.count_code_changes(ra, rb, oq, rsa, rsb)
+        log("requant o %s s=%s changed bytes %d of %d" % (oq, with_s, ref[0], w.size))
+        assert list(host(got)) == list(ref)

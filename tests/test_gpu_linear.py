@@ -1,0 +1,197 @@
+"""GPU parity of the W8A8 linear (a3): INT8 accumulators bit-exact, outputs within 1e-2 * max|ref|, for
+both kernels (small-m GEMV with split-K, tiled GEMM), ragged shapes, the toy and full-size workloads."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_rollout_amd as qr
+from oracle import core as O
+from quantized_rollout_amd import synth
+
+from gpu_util import assert_y_close, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+QT = [(O.INT8, qr.QR_INT8), (O.FP8, qr.QR_FP8_E4M3)]
+GQ = {O.INT8: qr.QR_INT8, O.FP8: qr.QR_FP8_E4M3}
+
+
+def _quantized_operands(m, n, k, oq, seed):
+    """Activations (with outlier channels) and weights, quantized by the oracle."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, rng.choice(k, min(4, k), replace=False)] *= np.float32(20)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    xc, xs = O.quantize_rows(x, oq, s_mode=O.S_MUL_RECIP)
+    wc, ws = O.quantize_rows(w, oq)
+    return xc, xs, wc, ws
+
+
+def _run(oq, xc, xs, wc, ws, y_dtype=torch.bfloat16):
+    y, acc = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), y_dtype=y_dtype, acc_out=True)
+    torch.cuda.synchronize()
+    return host(y), host(acc)
+
+
+def _check(oq, xc, xs, wc, ws, what, y_type=O.BF16):
+    y_ref, acc_i, acc_f = O.linear(oq, xc, xs, wc, ws, y_type)
+    y, acc = _run(oq, xc, xs, wc, ws, torch.bfloat16 if y_type == O.BF16 else torch.float32)
+    if oq == O.INT8:
+        if not np.array_equal(acc, acc_i):
+            bad = np.argwhere(acc != acc_i)
+            i = tuple(bad[0])
+            raise AssertionError("%s: %d INT32 accumulators differ, first %s gpu %d oracle %d"
+                                 % (what, len(bad), i, acc[i], acc_i[i]))
+    else:
+        # FP8 accumulates exact products in fp32: reported against the fp32 summation bound, gated by y
+        worst = np.abs(acc.astype(np.float64) - acc_f).max()
+        log("  fp8 acc max|gpu - exact| = %.3g (max|acc| %.3g)" % (worst, np.abs(acc_f).max()))
+    assert_y_close(y, y_ref, what)
+
+
+# (m, n, k): several 16-column tiles, ragged n (not a multiple of 16 / 128), ragged k (not a multiple of
+# the 256-byte step), every GEMV token-tile count (1, 2, 4), split-K and no split, and the tiled GEMM
+SHAPES = [(1, 16, 16), (4, 512, 256), (3, 37, 272), (16, 200, 1552), (17, 96, 512), (33, 130, 784),
+          (64, 64, 4096), (1, 1536, 8960), (16, 2048, 1536), (65, 150, 528), (128, 256, 1024),
+          (300, 333, 1040), (512, 384, 2048)]
+
+
+@pytest.mark.parametrize("oq,gq", QT)
+def test_linear_parity_shapes(oq, gq):
+    for i, (m, n, k) in enumerate(SHAPES):
+        log("linear %s m=%d n=%d k=%d" % (oq, m, n, k))
+        xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=200 + i)
+        _check(oq, xc, xs, wc, ws, "%s m=%d n=%d k=%d" % (oq, m, n, k))
+
+
+@pytest.mark.parametrize("oq,gq", QT)
+def test_linear_fp32_output(oq, gq):
+    xc, xs, wc, ws = _quantized_operands(8, 96, 512, oq, seed=5)
+    _check(oq, xc, xs, wc, ws, "fp32 out", y_type=O.F32)
+
+
+def test_toy_workload_int8():
+    """The toy INT8 linear: M=4, K=256, N=512, fp32 weights N(0, 0.02), activations N(0, 1) with 4 outlier
+    channels x20, seed 0 -- quantized on the GPU and checked end to end (codes, accumulators, outputs)."""
+    inp = synth.make_dense(synth.TOY)
+    w, x = inp.weights["toy"], inp.acts["toy"]
+    wc_ref, ws_ref = O.quantize_rows(w, O.INT8)
+    xc_ref, xs_ref = O.quantize_rows(x, O.INT8, s_mode=O.S_MUL_RECIP)
+    y_ref, acc_ref, _ = O.linear(O.INT8, xc_ref, xs_ref, wc_ref, ws_ref, O.BF16)
+    wc, ws = qr.qr_quantize_weights(dev(w), qr.QR_INT8)
+    xc, xs = qr.qr_quantize_acts(dev(x), qr.QR_INT8)
+    y, acc = qr.qr_w8a8_linear(qr.QR_INT8, xc, xs, wc, ws, acc_out=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(wc), wc_ref) and np.array_equal(host(xc), xc_ref)
+    assert np.array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), y_ref, "toy")
+    # the quantized product stays close to the unquantized one despite the outlier channels
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    yf = synth.bf16_bits_to_f32(host(y)).astype(np.float64)
+    assert np.abs(yf - ref).max() <= 0.05 * np.abs(ref).max()
+
+
+def test_int8_batch_prefix_and_determinism():
+    """INT8: row i of y is bitwise the same for every batch prefix (exact accumulators, elementwise
+    epilogue) and for repeated calls; crosses the GEMV/GEMM switch."""
+    xc, xs, wc, ws = _quantized_operands(200, 272, 1040, O.INT8, seed=77)
+    y_full, _ = _run(O.INT8, xc, xs, wc, ws)
+    y_again, _ = _run(O.INT8, xc, xs, wc, ws)
+    assert np.array_equal(y_full, y_again)
+    for m in (1, 5, 16, 17, 64, 65, 129):
+        y, _ = _run(O.INT8, xc[:m], xs[:m], wc, ws)
+        assert np.array_equal(y, y_full[:m]), m
+
+
+def test_fp8_determinism():
+    xc, xs, wc, ws = _quantized_operands(16, 1536, 8960, O.FP8, seed=78)
+    a, _ = _run(O.FP8, xc, xs, wc, ws)
+    b, _ = _run(O.FP8, xc, xs, wc, ws)
+    assert np.array_equal(a, b)
+
+
+def test_workspace_is_left_zeroed():
+    xc, xs, wc, ws = _quantized_operands(16, 1536, 8960, O.INT8, seed=79)
+    nbytes = qr.qr_workspace_bytes(qr.QR_INT8, 16, 1536, 8960)
+    assert nbytes > 0
+    wsp = qr.Workspace()
+    buf = wsp.get(nbytes)
+    for _ in range(3):
+        qr.qr_w8a8_linear(qr.QR_INT8, dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
+    torch.cuda.synchronize()
+    counters = buf[:262144].view(torch.int32)  # the fixed split-K counter region
+    assert int(counters.abs().sum()) == 0
+
+
+def test_workspace_reuse_across_plans():
+    """One workspace serves a sequence of differently split shapes (partials of one plan must never land in
+    another plan's counters): every call stays bit-exact (INT8) or within tolerance (FP8)."""
+    wsp = qr.Workspace()
+    wsp.get(64 << 20)
+    shapes = [(64, 64, 4096), (1, 1536, 8960), (16, 200, 1552), (33, 130, 784), (1, 2048, 8960), (64, 64, 4096),
+              (16, 1536, 8960)]
+    for oq in (O.INT8, O.FP8):
+        for i, (m, n, k) in enumerate(shapes * 2):
+            xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=400 + i)
+            log("workspace reuse %s m=%d n=%d k=%d" % (oq, m, n, k))
+            y_ref, acc_i, _ = O.linear(oq, xc, xs, wc, ws, O.BF16)
+            y, acc = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), acc_out=True, workspace=wsp)
+            torch.cuda.synchronize()
+            if oq == O.INT8:
+                assert np.array_equal(host(acc), acc_i), (m, n, k)
+            assert_y_close(host(y), y_ref, "reuse m=%d n=%d k=%d" % (m, n, k))
+
+
+def test_fp8_all_max_codes_accumulate_exactly():
+    """All-448 codes: every partial sum 200704 * j is exactly representable in fp32, so the accumulators equal
+    200704 * k exactly (closed form; k = 18944 gives 2^21 * 1813)."""
+    for (m, n, k) in [(1, 16, 18944), (16, 64, 3584), (200, 130, 2048)]:
+        xc = np.full((m, k), 0x7E, np.uint8)
+        wc = np.full((n, k), 0xFE, np.uint8)
+        ones_m, ones_n = np.ones(m, np.float32), np.ones(n, np.float32)
+        y, acc = qr.qr_w8a8_linear(qr.QR_FP8_E4M3, dev(xc), dev(ones_m), dev(wc), dev(ones_n), acc_out=True,
+                                   y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert np.all(host(acc) == np.float32(-200704.0 * k)), (m, n, k)
+        assert np.all(host(y) == np.float32(-200704.0 * k))
+
+
+def _full_size_case(wl, oq, m_list, n_sample=48):
+    inp = synth.make_dense(wl)
+    rng = np.random.default_rng(12)
+    for name, w in inp.weights.items():
+        x = inp.acts[name]
+        wc_ref, ws_ref = O.quantize_rows(w, oq)
+        xc_all, xs_all = O.quantize_rows(x, oq, s_mode=O.S_MUL_RECIP)
+        cols = np.sort(rng.choice(w.shape[0], n_sample, replace=False))
+        cols[-1] = w.shape[0] - 1
+        wcd, wsd = dev(wc_ref), dev(ws_ref)
+        for m in m_list:
+            log("full-size linear %s %s m=%d n=%d k=%d" % (wl.name, name, m, w.shape[0], w.shape[1]))
+            y, acc = qr.qr_w8a8_linear(GQ[oq], dev(xc_all[:m]), dev(xs_all[:m]), wcd, wsd, acc_out=True)
+            torch.cuda.synchronize()
+            y_ref, acc_i, _ = O.linear(oq, xc_all[:m], xs_all[:m], wc_ref[cols], ws_ref[cols], O.BF16)
+            y_h = host(y)[:, cols]
+            if oq == O.INT8:
+                assert np.array_equal(host(acc)[:, cols], acc_i), (name, m)
+            assert_y_close(y_h, y_ref, "%s %s m=%d" % (wl.name, name, m))
+
+
+def test_full_size_qwen_1p5b_int8_sampled():
+    _full_size_case(synth.QWEN_1P5B, O.INT8, [1, 16, 64])
+
+
+def test_full_size_7b_fp8_sampled():
+    _full_size_case(synth.DENSE_7B, O.FP8, [1, 16, 128, 512, 2048], n_sample=24)
+
+
+def test_empty_and_errors():
+    z = torch.zeros((0, 32), dtype=torch.uint8, device="cuda")
+    zs = torch.zeros((0,), dtype=torch.float32, device="cuda")
+    w = torch.zeros((8, 32), dtype=torch.uint8, device="cuda")
+    wsc = torch.ones((8,), dtype=torch.float32, device="cuda")
+    y = qr.qr_w8a8_linear(qr.QR_INT8, z, zs, w, wsc)
+    assert y.shape == (0, 8)
+    with pytest.raises(qr.QRError):
+        qr.qr_w8a8_linear(qr.QR_INT8, torch.zeros((2, 24), dtype=torch.uint8, device="cuda"),
+                          torch.ones(2, device="cuda"), torch.zeros((8, 24), dtype=torch.uint8, device="cuda"), wsc)
