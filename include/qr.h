@@ -81,10 +81,9 @@ qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k,
  *   acc[i,c] = sum_j xq[i,j] * wq[c,j]   (INT8: exact int32; FP8: fp32 accumulation of exact products)
  *   y[i,c]   = acc[i,c] * x_scales[i] * w_scales[c], stored as y_type (bfloat16 rounded to nearest even).
  * acc_out: optional [m,n] int32 (INT8) or fp32 (FP8) copy of the accumulators, or NULL.
- * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes, 256-byte aligned (NULL allowed
- * when that is 0). Zero-fill it once before its first use: its first 256 KiB hold split-K arrival counters
- * that every completed call returns to zero, and the rest is scratch, so one buffer serves any sequence of
- * shapes on one stream.
+ * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes, 256-byte aligned, or NULL when
+ * that is 0. Every current plan reduces inside its workgroups, so qr_workspace_bytes() returns 0 and NULL may be
+ * passed; the argument stays so that callers size it through qr_workspace_bytes() whatever a plan needs.
  * INT8 results are bitwise independent of m (row i depends only on row i of the inputs) and deterministic;
  * FP8 results are deterministic for a given (m, n, k).
  * Limits: k <= 131072 (INT8 accumulators stay below 2^31).

@@ -16,11 +16,14 @@ hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int6
 
 // Plan of a W8A8 linear (which kernel, its split of K and the workspace it needs).
 struct LinearPlan {
-    int kind;          // 0 = small-M MFMA GEMV with split-K, 1 = LDS-tiled MFMA GEMM
-    int m_tiles;       // GEMV: 16-row tiles per pass
-    int waves;         // GEMV: waves per block (intra-block split of K)
-    int splits;        // GEMV: blocks along K (inter-block split), 1 = none
-    int64_t n_tiles;   // GEMV: 16-column tiles
+    int kind;          // 0 = small-M MFMA GEMV, 1 = LDS-tiled MFMA GEMM
+    int m_tiles;       // GEMV: 16-token tiles per block
+    int waves;         // GEMV: waves per block (they split K)
+    int unroll;        // GEMV: 1-KiB load instructions per wave step
+    int tiles;         // GEMV: 16-channel tiles per block
+    bool prefetch;     // GEMV: software-pipelined loads
+    int splits;        // GEMV: blocks along K, 1 = none
+    int64_t n_tiles;   // GEMV: 16-channel tiles
     size_t ws_bytes;   // workspace bytes
 };
 

@@ -6,12 +6,13 @@
 // weight scales and token-wise activation scales.
 //
 // Two kernels, chosen by the batch m:
-//  * gemv_kernel (m <= 64): the decode regime, bound by streaming the n*k weight bytes from HBM. A wave owns
-//    16 output channels and walks K in 256-byte steps, each lane loading 64 contiguous bytes of one weight row
-//    (16 rows x 256 B per wave and step) plus the matching activation bytes, and issues MFMA 16x16 tiles over
-//    up to four 16-token tiles. The waves of a block split the block's K range (reduced through LDS in a fixed
-//    order); when the n tiles alone cannot fill 256 CUs, blocks also split K and the last block to finish a
-//    tile sums the partials in split order and applies the epilogue (deterministic, one launch).
+//  * gemv_kernel (m <= 64): the decode regime, bound by streaming the n*k weight bytes from HBM. A block owns
+//    one tile of 16 output channels; its waves split K. Each load instruction of a wave covers 64 contiguous K
+//    bytes of each of the 16 weight rows (four lanes per row, 16 bytes each), and a wave issues U of them back
+//    to back before its MFMAs, so every wave keeps U KiB of weights in flight. The waves of the block reduce
+//    their accumulators through LDS in wave order and wave 0 applies the epilogue: one launch, deterministic,
+//    no cross-block synchronization. The waves per block are chosen at launch so that even the narrow linears
+//    put a few thousand waves on the 256 CUs.
 //  * gemm_kernel (m > 64): LDS-tiled MFMA GEMM, 128x128 output tiles, 128-byte K steps, double-buffered LDS.
 #include "qr_device.hpp"
 #include "qr_internal.hpp"
@@ -20,14 +21,6 @@
 
 namespace qr {
 namespace {
-
-constexpr int kStep = 256;  // K bytes per wave step in the GEMV
-
-// Workspace layout of a split-K GEMV: [kMaxCounters uint32 arrival counters | partial tiles]. The counter
-// region has the same place and size for every plan, and the last block of each tile resets its counter, so
-// the region stays zero between calls whatever shapes ran before; the partials are scratch.
-constexpr int64_t kMaxCounters = 65536;
-constexpr size_t kCounterBytes = kMaxCounters * 4;
 
 __device__ __forceinline__ void store_y(void *y, int64_t idx, float v, bool bf16) {
     if (bf16)
@@ -41,166 +34,193 @@ __device__ __forceinline__ void store_acc(void *acc_out, int64_t idx, float v) {
     static_cast<float *>(acc_out)[idx] = v;
 }
 
-// Loads the 64 K bytes lane (j, g) contributes to one 256-byte step of row `row_ptr` (NULL = zero row).
-__device__ __forceinline__ void load_step(uint4 *dst, const uint8_t *__restrict__ row_ptr, int64_t kb, int64_t k) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int64_t off = kb + 16 * t;
-        if (row_ptr != nullptr && off < k)
-            dst[t] = *reinterpret_cast<const uint4 *>(row_ptr + off);
-        else
-            dst[t] = make_uint4(0, 0, 0, 0);
-    }
+__device__ __forceinline__ uint4 load16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ v4i as_v4i(const uint4 &a) { return v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w}; }
+__device__ __forceinline__ v8i as_v8i(const uint4 &a, const uint4 &b) {
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Small-m GEMV with split-K
+// Small-m GEMV
+//
+// A block owns TB tiles of 16 output channels (16 TB weight rows) and all of K. K is cut into slices of 64 U
+// bytes; wave w takes slices w, w + W, ... For each slice it loads the activations once -- coalesced (lane l
+// reads token row l >> 2, bytes 16 (l & 3) of each 64-byte block) and moved to the MFMA layout with ds_bpermute
+// -- and keeps them in registers while the TB weight tiles stream past them, the next tile's loads in flight
+// during the current tile's MFMAs. Activation traffic is therefore M K bytes per block rather than per tile.
+//
+// MFMA layout: lane (j, g) = (lane & 15, lane >> 4) supplies bytes [kb + 64 t + 16 g, +16) of weight row j of a
+// tile (B operand, output channel j) and of token row j of a 16-token tile (A operand) for load t of a slice.
+// INT8: one v_mfma_i32_16x16x64_i8 per load (K = 64 = the 4 lanes' 16 bytes). FP8: one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per pair of loads (32 bytes per lane). A and B use the same lane -> K map,
+// so the dot products are those of the plain definition. Result C[i][c] sits in lane (c + 16 (i / 4)),
+// element i % 4. Per-tile partials of all waves meet in LDS; every wave then sums a share of the 16x16
+// fragments over the waves in wave order (deterministic) and applies the epilogue to them.
 // ---------------------------------------------------------------------------------------------------------
-template <int QT, int MT, int WPB>
-__global__ __launch_bounds__(WPB * 64) void gemv_kernel(int64_t m, int64_t n, int64_t k,
-                                                        const uint8_t *__restrict__ xq,
-                                                        const float *__restrict__ xs,
-                                                        const uint8_t *__restrict__ wq,
-                                                        const float *__restrict__ ws, void *__restrict__ y,
-                                                        int y_bf16, void *__restrict__ acc_out, int splits,
-                                                        int64_t n_tiles, int32_t *__restrict__ partials,
-                                                        uint32_t *__restrict__ counters) {
+template <int QT, int MT, int U, int TB, int WMAX>
+__global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq,
+                                                         const float *__restrict__ xs, const uint8_t *__restrict__ wq,
+                                                         const float *__restrict__ ws, void *__restrict__ y,
+                                                         int y_bf16, void *__restrict__ acc_out) {
     typedef typename Acc<QT>::type acc_t;
+    static_assert(QT == kInt8 || U % 2 == 0, "FP8 pairs load instructions");
+    extern __shared__ int32_t red[];  // [waves][TB][MT][4][64]
+    const int waves = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int64_t tile = blockIdx.x;
-    const int split = blockIdx.y;
-    const int64_t m0 = (int64_t)blockIdx.z * (16 * MT);
+    const int64_t tile0 = (int64_t)blockIdx.x * TB;
+    const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+    constexpr int64_t kSlice = 64 * U;
+    const int64_t slices = (k + kSlice - 1) / kSlice;
 
-    const int64_t steps = (k + kStep - 1) / kStep;
-    const int64_t per = (steps + splits - 1) / splits;
-    const int64_t s_beg = (int64_t)split * per;
-    const int64_t s_end = s_beg + per < steps ? s_beg + per : steps;
-
-    const int64_t ncol = tile * 16 + j;
-    const uint8_t *__restrict__ wrow = ncol < n ? wq + ncol * k : nullptr;
+    // weight rows of this lane (rows past n re-read row n-1; those columns are never stored)
+    const uint8_t *__restrict__ wrow[TB];
+#pragma unroll
+    for (int r = 0; r < TB; ++r) {
+        const int64_t col = (tile0 + r) * 16 + j;
+        wrow[r] = wq + (col < n ? col : n - 1) * k + 16 * g;
+    }
+    // coalesced activation loads: lane l reads token row (l >> 2) of each token tile, piece (l & 3)
+    const int xr = lane >> 2, xp = lane & 3;
+    const int src_lane = 4 * j + g;  // the lane that loads what lane (j, g) needs
+    // token rows past m re-read row m-1: they only feed output rows that are never stored
     const uint8_t *__restrict__ xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int64_t r = m0 + mt * 16 + j;
-        xrow[mt] = r < m ? xq + r * k : nullptr;
+        const int64_t r = m0 + mt * 16 + xr;
+        xrow[mt] = xq + (r < m ? r : m - 1) * k + 16 * xp;
     }
 
-    acc_t acc[MT];
+    acc_t acc[TB][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = acc_t{0, 0, 0, 0};
+    for (int r = 0; r < TB; ++r)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = acc_t{0, 0, 0, 0};
 
-    int64_t st = s_beg + wave;
-    if (st < s_end) {
-        uint4 wcur[4], xcur[MT][4];
-        load_step(wcur, wrow, st * kStep + g * 64, k);
+    // Per slice, one burst: the slice's activations and all TB weight tiles are requested together, then the
+    // activations are moved to the MFMA layout (in place) and the tiles' MFMAs run. Few registers per wave
+    // keep many waves resident, and the resident waves hide each other's latency. Loads in full slices are
+    // unconditional; in the partial last slice (k not a multiple of the slice) out-of-range bytes are zero.
+    auto transpose = [&](uint4 (&xv)[MT][U]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) load_step(xcur[mt], xrow[mt], st * kStep + g * 64, k);
-        for (;;) {
-            const int64_t nx = st + WPB;
-            uint4 wnxt[4], xnxt[MT][4];
-            if (nx < s_end) {
-                load_step(wnxt, wrow, nx * kStep + g * 64, k);
+        for (int t = 0; t < U; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) load_step(xnxt[mt], xrow[mt], nx * kStep + g * 64, k);
+            for (int mt = 0; mt < MT; ++mt) {
+                xv[mt][t].x = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].x);
+                xv[mt][t].y = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].y);
+                xv[mt][t].z = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].z);
+                xv[mt][t].w = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].w);
             }
+    };
+    auto mma = [&](acc_t (&a)[MT], const uint4 (&xv)[MT][U], const uint4 (&wv)[U]) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) mma_step(acc[mt], xcur[mt], wcur);
-            if (nx >= s_end) break;
-            st = nx;
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (QT == kInt8) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                wcur[t] = wnxt[t];
+                for (int t = 0; t < U; ++t)
+                    a[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(xv[mt][t]), as_v4i(wv[t]), a[mt], 0, 0, 0);
+            } else {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xcur[mt][t] = xnxt[mt][t];
+                for (int t = 0; t < U; t += 2)
+                    // format 0 = E4M3 for both operands; scale exponents 127 = 2^0 (no block scaling)
+                    a[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        as_v8i(xv[mt][t], xv[mt][t + 1]), as_v8i(wv[t], wv[t + 1]), a[mt], 0, 0, 0, 127, 0, 127);
             }
         }
+    };
+    const int64_t full = k / kSlice;
+    for (int64_t sl = wave; sl < full; sl += waves) {
+        const int64_t kb = sl * kSlice;
+        uint4 xv[MT][U], wv[TB][U];
+#pragma unroll
+        for (int t = 0; t < U; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xv[mt][t] = load16(xrow[mt] + kb + 64 * t);
+#pragma unroll
+        for (int r = 0; r < TB; ++r)
+#pragma unroll
+            for (int t = 0; t < U; ++t) wv[r][t] = load16(wrow[r] + kb + 64 * t);
+        transpose(xv);
+#pragma unroll
+        for (int r = 0; r < TB; ++r) mma(acc[r], xv, wv[r]);
+    }
+    if (full < slices && wave == full % waves) {  // the partial last slice
+        const int64_t kb = full * kSlice;
+        uint4 xv[MT][U], wv[TB][U];
+#pragma unroll
+        for (int t = 0; t < U; ++t) {
+            const bool in = kb + 64 * t + 16 * xp < k;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xv[mt][t] = in ? load16(xrow[mt] + kb + 64 * t) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < TB; ++r)
+#pragma unroll
+            for (int t = 0; t < U; ++t) {
+                const bool in = kb + 64 * t + 16 * g < k;
+                wv[r][t] = in ? load16(wrow[r] + kb + 64 * t) : make_uint4(0, 0, 0, 0);
+            }
+        transpose(xv);
+#pragma unroll
+        for (int r = 0; r < TB; ++r) mma(acc[r], xv, wv[r]);
     }
 
-    // intra-block reduction over the waves, in wave order
-    if constexpr (WPB > 1) {
-        __shared__ int32_t red[WPB - 1][MT][4][64];
-        if (wave > 0) {
+    // every wave publishes its partials; each wave then reduces a share of the fragments in wave order
+    constexpr int kFrags = TB * MT;
+    if (waves > 1) {
+        int32_t *mine = red + (int64_t)wave * (kFrags * 256);
+#pragma unroll
+        for (int r = 0; r < TB; ++r)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = (r * MT + mt) * 256 + i * 64 + lane;
                     if constexpr (QT == kInt8)
-                        red[wave - 1][mt][r][lane] = acc[mt][r];
+                        mine[idx] = acc[r][mt][i];
                     else
-                        red[wave - 1][mt][r][lane] = __float_as_int(acc[mt][r]);
+                        mine[idx] = __float_as_int(acc[r][mt][i]);
                 }
-        }
         __syncthreads();
-        if (wave > 0) return;
-#pragma unroll
-        for (int w = 0; w < WPB - 1; ++w)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (QT == kInt8)
-                        acc[mt][r] += red[w][mt][r][lane];
-                    else
-                        acc[mt][r] += __int_as_float(red[w][mt][r][lane]);
-                }
     }
-
-    // inter-block split of K: publish the partial, the last block of the tile reduces in split order
-    if (splits > 1) {
-        const int64_t slot = (int64_t)blockIdx.z * n_tiles + tile;
-        int32_t *__restrict__ mine = partials + (slot * splits + split) * (MT * 256);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+    for (int r = 0; r < TB; ++r)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (QT == kInt8)
-                    mine[mt * 256 + r * 64 + lane] = acc[mt][r];
-                else
-                    mine[mt * 256 + r * 64 + lane] = __float_as_int(acc[mt][r]);
-            }
-        __threadfence();  // release the partial to the whole device (all XCDs)
-        uint32_t old = 0;
-        if (lane == 0) old = atomicAdd(counters + slot, 1u);
-        old = __shfl(old, 0, 64);
-        if (old != (uint32_t)(splits - 1)) return;
-        __threadfence();  // acquire the other blocks' partials
-        const int32_t *__restrict__ all = partials + slot * splits * (MT * 256);
+        for (int mt = 0; mt < MT; ++mt) {
+            const int f = r * MT + mt;
+            if (waves > 1) {
+                if (f % waves != wave) continue;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = mt * 256 + r * 64 + lane;
-                if constexpr (QT == kInt8) {
-                    int32_t sum = all[idx];
-                    for (int s2 = 1; s2 < splits; ++s2) sum += all[s2 * (MT * 256) + idx];
-                    acc[mt][r] = sum;
-                } else {
-                    float sum = __int_as_float(all[idx]);
-                    for (int s2 = 1; s2 < splits; ++s2) sum += __int_as_float(all[s2 * (MT * 256) + idx]);
-                    acc[mt][r] = sum;
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = f * 256 + i * 64 + lane;
+                    if constexpr (QT == kInt8) {
+                        int32_t sum = red[idx];
+                        for (int w = 1; w < waves; ++w) sum += red[(int64_t)w * (kFrags * 256) + idx];
+                        acc[r][mt][i] = sum;
+                    } else {
+                        float sum = __int_as_float(red[idx]);
+                        for (int w = 1; w < waves; ++w) sum += __int_as_float(red[(int64_t)w * (kFrags * 256) + idx]);
+                        acc[r][mt][i] = sum;
+                    }
                 }
             }
-        if (lane == 0) counters[slot] = 0u;  // leave the workspace zeroed for the next call
-    }
-
-    // epilogue: y = acc * x_scale[row] * w_scale[col]
-    if (ncol < n) {
-        const float sw = ws[ncol];
+            // epilogue: y = acc * x_scale[row] * w_scale[col]
+            const int64_t col = (tile0 + r) * 16 + j;
+            if (col >= n) continue;
+            const float sw = ws[col];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + mt * 16 + 4 * g + r;
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + mt * 16 + 4 * g + i;
                 if (row < m) {
-                    const float v = acc_to_f32(acc[mt][r]) * xs[row] * sw;
-                    store_y(y, row * n + ncol, v, y_bf16 != 0);
-                    if (acc_out != nullptr) store_acc(acc_out, row * n + ncol, acc[mt][r]);
+                    const float v = acc_to_f32(acc[r][mt][i]) * xs[row] * sw;
+                    store_y(y, row * n + col, v, y_bf16 != 0);
+                    if (acc_out != nullptr) store_acc(acc_out, row * n + col, acc[r][mt][i]);
                 }
             }
-    }
+        }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -315,39 +335,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(int64_t m, int64_t n, int64_t
     }
 }
 
-template <int QT, int MT, int WPB>
+template <int QT, int MT, int U, int TB, int WMAX>
 void launch_gemv_t(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
-                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
-                   hipStream_t stream) {
+                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
     const int64_t m_blocks = (m + 16 * MT - 1) / (16 * MT);
-    int32_t *partials = nullptr;
-    uint32_t *counters = nullptr;
-    if (p.splits > 1) {
-        counters = static_cast<uint32_t *>(workspace);
-        partials = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
-    }
-    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)m_blocks);
-    hipLaunchKernelGGL((gemv_kernel<QT, MT, WPB>), grid, dim3(WPB * 64), 0, stream, m, n, k, xq, xs, wq, ws, y,
-                       y_bf16 ? 1 : 0, acc_out, p.splits, p.n_tiles, partials, counters);
+    const dim3 grid((unsigned)((p.n_tiles + TB - 1) / TB), (unsigned)m_blocks);
+    const size_t lds = p.waves > 1 ? (size_t)p.waves * TB * MT * 256 * 4 : 0;
+    hipLaunchKernelGGL((gemv_kernel<QT, MT, U, TB, WMAX>), grid, dim3(p.waves * 64), lds, stream, m, n, k, xq, xs, wq,
+                       ws, y, y_bf16 ? 1 : 0, acc_out);
+}
+
+// (m_tiles, unroll, tiles per block, most waves per block); the planner further limits the waves so that the
+// reduction's LDS, waves x TB x MT KiB, stays within 64 KiB.
+#define QR_GEMV_VARIANTS(X) \
+    X(1, 4, 1, 16) X(1, 4, 2, 16) X(1, 4, 4, 16) X(1, 8, 1, 16) X(1, 8, 2, 16) \
+    X(2, 4, 1, 16) X(2, 4, 2, 16) X(2, 8, 1, 16) \
+    X(4, 2, 1, 16) X(4, 2, 2, 16) X(4, 4, 1, 8)
+
+// most waves per block of a variant, 0 if it does not exist
+int gemv_variant_waves(int mt, int u, int tb) {
+#define QR_GEMV_HAS(MT_, U_, TB_, W_) if (mt == MT_ && u == U_ && tb == TB_) return W_;
+    QR_GEMV_VARIANTS(QR_GEMV_HAS)
+#undef QR_GEMV_HAS
+    return 0;
 }
 
 template <int QT>
 void launch_gemv_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
-                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
-                   hipStream_t stream) {
-#define QR_GEMV_CASE(MT_, W_)                                                                                   \
-    if (p.m_tiles == MT_ && p.waves == W_) {                                                                    \
-        launch_gemv_t<QT, MT_, W_>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);           \
+                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+#define QR_GEMV_CASE(MT_, U_, TB_, W_)                                                                          \
+    if (p.m_tiles == MT_ && p.unroll == U_ && p.tiles == TB_) {                                                 \
+        launch_gemv_t<QT, MT_, U_, TB_, W_>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);            \
         return;                                                                                                 \
     }
-    QR_GEMV_CASE(1, 4)
-    QR_GEMV_CASE(2, 4)
-    QR_GEMV_CASE(4, 4)
-    QR_GEMV_CASE(1, 8)
-    QR_GEMV_CASE(2, 8)
-    QR_GEMV_CASE(4, 8)
-    QR_GEMV_CASE(1, 2)
-    QR_GEMV_CASE(1, 1)
+    QR_GEMV_VARIANTS(QR_GEMV_CASE)
 #undef QR_GEMV_CASE
     // plan_linear only produces the cases above
     abort();
@@ -366,49 +387,56 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     LinearPlan p{};
     const int force = env_int("QR_FORCE_VARIANT", -1);  // 0 = GEMV, 1 = tiled GEMM
     const bool gemv = force == 0 || (force != 1 && m <= 64);
+    p.ws_bytes = 0;
+    p.splits = 1;
     if (!gemv) {
         p.kind = 1;
-        p.ws_bytes = 0;
         return p;
     }
     p.kind = 0;
     p.m_tiles = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-    int waves = env_int("QR_GEMV_WAVES", 4);
-    if (waves != 1 && waves != 2 && waves != 4 && waves != 8) waves = 4;
-    if (p.m_tiles > 1 && waves == 2) waves = 4;
-    if (p.m_tiles > 1 && waves == 1) waves = 4;
-    p.waves = waves;
     p.n_tiles = (n + 15) / 16;
-    const int64_t steps = (k + kStep - 1) / kStep;
     const int64_t m_blocks = (m + 16 * p.m_tiles - 1) / (16 * p.m_tiles);
-    // enough blocks to keep every CU streaming; never more splits than K steps per wave allow
-    const int64_t target = env_int("QR_GEMV_TARGET_BLOCKS", 1024);
-    int64_t splits = (target + p.n_tiles * m_blocks - 1) / (p.n_tiles * m_blocks);
-    const int64_t max_split = steps / p.waves > 0 ? steps / p.waves : 1;
-    if (splits > max_split) splits = max_split;
-    if (splits < 1) splits = 1;
-    const int forced = env_int("QR_SPLITK", 0);
-    if (forced > 0) splits = forced < steps ? forced : steps;
-    if (splits > 65535) splits = 65535;
-    // split-K needs one counter per output tile; they live in a fixed region at the start of the workspace
-    if (m_blocks * p.n_tiles > kMaxCounters) splits = 1;
-    p.splits = (int)splits;
-    if (p.splits > 1) {
-        p.ws_bytes = kCounterBytes + (size_t)(m_blocks * p.n_tiles) * (size_t)p.splits * (size_t)(p.m_tiles * 256) * 4;
-    } else {
-        p.ws_bytes = 0;
+    // slices of 256 bytes (128 for four token tiles) unless overridden
+    int u = p.m_tiles == 4 ? 2 : 4;
+    // more tiles per block share each activation load; keep at least ~1000 blocks in flight
+    const int64_t min_blocks = env_int("QR_GEMV_MIN_BLOCKS", 1024);
+    int tb = 1;
+    for (int cand : {4, 2}) {
+        if (gemv_variant_waves(p.m_tiles, u, cand) == 0) continue;
+        if (((p.n_tiles + cand - 1) / cand) * m_blocks >= min_blocks) {
+            tb = cand;
+            break;
+        }
     }
+    const int fu = env_int("QR_GEMV_UNROLL", 0), ft = env_int("QR_GEMV_TILES", 0);
+    if ((fu > 0 || ft > 0) && gemv_variant_waves(p.m_tiles, fu > 0 ? fu : u, ft > 0 ? ft : tb) > 0) {
+        u = fu > 0 ? fu : u;
+        tb = ft > 0 ? ft : tb;
+    }
+    p.unroll = u;
+    p.tiles = tb;
+    const int64_t slices = (k + 64 * u - 1) / (64 * u);
+    // the reduction's LDS (waves x tb x m_tiles KiB) stays within 64 KiB
+    int cap = gemv_variant_waves(p.m_tiles, u, tb);
+    if (cap > 64 / (tb * p.m_tiles)) cap = 64 / (tb * p.m_tiles);
+    int64_t waves = slices < cap ? slices : cap;
+    const int forced_w = env_int("QR_GEMV_WAVES", 0);
+    if (forced_w >= 1 && forced_w <= cap) waves = forced_w;
+    p.waves = (int)(waves < 1 ? 1 : waves);
+    p.prefetch = true;
     return p;
 }
 
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          void *workspace, hipStream_t stream) {
+    (void)workspace;
     if (p.kind == 0) {
         if (qtype == kInt8)
-            launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+            launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
         else
-            launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+            launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
     } else {
         const int64_t tiles_m = (m + kBM - 1) / kBM, tiles_n = (n + kBN - 1) / kBN;
         const dim3 grid((unsigned)(tiles_m * tiles_n));

@@ -110,22 +110,49 @@ def test_fp8_determinism():
     assert np.array_equal(a, b)
 
 
-def test_workspace_is_left_zeroed():
+def test_no_workspace_needed():
+    """Every plan reduces inside its blocks: the call works with no workspace at all."""
     xc, xs, wc, ws = _quantized_operands(16, 1536, 8960, O.INT8, seed=79)
-    nbytes = qr.qr_workspace_bytes(qr.QR_INT8, 16, 1536, 8960)
-    assert nbytes > 0
-    wsp = qr.Workspace()
-    buf = wsp.get(nbytes)
-    for _ in range(3):
-        qr.qr_w8a8_linear(qr.QR_INT8, dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
+    assert qr.qr_workspace_bytes(qr.QR_INT8, 16, 1536, 8960) == 0
+    y_ref, acc_i, _ = O.linear(O.INT8, xc, xs, wc, ws, O.BF16)
+    y = torch.empty((16, 1536), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty((16, 1536), dtype=torch.int32, device="cuda")
+    L = qr.lib()
+    ops = [dev(a) for a in (xc, xs, wc, ws)]  # kept alive until the kernel has run
+    rc = L.qr_w8a8_linear(qr.QR_INT8, 16, 1536, 8960, *[t.data_ptr() for t in ops], y.data_ptr(), qr.QR_BF16,
+                          acc.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
     torch.cuda.synchronize()
-    counters = buf[:262144].view(torch.int32)  # the fixed split-K counter region
-    assert int(counters.abs().sum()) == 0
+    assert np.array_equal(host(acc), acc_i)
+    assert_y_close(host(y), y_ref, "no workspace")
+
+
+# every compiled GEMV variant: (token tiles, 64-byte loads per slice, weight tiles per block)
+GEMV_VARIANTS = [(1, 4, 1), (1, 4, 2), (1, 4, 4), (1, 8, 1), (1, 8, 2), (2, 4, 1), (2, 4, 2), (2, 8, 1),
+                 (4, 2, 1), (4, 2, 2), (4, 4, 1)]
+
+
+@pytest.mark.parametrize("mt,u,tb", GEMV_VARIANTS)
+def test_every_gemv_variant(mt, u, tb, monkeypatch, capfd):
+    """Each variant, forced through the planner's overrides, on ragged shapes: n not a multiple of the block's
+    16 tb channels, k with a partial last slice, m not a multiple of 16 -- INT8 accumulators bit-exact, FP8
+    and bf16 outputs within the tolerance."""
+    monkeypatch.setenv("QR_GEMV_UNROLL", str(u))
+    monkeypatch.setenv("QR_GEMV_TILES", str(tb))
+    monkeypatch.setenv("QR_TRACE", "1")
+    m = {1: 13, 2: 29, 4: 61}[mt]
+    for oq in (O.INT8, O.FP8):
+        for i, (n, k) in enumerate([(16 * tb * 3 + 5, 64 * u * 3 + 48), (200, 64 * u * 17 + 16)]):
+            xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=900 + 10 * i + oq)
+            log("variant mt=%d u=%d tb=%d %s m=%d n=%d k=%d" % (mt, u, tb, oq, m, n, k))
+            _check(oq, xc, xs, wc, ws, "variant mt=%d u=%d tb=%d m=%d n=%d k=%d" % (mt, u, tb, m, n, k))
+            err = capfd.readouterr().err
+            assert "mt=%d" % mt in err and "unroll=%d tiles=%d" % (u, tb) in err, err
 
 
 def test_workspace_reuse_across_plans():
-    """One workspace serves a sequence of differently split shapes (partials of one plan must never land in
-    another plan's counters): every call stays bit-exact (INT8) or within tolerance (FP8)."""
+    """One workspace object serves a sequence of differently planned shapes: every call stays bit-exact (INT8)
+    or within tolerance (FP8)."""
     wsp = qr.Workspace()
     wsp.get(64 << 20)
     shapes = [(64, 64, 4096), (1, 1536, 8960), (16, 200, 1552), (33, 130, 784), (1, 2048, 8960), (64, 64, 4096),
