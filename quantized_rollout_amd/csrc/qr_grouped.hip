@@ -141,6 +141,11 @@ __device__ __forceinline__ void count_word(uint32_t a, uint32_t b, bool fp8, uns
     }
 }
 
+// One streaming pass over both code sets: each lane keeps kCountUnroll pairs of 16-byte loads in flight (grid-
+// stride over 16-byte words), compares bytes four at a time, and the counts are summed over the wave and added
+// with one 64-bit atomic per wave and count.
+constexpr int kCountUnroll = 4;
+
 __global__ __launch_bounds__(256) void count_kernel(const uint8_t *__restrict__ a, const uint8_t *__restrict__ b,
                                                     int64_t count, int fp8, const uint32_t *__restrict__ sa,
                                                     const uint32_t *__restrict__ sb, int64_t n_scales,
@@ -151,15 +156,31 @@ __global__ __launch_bounds__(256) void count_kernel(const uint8_t *__restrict__ 
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(a);
     const uint4 *__restrict__ b4 = reinterpret_cast<const uint4 *>(b);
-    for (int64_t i = tid; i < n16; i += stride) {
+    int64_t i = tid;
+    for (; i + (kCountUnroll - 1) * stride < n16; i += kCountUnroll * stride) {
+        uint4 x[kCountUnroll], z[kCountUnroll];
+#pragma unroll
+        for (int u = 0; u < kCountUnroll; ++u) {
+            x[u] = a4[i + u * stride];
+            z[u] = b4[i + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < kCountUnroll; ++u) {
+            count_word(x[u].x, z[u].x, fp8 != 0, nb, nv);
+            count_word(x[u].y, z[u].y, fp8 != 0, nb, nv);
+            count_word(x[u].z, z[u].z, fp8 != 0, nb, nv);
+            count_word(x[u].w, z[u].w, fp8 != 0, nb, nv);
+        }
+    }
+    for (; i < n16; i += stride) {
         const uint4 x = a4[i], z = b4[i];
         count_word(x.x, z.x, fp8 != 0, nb, nv);
         count_word(x.y, z.y, fp8 != 0, nb, nv);
         count_word(x.z, z.z, fp8 != 0, nb, nv);
         count_word(x.w, z.w, fp8 != 0, nb, nv);
     }
-    for (int64_t i = n16 * 16 + tid; i < count; i += stride) count_word(a[i], b[i], fp8 != 0, nb, nv);
-    for (int64_t i = tid; i < n_scales; i += stride) ns += (sa[i] != sb[i]) ? 1ull : 0ull;
+    for (int64_t t = n16 * 16 + tid; t < count; t += stride) count_word(a[t], b[t], fp8 != 0, nb, nv);
+    for (int64_t t = tid; t < n_scales; t += stride) ns += (sa[t] != sb[t]) ? 1ull : 0ull;
 
     nb = wave_sum_u64(nb);
     nv = wave_sum_u64(nv);
@@ -203,9 +224,11 @@ hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t coun
     hipLaunchKernelGGL(zero3_kernel, dim3(1), dim3(64), 0, stream, o);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // enough 256-thread blocks for every CU to hold several (2048 = 256 CUs x 8), fewer for small inputs
     const int64_t work = count / 16 > n_scales ? count / 16 : n_scales;
-    int64_t blocks = (work + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    int64_t blocks = (work + 256 * kCountUnroll - 1) / (256 * kCountUnroll);
+    const int64_t max_blocks = env_int("QR_COUNT_BLOCKS", 2048);
+    if (blocks > max_blocks) blocks = max_blocks;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(count_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, b, count,
                        qtype == kFp8 ? 1 : 0, reinterpret_cast<const uint32_t *>(sa),

@@ -1,10 +1,11 @@
 // qr_quantize.hip -- per-row absmax quantization to INT8 / FP8 E4M3 (weights and activations).
 //
-// One workgroup per row. The row is streamed from HBM once in coalesced 16-byte chunks and kept in VGPRs
-// (up to 8 chunks per lane); the absmax is reduced across the wavefront with DPP/permute shuffles and across
-// wavefronts through LDS; the second pass divides by the scale, rounds and stores the codes. Rows longer
-// than the register budget re-read the remainder (it is still in L2). Workgroup size follows the row length
-// so that each lane holds a few chunks.
+// One row per wavefront team: rows of up to 512 16-byte chunks (bf16 k <= 4096, fp32 k <= 2048) take one
+// wavefront each, four rows per workgroup; longer rows take a workgroup of 2..16 wavefronts. The row is
+// streamed from HBM once in coalesced 16-byte chunks and kept in VGPRs (up to 8 chunks per lane); the absmax
+// is reduced across the wavefront with shuffles and, for multi-wave rows, across wavefronts through LDS; the
+// second pass divides by the scale, rounds and stores the codes. Rows longer than the register budget
+// re-read the remainder (it is still in L2).
 //
 // The arithmetic follows the quantizer of "QaRL: Rollout-Aligned Quantization-Aware RL ...", section 2.2
 // (integer Quant with zero point 0; floating-point Quant with s = max|W| / alpha), with per-output-channel
@@ -48,15 +49,18 @@ __device__ __forceinline__ void expand_chunk(const uint4 &c, const float *__rest
     }
 }
 
-template <bool BF16, int QT, int SMODE, int THREADS>
-__global__ __launch_bounds__(THREADS) void quantize_rows_kernel(const void *__restrict__ in, int64_t k,
-                                                                 const float *__restrict__ s,
-                                                                 uint8_t *__restrict__ codes,
-                                                                 float *__restrict__ scales) {
+// THREADS lanes per row, RPB rows per workgroup (RPB > 1 only with one-wavefront rows)
+template <bool BF16, int QT, int SMODE, int THREADS, int RPB>
+__global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void *__restrict__ in, int64_t rows,
+                                                                       int64_t k, const float *__restrict__ s,
+                                                                       uint8_t *__restrict__ codes,
+                                                                       float *__restrict__ scales) {
+    static_assert(RPB == 1 || THREADS == 64, "several rows per workgroup only with one-wavefront rows");
     constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
     constexpr float qmax = QMax<QT>::value;
-    const int64_t row = blockIdx.x;
-    const int t = threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * RPB + (RPB > 1 ? (int)(threadIdx.x >> 6) : 0);
+    if (row >= rows) return;  // whole wavefronts only (RPB > 1 implies one wavefront per row)
+    const int t = RPB > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
     const int64_t nch = k / E;
     const uint4 *__restrict__ src =
         reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(in) + row * k * (BF16 ? 2 : 4));
@@ -132,20 +136,21 @@ hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uin
     const int64_t nch = k / E;
     const dim3 grid((unsigned)rows);
     if (nch <= 64 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 64>), grid, dim3(64), 0, stream, in, k, s, codes,
-                           scales);
+        constexpr int kRows = 4;
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 64, kRows>), dim3((unsigned)((rows + kRows - 1) / kRows)),
+                           dim3(64 * kRows), 0, stream, in, rows, k, s, codes, scales);
     } else if (nch <= 128 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 128>), grid, dim3(128), 0, stream, in, k, s,
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 128, 1>), grid, dim3(128), 0, stream, in, rows, k, s,
                            codes, scales);
     } else if (nch <= 256 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 256>), grid, dim3(256), 0, stream, in, k, s,
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 256, 1>), grid, dim3(256), 0, stream, in, rows, k, s,
                            codes, scales);
     } else if (nch <= 512 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 512>), grid, dim3(512), 0, stream, in, k, s,
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 512, 1>), grid, dim3(512), 0, stream, in, rows, k, s,
                            codes, scales);
     } else {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 1024>), grid, dim3(1024), 0, stream, in, k, s,
-                           codes, scales);
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 1024, 1>), grid, dim3(1024), 0, stream, in, rows, k,
+                           s, codes, scales);
     }
     return hipGetLastError();
 }
