@@ -1,0 +1,593 @@
+// qr_gemm.hip -- the W8A8 linear for large batches: LDS-tiled MFMA GEMM (INT8 -> INT32, E4M3 -> FP32).
+//
+// y[i,c] = acc[i,c] * x_scale[i] * w_scale[c], acc = sum_j xq[i,j] * wq[c,j] -- the W8A8 product of quantized
+// rollout ("QuRL: Efficient Reinforcement Learning with Quantized Rollout", section 5; "QaRL: Rollout-Aligned
+// Quantization-Aware RL ...", sections 2.2 and 3.1) at the rollout batch sizes where the matrix cores, not HBM,
+// bound the layer.
+//
+// Workgroup tile BM x BN of outputs, four wavefronts in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2)
+// register tile of 16x16 MFMA fragments (256 accumulators per lane at 256 x 256). K advances in 128-byte
+// stages through two LDS buffers (rows padded to 144 bytes so that the sixteen rows a fragment read touches
+// fall on distinct banks); the global loads of stage s+1 are in flight while stage s runs its MFMAs. Both
+// operands are K-contiguous (codes in their canonical row-major layout), and a fragment read gives lane
+// (j, g) 16 bytes of row j at K offset 16 g of each 64-byte half of the stage, the same for activations and
+// weights, so the MFMA dot products are those of the plain definition. Workgroups are dispatched round-robin
+// over the 8 XCDs; the tile order gives each XCD a contiguous run of tiles, token tiles fastest, so the
+// workgroups that share a weight tile run on one XCD and share its L2.
+#include "qr_device.hpp"
+#include "qr_internal.hpp"
+
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
+namespace qr {
+namespace {
+
+// f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N-1>): indices known at compile time, so
+// register arrays (the accumulators) indexed by them stay in registers
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F &&f) {
+    unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int kBK = 128;            // K bytes per stage
+constexpr int kRow = kBK + 16;      // padded LDS row stride
+
+__device__ __forceinline__ v4i v4(const uint4 &a) { return v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w}; }
+__device__ __forceinline__ v8i v8(const uint4 &a, const uint4 &b) {
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+template <int QT, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(int64_t m, int64_t n, int64_t k,
+                                                            const uint8_t *__restrict__ xq,
+                                                            const float *__restrict__ xs,
+                                                            const uint8_t *__restrict__ wq,
+                                                            const float *__restrict__ ws, void *__restrict__ y,
+                                                            int y_bf16, void *__restrict__ acc_out, int tiles_m,
+                                                            int tiles_n) {
+    typedef typename Acc<QT>::type acc_t;
+    constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
+    constexpr int FM = WM / 16, FN = WN / 16;   // 16x16 fragments per wave
+    constexpr int CA = BM * kBK / 16 / 256;     // 16-byte chunks per thread per stage, activations
+    constexpr int CB = BN * kBK / 16 / 256;     // weights
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kRow];
+
+    // tile order: each XCD (workgroup id mod 8) takes a contiguous run of the order, token tiles fastest
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + 7) / 8;
+    const int order = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (order >= total) return;
+    const int64_t m0 = (int64_t)(order % tiles_m) * BM;
+    const int64_t n0 = (int64_t)(order / tiles_m) * BN;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int j = lane & 15, g = lane >> 4;
+
+    // global -> LDS staging: chunk c of a stage is row c >> 3, bytes 16 (c & 7); rows past the end re-read the
+    // last row (they only feed outputs that are never stored)
+    const uint8_t *arow[CA];
+    const uint8_t *brow[CB];
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+        const int c = t + 256 * i;
+        const int64_t r = m0 + (c >> 3);
+        arow[i] = xq + (r < m ? r : m - 1) * k + 16 * (c & 7);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+        const int c = t + 256 * i;
+        const int64_t r = n0 + (c >> 3);
+        brow[i] = wq + (r < n ? r : n - 1) * k + 16 * (c & 7);
+    }
+    uint4 ra[CA], rb[CB];
+    auto gload = [&](int64_t k0) {  // a full stage: every load in range, none conditional
+#pragma unroll
+        for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const uint4 *>(arow[i] + k0);
+#pragma unroll
+        for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const uint4 *>(brow[i] + k0);
+    };
+    auto gload_tail = [&](int64_t k0) {  // the partial last stage: bytes past k are zero
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int c = t + 256 * i;
+            ra[i] = k0 + 16 * (c & 7) < k ? *reinterpret_cast<const uint4 *>(arow[i] + k0) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int c = t + 256 * i;
+            rb[i] = k0 + 16 * (c & 7) < k ? *reinterpret_cast<const uint4 *>(brow[i] + k0) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int c = t + 256 * i;
+            *reinterpret_cast<uint4 *>(&lds[buf][(c >> 3) * kRow + 16 * (c & 7)]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int c = t + 256 * i;
+            *reinterpret_cast<uint4 *>(&lds[buf][(BM + (c >> 3)) * kRow + 16 * (c & 7)]) = rb[i];
+        }
+    };
+
+    acc_t acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) acc[a][b] = acc_t{0, 0, 0, 0};
+
+    auto compute = [&](int buf) {
+        const uint8_t *A = &lds[buf][(wm * WM + j) * kRow + 16 * g];
+        const uint8_t *B = &lds[buf][(BM + wn * WN + j) * kRow + 16 * g];
+        uint4 fa[FM][2], fb[FN][2];
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            fa[a][0] = *reinterpret_cast<const uint4 *>(A + a * 16 * kRow);
+            fa[a][1] = *reinterpret_cast<const uint4 *>(A + a * 16 * kRow + 64);
+        }
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            fb[b][0] = *reinterpret_cast<const uint4 *>(B + b * 16 * kRow);
+            fb[b][1] = *reinterpret_cast<const uint4 *>(B + b * 16 * kRow + 64);
+        }
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                if constexpr (QT == kInt8) {
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4(fa[a][0]), v4(fb[b][0]), acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4(fa[a][1]), v4(fb[b][1]), acc[a][b], 0, 0, 0);
+                } else {
+                    // format 0 = E4M3 for both operands; scale exponents 127 = 2^0 (no block scaling)
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        v8(fa[a][0], fa[a][1]), v8(fb[b][0], fb[b][1]), acc[a][b], 0, 0, 0, 127, 0, 127);
+                }
+            }
+    };
+
+    const int64_t full = k / kBK;
+    const int64_t stages = (k + kBK - 1) / kBK;
+    if (full > 0)
+        gload(0);
+    else
+        gload_tail(0);
+    sstore(0);
+    __syncthreads();
+    for (int64_t s = 0; s < stages; ++s) {
+        const int buf = (int)(s & 1);
+        const bool more = s + 1 < stages;
+        if (s + 1 < full)
+            gload((s + 1) * kBK);
+        else if (more)
+            gload_tail((s + 1) * kBK);
+        compute(buf);
+        if (more) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: y = acc * x_scale[row] * w_scale[col], the scales loaded together from clamped indices
+    float sw[FN];
+#pragma unroll
+    for (int b = 0; b < FN; ++b) {
+        const int64_t col = n0 + wn * WN + b * 16 + j;
+        sw[b] = ws[col < n ? col : n - 1];
+    }
+    unroll<FM>([&](auto A) {
+        constexpr int a = decltype(A)::value;
+        float sx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + wm * WM + a * 16 + 4 * g + i;
+            sx[i] = xs[row < m ? row : m - 1];
+        }
+        unroll<FN>([&](auto B) {
+            constexpr int b = decltype(B)::value;
+            const int64_t col = n0 + wn * WN + b * 16 + j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + wm * WM + a * 16 + 4 * g + i;
+                if (row < m && col < n) {
+                    const float v = acc_to_f32(acc[a][b][i]) * sx[i] * sw[b];
+                    if (y_bf16)
+                        static_cast<uint16_t *>(y)[row * n + col] = f32_to_bf16(v);
+                    else
+                        static_cast<float *>(y)[row * n + col] = v;
+                    if (acc_out != nullptr) {
+                        if constexpr (QT == kInt8)
+                            static_cast<int32_t *>(acc_out)[row * n + col] = acc[a][b][i];
+                        else
+                            static_cast<float *>(acc_out)[row * n + col] = acc[a][b][i];
+                    }
+                }
+            }
+        });
+    });
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Ring-pipelined GEMM: 256 x 256 outputs per workgroup, eight wavefronts (two per SIMD) of 128 x 64 outputs
+// each (4 x 2 fragments of the 32x32 MFMA: v_mfma_i32_32x32x32_i8, or v_mfma_scale_f32_32x32x64_f8f6f4 with
+// E4M3 operands and unit block scales), 128 accumulators per lane. K advances in 64-byte stages through a ring
+// of four LDS buffers filled straight from memory by buffer loads with the LDS flag (no registers in between),
+// up to three stages ahead of the MFMAs. A workgroup's loads are spread over all eight wavefronts: the rate at
+// which one wavefront's memory instructions are served is limited, so more wavefronts issuing them fetch
+// more per CU. Each buffer holds the stage's 256 activation rows then its 256 weight rows, 64 bytes each, with
+// logical 16-byte piece c of row r stored at physical piece c ^ ring_swizzle(r). The buffer resources bound
+// the rows (rows past m or n load zeros) and the partial last stage points its out-of-range pieces past the
+// end. A 32x32 fragment read gives lane l row (l & 31) and logical pieces (l >> 5) and 2 + (l >> 5) (INT8,
+// two MFMAs of K = 32) or 2 (l >> 5) and 2 (l >> 5) + 1 (FP8, one MFMA of K = 64), the same for both
+// operands, so the dot products are those of the plain definition. Result C[i][c] sits in lane
+// (c + 32 (i / 4 mod 2)), register 4 (i / 8) + i mod 4.
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kRingK = 64;        // K bytes per stage
+constexpr int kRingTile = 256;    // rows of each operand per stage
+constexpr int kRingBuf = 2 * kRingTile * kRingK;  // bytes per ring buffer (32 KiB)
+constexpr int kRingThreads = 1024;                // sixteen wavefronts, four per SIMD
+constexpr int kRingWaveM = 64, kRingWaveN = 64;   // outputs per wavefront (4 x 4 arrangement)
+constexpr int kBufferFlags = 0x00020000;          // raw buffer descriptor word 3 (32-bit untyped data)
+constexpr uint32_t kOutOfRange = 0x80000000u;      // a buffer offset past every operand (they stay below 2 GiB)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// piece permutation of a ring row (see above). A 16-byte-per-lane LDS read serves each half-wave as two
+// groups of 16 lanes (split by the parity of lane bits 2..4), each group in one cycle over 64 four-byte banks;
+// the lanes of a fragment read are 32 consecutive rows at one logical piece, so a group is conflict-free when
+// its rows with equal (r mod 4) hold that piece at distinct physical pieces, which (r / 4) mod 4 provides.
+__device__ __forceinline__ int ring_swizzle(int r) { return (r >> 2) & 3; }
+
+template <int QT>
+struct Acc32;
+template <>
+struct Acc32<kInt8> {
+    typedef int __attribute__((ext_vector_type(16))) type;
+};
+template <>
+struct Acc32<kFp8> {
+    typedef float __attribute__((ext_vector_type(16))) type;
+};
+
+// One 16-byte-per-lane buffer load straight into LDS: lane l's 16 bytes land at lds_base + 16 l. Issued as
+// assembly so that the compiler neither tracks it nor inserts its own waits for the LDS it writes: the kernel
+// counts these loads itself (vmcnt) and orders them with the workgroup barrier. M0 (the LDS base register)
+// is restored afterwards.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, uint32_t voffset) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(voffset), "s"(rsrc)
+        : "memory");
+}
+
+// Raw buffer descriptor (32-bit untyped elements, no stride): base, num_records bytes; loads at offsets
+// >= num_records return zero.
+__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = kBufferFlags;
+    return r;
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+// LDS address of a wave-uniform pointer, as a scalar
+__device__ __forceinline__ uint32_t lds_addr(uint8_t *p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)(lds_u8_t *)p);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt with the vector-memory counter at N and the LDS counter at zero
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// workgroup barrier that the compiler may not move memory accesses across (the loads into LDS it cannot see
+// are ordered by it)
+__device__ __forceinline__ void barrier_fenced() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int QT>
+__global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, int64_t n, int64_t k,
+                                                                    const uint8_t *__restrict__ xq,
+                                                                    const float *__restrict__ xs,
+                                                                    const uint8_t *__restrict__ wq,
+                                                                    const float *__restrict__ ws,
+                                                                    void *__restrict__ y, int y_bf16,
+                                                                    void *__restrict__ acc_out, int tiles_m,
+                                                                    int tiles_n) {
+    typedef typename Acc32<QT>::type acc_t;
+    constexpr int FA = kRingWaveM / 32, FB = kRingWaveN / 32;  // 32x32 fragments per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kRingBuf];  // stage s in buffer s mod 4
+
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + 7) / 8;
+    const int order = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (order >= total) return;
+    const int64_t m0 = (int64_t)(order % tiles_m) * kRingTile;
+    const int64_t n0 = (int64_t)(order / tiles_m) * kRingTile;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave / (kRingTile / kRingWaveN), wn = wave % (kRingTile / kRingWaveN);
+
+    // buffer resources over the whole operands: rows past the end load zeros
+    const v4i rsa = make_rsrc(xq, (uint32_t)(m * k));
+    const v4i rsb = make_rsrc(wq, (uint32_t)(n * k));
+
+    // stage loads: wave w fills rows 32 w .. 32 w + 31 of each operand, 16 rows per instruction; lane l writes
+    // piece l & 3 of row 16 q + l / 4 of its block, which holds logical piece (l & 3) ^ swz(row)
+    constexpr int kRowsPerWave = kRingTile / (kRingThreads / 64);
+    constexpr int kLoadsPerOperand = kRowsPerWave / 16;
+    constexpr int kLoadsPerStage = 2 * kLoadsPerOperand;  // vmcnt per stage per wave
+    uint32_t offa[kLoadsPerOperand], offb[kLoadsPerOperand];
+    int lpiece[kLoadsPerOperand];
+#pragma unroll
+    for (int q = 0; q < kLoadsPerOperand; ++q) {
+        const int r = wave * kRowsPerWave + q * 16 + (lane >> 2);
+        lpiece[q] = (lane & 3) ^ ring_swizzle(r);
+        offa[q] = m0 + r < m ? (uint32_t)((m0 + r) * k + 16 * lpiece[q]) : kOutOfRange;
+        offb[q] = n0 + r < n ? (uint32_t)((n0 + r) * k + 16 * lpiece[q]) : kOutOfRange;
+    }
+    const int64_t stages = (k + kRingK - 1) / kRingK;
+    const int64_t full = k / kRingK;
+    // load number idx (0 .. kLoadsPerStage - 1) of stage st: operand idx & 1, rows block idx >> 1
+    auto issue_one = [&](int64_t st, uint8_t *buf, int idx) {
+        const uint32_t k0 = (uint32_t)(st * kRingK);
+        const int q = idx >> 1;
+        const bool in = st < full || (int64_t)k0 + 16 * lpiece[q] < k;
+        const uint32_t off = (idx & 1) ? offb[q] : offa[q];
+        const uint32_t o = (in && off != kOutOfRange) ? off + k0 : kOutOfRange;
+        dma16((idx & 1) ? rsb : rsa,
+              lds_addr(buf + ((idx & 1) * kRingTile + wave * kRowsPerWave + q * 16) * kRingK), o);
+    };
+    auto issue = [&](int64_t st, uint8_t *buf) {
+#pragma unroll
+        for (int idx = 0; idx < kLoadsPerStage; ++idx) issue_one(st, buf, idx);
+    };
+
+    acc_t acc[FA][FB];
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j) acc[i][j] = acc_t{};
+
+    // fragment reads: lane row (l & 31), half h = l >> 5
+    const int fr = lane & 31, h = lane >> 5;
+    const int p0 = QT == kInt8 ? h : 2 * h, p1 = QT == kInt8 ? 2 + h : 2 * h + 1;
+    auto read_frags = [&](const uint8_t *buf, uint4 (&fa)[FA][2], uint4 (&fb)[FB][2]) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i) {
+            const int r = wm * kRingWaveM + i * 32 + fr;
+            const int sw = ring_swizzle(r);
+            fa[i][0] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (p0 ^ sw));
+            fa[i][1] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (p1 ^ sw));
+        }
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+            const int r = wn * kRingWaveN + j * 32 + fr;
+            const int sw = ring_swizzle(r);
+            fb[j][0] = *reinterpret_cast<const uint4 *>(buf + (kRingTile + r) * kRingK + 16 * (p0 ^ sw));
+            fb[j][1] = *reinterpret_cast<const uint4 *>(buf + (kRingTile + r) * kRingK + 16 * (p1 ^ sw));
+        }
+    };
+    auto mfmas = [&](const uint4 (&fa)[FA][2], const uint4 (&fb)[FB][2]) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+            for (int j = 0; j < FB; ++j) {
+                if constexpr (QT == kInt8) {
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(fa[i][0]), v4(fb[j][0]), acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(fa[i][1]), v4(fb[j][1]), acc[i][j], 0, 0, 0);
+                } else {
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        v8(fa[i][0], fa[i][1]), v8(fb[j][0], fb[j][1]), acc[i][j], 0, 0, 0, 127, 0, 127);
+                }
+            }
+    };
+    // wait until this wave's loads of a stage have landed, `later` = stages issued after it (0..3), and until
+    // its own fragment reads are done; then the barrier makes every wave's loads of that stage visible and
+    // tells every wave that all fragment reads issued before it are complete
+    auto sync_stage = [&](int64_t later) {
+        if (later >= 3)
+            wait_vmcnt_lgkm0<3 * kLoadsPerStage>();
+        else if (later == 2)
+            wait_vmcnt_lgkm0<2 * kLoadsPerStage>();
+        else if (later == 1)
+            wait_vmcnt_lgkm0<kLoadsPerStage>();
+        else
+            wait_vmcnt_lgkm0<0>();
+        barrier_fenced();
+    };
+
+    // Pipeline: stage st + 3 is loaded while stage st runs. Each step waits for its own stage, refills the
+    // buffer of stage st - 1 (which every wave has finished reading before the barrier of step st) with stage
+    // st + 3, reads its fragments and runs its MFMAs; the four wavefronts of a SIMD cover each other's
+    // fragment reads.
+    uint4 fa[FA][2], fb[FB][2];
+    auto buffer = [&](int64_t st) { return ring + (int)(st & 3) * kRingBuf; };
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        if (i < stages) issue(i, ring + i * kRingBuf);
+    int64_t st = 0;
+    for (; st + 3 < stages; ++st) {  // steady: two later stages in flight, one more issued here
+        sync_stage(2);
+        issue(st + 3, buffer(st + 3));
+        read_frags(buffer(st), fa, fb);
+        mfmas(fa, fb);
+    }
+    for (; st < stages; ++st) {  // the last (up to) three stages: nothing more to issue
+        sync_stage(stages - st - 1);
+        read_frags(buffer(st), fa, fb);
+        mfmas(fa, fb);
+    }
+    wait_vmcnt<0>();  // no load may still be writing LDS when the wave ends
+
+    // epilogue: y = acc * x_scale[row] * w_scale[col], the scales loaded together from clamped indices
+    const int64_t wrow0 = m0 + wm * kRingWaveM, wcol0 = n0 + wn * kRingWaveN;
+    float sw[FB];
+#pragma unroll
+    for (int j = 0; j < FB; ++j) {
+        const int64_t col = wcol0 + j * 32 + fr;
+        sw[j] = ws[col < n ? col : n - 1];
+    }
+    // uniform over the workgroup (the barrier below is reached by every wavefront or by none)
+    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + kRingTile <= n;
+    if (fast) {
+        // bf16 tile through LDS: each wave converts its outputs into its own part of the ring (row stride
+        // 2 kRingWaveN bytes), then writes 16-byte row pieces with buffer stores (rows past m fall outside the
+        // buffer and are dropped) instead of scattered 2-byte stores
+        constexpr int kStride = 2 * kRingWaveN;
+        constexpr int kPieces = kRingWaveM * kStride / 16 / 64;  // 16-byte stores per lane
+        __syncthreads();  // every wave is done with the ring
+        uint8_t *stage = ring + wave * (kRingWaveM * kStride);
+        unroll<FA>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            float sx[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                sx[e] = xs[row < m ? row : m - 1];
+            }
+            unroll<FB>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int r = i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                    const float v = acc_to_f32(acc[i][j][e]) * sx[e] * sw[j];
+                    *reinterpret_cast<uint16_t *>(stage + r * kStride + (j * 32 + fr) * 2) = f32_to_bf16(v);
+                }
+            });
+        });
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)(m * n * 2), kBufferFlags);
+#pragma unroll 8
+        for (int q = 0; q < kPieces; ++q) {
+            const int c = lane + 64 * q;  // 16-byte piece: row c / (kStride / 16), 8 columns from 8 (c % ...)
+            const int r = c / (kStride / 16), c8 = (c % (kStride / 16)) * 8;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kStride + c8 * 2);
+            const int64_t row = wrow0 + r;
+            const uint32_t off = row < m ? (uint32_t)((row * n + wcol0 + c8) * 2) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ry, off, 0, 0);
+        }
+        return;
+    }
+    unroll<FA>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        float sx[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+            sx[e] = xs[row < m ? row : m - 1];
+        }
+        unroll<FB>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const int64_t col = wcol0 + j * 32 + fr;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                if (row < m && col < n) {
+                    const float v = acc_to_f32(acc[i][j][e]) * sx[e] * sw[j];
+                    if (y_bf16)
+                        static_cast<uint16_t *>(y)[row * n + col] = f32_to_bf16(v);
+                    else
+                        static_cast<float *>(y)[row * n + col] = v;
+                    if (acc_out != nullptr) {
+                        if constexpr (QT == kInt8)
+                            static_cast<int32_t *>(acc_out)[row * n + col] = acc[i][j][e];
+                        else
+                            static_cast<float *>(acc_out)[row * n + col] = acc[i][j][e];
+                    }
+                }
+            }
+        });
+    });
+}
+
+template <int QT>
+hipError_t launch_ring(int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs, const uint8_t *wq,
+                       const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+    const int tiles_m = (int)((m + kRingTile - 1) / kRingTile), tiles_n = (int)((n + kRingTile - 1) / kRingTile);
+    const int total = tiles_m * tiles_n;
+    const int grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((gemm_ring_kernel<QT>), dim3(grid), dim3(kRingThreads), 0, stream, m, n, k, xq, xs, wq, ws, y,
+                       y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int QT, int BM, int BN>
+hipError_t launch_t(int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs, const uint8_t *wq,
+                    const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+    const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
+    const int total = tiles_m * tiles_n;
+    const int grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((gemm_tiled_kernel<QT, BM, BN>), dim3(grid), dim3(256), 0, stream, m, n, k, xq, xs, wq, ws, y,
+                       y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int QT>
+hipError_t launch_q(int tile, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs, const uint8_t *wq,
+                    const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+    switch (tile) {
+        case kGemmRing: return launch_ring<QT>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+        case 1: return launch_t<QT, 256, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+        case 2: return launch_t<QT, 128, 256>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+        default: return launch_t<QT, 128, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+    }
+}
+
+}  // namespace
+
+bool gemm_ring_fits(int64_t m, int64_t n, int64_t k) {
+    // every buffer offset of the ring kernel (operands, bf16 output) stays below 2^31
+    const int64_t lim = (int64_t)1 << 31;
+    return m * k < lim && n * k < lim && m * n * 2 < lim;
+}
+
+int gemm_pick_tile(int64_t m, int64_t n, int64_t k) {
+    auto count = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    const bool ring = gemm_ring_fits(m, n, k);
+    const int forced = env_int("QR_GEMM_TILE", -1);
+    if (forced >= 1 && forced <= 3) return forced;
+    if (forced == kGemmRing && ring) return kGemmRing;
+    // the ring kernel once a quarter of the CUs get a 256 x 256 tile; below that, 128 x 128 tiles keep more
+    // CUs busy
+    if (ring && count(256, 256) >= 64) return kGemmRing;
+    if (count(256, 128) >= 256) return 1;
+    if (count(128, 256) >= 256) return 2;
+    return 3;
+}
+
+hipError_t launch_gemm_tiled(int tile, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                             const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                             hipStream_t stream) {
+    if (qtype == kInt8) return launch_q<kInt8>(tile, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+    return launch_q<kFp8>(tile, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+}
+
+}  // namespace qr

@@ -22,6 +22,8 @@ struct LinearPlan {
     int unroll;        // GEMV: 1-KiB load instructions per wave step
     int tiles;         // GEMV: 16-channel tiles per block
     bool prefetch;     // GEMV: software-pipelined loads
+    int gemm_tile;     // GEMM: kGemmRing = 256x256 ring kernel, register-staged 1 = 256x128,
+                       // 2 = 128x256, 3 = 128x128 (tokens x channels)
     int splits;        // GEMV: blocks along K, 1 = none
     int64_t n_tiles;   // GEMV: 16-channel tiles
     size_t ws_bytes;   // workspace bytes
@@ -32,6 +34,13 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          void *workspace, hipStream_t stream);
+
+// Tiled MFMA GEMM for large m (qr_gemm.hip).
+constexpr int kGemmRing = 0;
+int gemm_pick_tile(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_tiled(int tile, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                             const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                             hipStream_t stream);
 
 size_t grouped_workspace_bytes(int qtype, int64_t total_rows, int64_t n, int64_t k, int64_t num_experts);
 

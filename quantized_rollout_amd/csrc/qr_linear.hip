@@ -13,7 +13,7 @@
 //    their accumulators through LDS in wave order and wave 0 applies the epilogue: one launch, deterministic,
 //    no cross-block synchronization. The waves per block are chosen at launch so that even the narrow linears
 //    put a few thousand waves on the 256 CUs.
-//  * gemm_kernel (m > 64): LDS-tiled MFMA GEMM, 128x128 output tiles, 128-byte K steps, double-buffered LDS.
+//  * m > 64: the LDS-tiled MFMA GEMM of qr_gemm.hip.
 #include "qr_device.hpp"
 #include "qr_internal.hpp"
 
@@ -207,132 +207,27 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
                     }
                 }
             }
-            // epilogue: y = acc * x_scale[row] * w_scale[col]
+            // epilogue: y = acc * x_scale[row] * w_scale[col]; the scales are loaded together from clamped
+            // indices (one round trip), then the stores are predicated
             const int64_t col = (tile0 + r) * 16 + j;
+            const float sw = ws[col < n ? col : n - 1];
+            float sx[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + mt * 16 + 4 * g + i;
+                sx[i] = xs[row < m ? row : m - 1];
+            }
             if (col >= n) continue;
-            const float sw = ws[col];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t row = m0 + mt * 16 + 4 * g + i;
                 if (row < m) {
-                    const float v = acc_to_f32(acc[r][mt][i]) * xs[row] * sw;
+                    const float v = acc_to_f32(acc[r][mt][i]) * sx[i] * sw;
                     store_y(y, row * n + col, v, y_bf16 != 0);
                     if (acc_out != nullptr) store_acc(acc_out, row * n + col, acc[r][mt][i]);
                 }
             }
         }
-}
-
-// ---------------------------------------------------------------------------------------------------------
-// Large-m LDS-tiled GEMM: 128 x 128 output tile per block of 4 waves (2 x 2), 64 x 64 per wave as 4 x 4
-// MFMA 16x16 tiles, 128-byte K steps staged through double-buffered LDS (row stride padded to 144 bytes).
-// ---------------------------------------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kBK = 128, kLds = kBK + 16;
-
-template <int QT>
-__global__ __launch_bounds__(256) void gemm_kernel(int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq,
-                                                   const float *__restrict__ xs, const uint8_t *__restrict__ wq,
-                                                   const float *__restrict__ ws, void *__restrict__ y, int y_bf16,
-                                                   void *__restrict__ acc_out, int64_t tiles_n) {
-    typedef typename Acc<QT>::type acc_t;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBM * kLds];  // [buffer][A/B][tile]
-
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int j = lane & 15, g = lane >> 4;
-    const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-    const int64_t m0 = tm * kBM, n0 = tn * kBN;
-
-    // global -> register staging: 128 rows x 128 B = 1024 chunks of 16 B per operand, 4 per thread
-    auto gload = [&](uint4 *ra, uint4 *rb, int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = t + 256 * i;
-            const int row = c >> 3, col = (c & 7) * 16;
-            const int64_t kk = k0 + col;
-            const int64_t ar = m0 + row, br = n0 + row;
-            ra[i] = (ar < m && kk < k) ? *reinterpret_cast<const uint4 *>(xq + ar * k + kk) : make_uint4(0, 0, 0, 0);
-            rb[i] = (br < n && kk < k) ? *reinterpret_cast<const uint4 *>(wq + br * k + kk) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto sstore = [&](int buf, const uint4 *ra, const uint4 *rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = t + 256 * i;
-            const int row = c >> 3, col = (c & 7) * 16;
-            *reinterpret_cast<uint4 *>(&lds[buf][0][row * kLds + col]) = ra[i];
-            *reinterpret_cast<uint4 *>(&lds[buf][1][row * kLds + col]) = rb[i];
-        }
-    };
-
-    acc_t acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = acc_t{0, 0, 0, 0};
-
-    const int64_t nsteps = (k + kBK - 1) / kBK;
-    uint4 ra[4], rb[4];
-    gload(ra, rb, 0);
-    sstore(0, ra, rb);
-    __syncthreads();
-    for (int64_t s = 0; s < nsteps; ++s) {
-        const int buf = (int)(s & 1);
-        if (s + 1 < nsteps) gload(ra, rb, (s + 1) * kBK);
-        // lane (j, g) reads 32 contiguous K bytes of row j of each 16-row sub-tile
-        uint4 fa[4][2], fb[4][2];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const uint8_t *p = &lds[buf][0][(wm * 64 + a * 16 + j) * kLds + g * 32];
-            fa[a][0] = *reinterpret_cast<const uint4 *>(p);
-            fa[a][1] = *reinterpret_cast<const uint4 *>(p + 16);
-            const uint8_t *q = &lds[buf][1][(wn * 64 + a * 16 + j) * kLds + g * 32];
-            fb[a][0] = *reinterpret_cast<const uint4 *>(q);
-            fb[a][1] = *reinterpret_cast<const uint4 *>(q + 16);
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if constexpr (QT == kInt8) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        v4i av = {(int)fa[a][h].x, (int)fa[a][h].y, (int)fa[a][h].z, (int)fa[a][h].w};
-                        v4i bv = {(int)fb[b][h].x, (int)fb[b][h].y, (int)fb[b][h].z, (int)fb[b][h].w};
-                        acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[a][b], 0, 0, 0);
-                    }
-                } else {
-                    v8i av = {(int)fa[a][0].x, (int)fa[a][0].y, (int)fa[a][0].z, (int)fa[a][0].w,
-                              (int)fa[a][1].x, (int)fa[a][1].y, (int)fa[a][1].z, (int)fa[a][1].w};
-                    v8i bv = {(int)fb[b][0].x, (int)fb[b][0].y, (int)fb[b][0].z, (int)fb[b][0].w,
-                              (int)fb[b][1].x, (int)fb[b][1].y, (int)fb[b][1].z, (int)fb[b][1].w};
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[a][b], 0, 0, 0, 127, 0,
-                                                                                   127);
-                }
-            }
-        if (s + 1 < nsteps) sstore(buf ^ 1, ra, rb);
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int64_t col = n0 + wn * 64 + b * 16 + j;
-        if (col >= n) continue;
-        const float sw = ws[col];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * 64 + a * 16 + 4 * g + r;
-                if (row < m) {
-                    const float v = acc_to_f32(acc[a][b][r]) * xs[row] * sw;
-                    store_y(y, row * n + col, v, y_bf16 != 0);
-                    if (acc_out != nullptr) store_acc(acc_out, row * n + col, acc[a][b][r]);
-                }
-            }
-    }
 }
 
 template <int QT, int MT, int U, int TB, int WMAX>
@@ -391,6 +286,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     p.splits = 1;
     if (!gemv) {
         p.kind = 1;
+        p.gemm_tile = gemm_pick_tile(m, n, k);
         return p;
     }
     p.kind = 0;
@@ -438,14 +334,7 @@ hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, i
         else
             launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
     } else {
-        const int64_t tiles_m = (m + kBM - 1) / kBM, tiles_n = (n + kBN - 1) / kBN;
-        const dim3 grid((unsigned)(tiles_m * tiles_n));
-        if (qtype == kInt8)
-            hipLaunchKernelGGL((gemm_kernel<kInt8>), grid, dim3(256), 0, stream, m, n, k, xq, xs, wq, ws, y,
-                               y_bf16 ? 1 : 0, acc_out, tiles_n);
-        else
-            hipLaunchKernelGGL((gemm_kernel<kFp8>), grid, dim3(256), 0, stream, m, n, k, xq, xs, wq, ws, y,
-                               y_bf16 ? 1 : 0, acc_out, tiles_n);
+        return launch_gemm_tiled(p.gemm_tile, qtype, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
     }
     return hipGetLastError();
 }

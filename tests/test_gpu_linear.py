@@ -150,6 +150,36 @@ def test_every_gemv_variant(mt, u, tb, monkeypatch, capfd):
             assert "mt=%d" % mt in err and "unroll=%d tiles=%d" % (u, tb) in err, err
 
 
+# every large-batch GEMM kernel: 0 = the 256 x 256 LDS-ring kernel, 1..3 = register-staged 256x128,
+# 128x256, 128x128; shapes with ragged m and n, k with a partial last stage, a single partial stage and fewer
+# stages than the ring holds, n not a multiple of 8 (element-wise epilogue) and whole 256-column tiles (the
+# vectorized bf16 epilogue)
+GEMM_SHAPES = [(65, 264, 16), (300, 512, 1040), (257, 520, 176), (130, 333, 4160), (512, 768, 2048)]
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_every_gemm_tile(tile, monkeypatch, capfd):
+    monkeypatch.setenv("QR_GEMM_TILE", str(tile))
+    monkeypatch.setenv("QR_TRACE", "1")
+    for i, (m, n, k) in enumerate(GEMM_SHAPES):
+        for oq in (O.INT8, O.FP8):
+            xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1300 + 10 * i + oq)
+            what = "gemm tile=%d %s m=%d n=%d k=%d" % (tile, oq, m, n, k)
+            log(what)
+            _check(oq, xc, xs, wc, ws, what)
+            err = capfd.readouterr().err
+            assert "kind=1" in err and "gemm=%d" % tile in err, err
+            # without accumulators: the bf16 output takes the kernel's other epilogue where it has one, and
+            # is bitwise the one written next to the accumulators
+            y_ref, _, _ = O.linear(oq, xc, xs, wc, ws, O.BF16)
+            y_acc, _ = _run(oq, xc, xs, wc, ws)
+            y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws))
+            torch.cuda.synchronize()
+            y = host(y)
+            assert_y_close(y, y_ref, what + " (no accumulators)")
+            assert np.array_equal(y, y_acc), what
+
+
 def test_workspace_reuse_across_plans():
     """One workspace object serves a sequence of differently planned shapes: every call stays bit-exact (INT8)
     or within tolerance (FP8)."""
