@@ -82,8 +82,9 @@ qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k,
  *   y[i,c]   = acc[i,c] * x_scales[i] * w_scales[c], stored as y_type (bfloat16 rounded to nearest even).
  * acc_out: optional [m,n] int32 (INT8) or fp32 (FP8) copy of the accumulators, or NULL.
  * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes, 256-byte aligned, or NULL when
- * that is 0. Every current plan reduces inside its workgroups, so qr_workspace_bytes() returns 0 and NULL may be
- * passed; the argument stays so that callers size it through qr_workspace_bytes() whatever a plan needs.
+ * that is 0. It is nonzero only for large batches with too few output tiles to occupy the GPU: there K is
+ * split and the workspace holds the int32 (INT8) or fp32 (FP8) partial sums, splits x m x n x 4 bytes, which a
+ * second kernel adds in a fixed order. Its contents need no initialisation and are not preserved.
  * INT8 results are bitwise independent of m (row i depends only on row i of the inputs) and deterministic;
  * FP8 results are deterministic for a given (m, n, k).
  * Limits: k <= 131072 (INT8 accumulators stay below 2^31).

@@ -228,11 +228,21 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(int64_t m, int64_t n
 // operands, so the dot products are those of the plain definition. Result C[i][c] sits in lane
 // (c + 32 (i / 4 mod 2)), register 4 (i / 8) + i mod 4.
 // ---------------------------------------------------------------------------------------------------------
-constexpr int kRingK = 64;        // K bytes per stage
-constexpr int kRingTile = 256;    // rows of each operand per stage
-constexpr int kRingBuf = 2 * kRingTile * kRingK;  // bytes per ring buffer (32 KiB)
-constexpr int kRingThreads = 1024;                // sixteen wavefronts, four per SIMD
-constexpr int kRingWaveM = 64, kRingWaveN = 64;   // outputs per wavefront (4 x 4 arrangement)
+constexpr int kRingK = 64;   // K bytes per stage
+constexpr int kRingN = 256;  // weight rows (output channels) per tile
+
+// Tile of BM activation rows (256, or 128 for small batches) x 256 channels: BM / 16 wavefronts of 64 x 64
+// outputs in a (BM / 64) x 4 arrangement, each loading 16 activation rows and 256 / (BM / 16) weight rows of
+// every stage.
+template <int BM>
+struct Ring {
+    static constexpr int kWaves = BM / 16;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBuf = (BM + kRingN) * kRingK;  // bytes per ring buffer
+    static constexpr int kRowsB = kRingN / kWaves;       // weight rows loaded per wavefront
+    static constexpr int kLoadsB = kRowsB / 16;
+    static constexpr int kLoads = 1 + kLoadsB;           // buffer loads per wavefront per stage
+};
 constexpr int kBufferFlags = 0x00020000;          // raw buffer descriptor word 3 (32-bit untyped data)
 constexpr uint32_t kOutOfRange = 0x80000000u;      // a buffer offset past every operand (they stay below 2 GiB)
 
@@ -311,95 +321,98 @@ __device__ __forceinline__ void barrier_fenced() {
     asm volatile("" ::: "memory");
 }
 
-template <int QT>
-__global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, int64_t n, int64_t k,
-                                                                    const uint8_t *__restrict__ xq,
-                                                                    const float *__restrict__ xs,
-                                                                    const uint8_t *__restrict__ wq,
-                                                                    const float *__restrict__ ws,
-                                                                    void *__restrict__ y, int y_bf16,
-                                                                    void *__restrict__ acc_out, int tiles_m,
-                                                                    int tiles_n) {
+template <int QT, int BM>
+__global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
+    int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq, const float *__restrict__ xs,
+    const uint8_t *__restrict__ wq, const float *__restrict__ ws, void *__restrict__ y, int y_bf16,
+    void *__restrict__ acc_out, int tiles_m, int tiles_n, int splits, int stages_per_split,
+    void *__restrict__ partial) {
+    typedef Ring<BM> R;
     typedef typename Acc32<QT>::type acc_t;
-    constexpr int FA = kRingWaveM / 32, FB = kRingWaveN / 32;  // 32x32 fragments per wave
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kRingBuf];  // stage s in buffer s mod 4
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * R::kBuf];  // local stage s in buffer s mod 4
 
-    const int total = tiles_m * tiles_n;
+    // work item order: each XCD (workgroup id mod 8) takes a contiguous run, split-major then token tiles
+    // fastest, so the workgroups that share an operand slice run on one XCD and share its L2
+    const int tiles = tiles_m * tiles_n;
+    const int total = tiles * splits;
     const int per_xcd = (total + 7) / 8;
     const int order = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (order >= total) return;
-    const int64_t m0 = (int64_t)(order % tiles_m) * kRingTile;
-    const int64_t n0 = (int64_t)(order / tiles_m) * kRingTile;
+    const int split = order / tiles, tile = order % tiles;
+    const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
+    const int64_t n0 = (int64_t)(tile / tiles_m) * kRingN;
+    const int64_t all_stages = (k + kRingK - 1) / kRingK;
+    const int64_t st0 = (int64_t)split * stages_per_split;
+    const int64_t stages = std::min<int64_t>(stages_per_split, all_stages - st0);  // >= 1 by construction
+    const int64_t full = k / kRingK;  // stages with every piece inside k
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = wave / (kRingTile / kRingWaveN), wn = wave % (kRingTile / kRingWaveN);
+    const int wm = wave / 4, wn = wave % 4;
 
     // buffer resources over the whole operands: rows past the end load zeros
     const v4i rsa = make_rsrc(xq, (uint32_t)(m * k));
     const v4i rsb = make_rsrc(wq, (uint32_t)(n * k));
 
-    // stage loads: wave w fills rows 32 w .. 32 w + 31 of each operand, 16 rows per instruction; lane l writes
-    // piece l & 3 of row 16 q + l / 4 of its block, which holds logical piece (l & 3) ^ swz(row)
-    constexpr int kRowsPerWave = kRingTile / (kRingThreads / 64);
-    constexpr int kLoadsPerOperand = kRowsPerWave / 16;
-    constexpr int kLoadsPerStage = 2 * kLoadsPerOperand;  // vmcnt per stage per wave
-    uint32_t offa[kLoadsPerOperand], offb[kLoadsPerOperand];
-    int lpiece[kLoadsPerOperand];
+    // stage loads, 16 rows per instruction; lane l writes physical piece l & 3 of row l / 4 of the block, which
+    // holds logical piece (l & 3) ^ swz(row). Activation rows 16 wave ..; weight rows kRowsB wave ..
+    const int ra = wave * 16 + (lane >> 2);
+    const int lpa = (lane & 3) ^ ring_swizzle(ra);
+    const uint32_t offa = m0 + ra < m ? (uint32_t)((m0 + ra) * k + 16 * lpa) : kOutOfRange;
+    uint32_t offb[R::kLoadsB];
+    int lpb[R::kLoadsB];
 #pragma unroll
-    for (int q = 0; q < kLoadsPerOperand; ++q) {
-        const int r = wave * kRowsPerWave + q * 16 + (lane >> 2);
-        lpiece[q] = (lane & 3) ^ ring_swizzle(r);
-        offa[q] = m0 + r < m ? (uint32_t)((m0 + r) * k + 16 * lpiece[q]) : kOutOfRange;
-        offb[q] = n0 + r < n ? (uint32_t)((n0 + r) * k + 16 * lpiece[q]) : kOutOfRange;
+    for (int q = 0; q < R::kLoadsB; ++q) {
+        const int r = wave * R::kRowsB + q * 16 + (lane >> 2);
+        lpb[q] = (lane & 3) ^ ring_swizzle(r);
+        offb[q] = n0 + r < n ? (uint32_t)((n0 + r) * k + 16 * lpb[q]) : kOutOfRange;
     }
-    const int64_t stages = (k + kRingK - 1) / kRingK;
-    const int64_t full = k / kRingK;
-    // load number idx (0 .. kLoadsPerStage - 1) of stage st: operand idx & 1, rows block idx >> 1
-    auto issue_one = [&](int64_t st, uint8_t *buf, int idx) {
-        const uint32_t k0 = (uint32_t)(st * kRingK);
-        const int q = idx >> 1;
-        const bool in = st < full || (int64_t)k0 + 16 * lpiece[q] < k;
-        const uint32_t off = (idx & 1) ? offb[q] : offa[q];
-        const uint32_t o = (in && off != kOutOfRange) ? off + k0 : kOutOfRange;
-        dma16((idx & 1) ? rsb : rsa,
-              lds_addr(buf + ((idx & 1) * kRingTile + wave * kRowsPerWave + q * 16) * kRingK), o);
-    };
-    auto issue = [&](int64_t st, uint8_t *buf) {
+    auto issue = [&](int64_t gst, uint8_t *buf) {  // global stage gst into buffer buf
+        const uint32_t k0 = (uint32_t)(gst * kRingK);
+        const bool tail = gst >= full;
+        {
+            const bool in = !tail || (int64_t)k0 + 16 * lpa < k;
+            dma16(rsa, lds_addr(buf + (wave * 16) * kRingK), (in && offa != kOutOfRange) ? offa + k0 : kOutOfRange);
+        }
 #pragma unroll
-        for (int idx = 0; idx < kLoadsPerStage; ++idx) issue_one(st, buf, idx);
+        for (int q = 0; q < R::kLoadsB; ++q) {
+            const bool in = !tail || (int64_t)k0 + 16 * lpb[q] < k;
+            dma16(rsb, lds_addr(buf + (BM + wave * R::kRowsB + q * 16) * kRingK),
+                  (in && offb[q] != kOutOfRange) ? offb[q] + k0 : kOutOfRange);
+        }
     };
 
-    acc_t acc[FA][FB];
+    acc_t acc[2][2];
 #pragma unroll
-    for (int i = 0; i < FA; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < FB; ++j) acc[i][j] = acc_t{};
+        for (int j = 0; j < 2; ++j) acc[i][j] = acc_t{};
 
     // fragment reads: lane row (l & 31), half h = l >> 5
     const int fr = lane & 31, h = lane >> 5;
     const int p0 = QT == kInt8 ? h : 2 * h, p1 = QT == kInt8 ? 2 + h : 2 * h + 1;
-    auto read_frags = [&](const uint8_t *buf, uint4 (&fa)[FA][2], uint4 (&fb)[FB][2]) {
+    uint4 fa[2][2], fb[2][2];
+    auto read_frags = [&](const uint8_t *buf) {
 #pragma unroll
-        for (int i = 0; i < FA; ++i) {
-            const int r = wm * kRingWaveM + i * 32 + fr;
+        for (int i = 0; i < 2; ++i) {
+            const int r = wm * 64 + i * 32 + fr;
             const int sw = ring_swizzle(r);
             fa[i][0] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (p0 ^ sw));
             fa[i][1] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (p1 ^ sw));
         }
 #pragma unroll
-        for (int j = 0; j < FB; ++j) {
-            const int r = wn * kRingWaveN + j * 32 + fr;
+        for (int j = 0; j < 2; ++j) {
+            const int r = wn * 64 + j * 32 + fr;
             const int sw = ring_swizzle(r);
-            fb[j][0] = *reinterpret_cast<const uint4 *>(buf + (kRingTile + r) * kRingK + 16 * (p0 ^ sw));
-            fb[j][1] = *reinterpret_cast<const uint4 *>(buf + (kRingTile + r) * kRingK + 16 * (p1 ^ sw));
+            fb[j][0] = *reinterpret_cast<const uint4 *>(buf + (BM + r) * kRingK + 16 * (p0 ^ sw));
+            fb[j][1] = *reinterpret_cast<const uint4 *>(buf + (BM + r) * kRingK + 16 * (p1 ^ sw));
         }
     };
-    auto mfmas = [&](const uint4 (&fa)[FA][2], const uint4 (&fb)[FB][2]) {
+    auto mfmas = [&]() {
 #pragma unroll
-        for (int i = 0; i < FA; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < FB; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 if constexpr (QT == kInt8) {
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(fa[i][0]), v4(fb[j][0]), acc[i][j], 0, 0, 0);
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(fa[i][1]), v4(fb[j][1]), acc[i][j], 0, 0, 0);
@@ -409,63 +422,76 @@ __global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, i
                 }
             }
     };
-    // wait until this wave's loads of a stage have landed, `later` = stages issued after it (0..3), and until
-    // its own fragment reads are done; then the barrier makes every wave's loads of that stage visible and
-    // tells every wave that all fragment reads issued before it are complete
+    // wait until this wave's loads of a stage have landed (`later` = stages issued after it, 0..2) and its own
+    // fragment reads are done; the barrier then makes every wave's loads of the stage visible and tells every
+    // wave that all fragment reads issued before it are complete
     auto sync_stage = [&](int64_t later) {
-        if (later >= 3)
-            wait_vmcnt_lgkm0<3 * kLoadsPerStage>();
-        else if (later == 2)
-            wait_vmcnt_lgkm0<2 * kLoadsPerStage>();
+        if (later >= 2)
+            wait_vmcnt_lgkm0<2 * R::kLoads>();
         else if (later == 1)
-            wait_vmcnt_lgkm0<kLoadsPerStage>();
+            wait_vmcnt_lgkm0<R::kLoads>();
         else
             wait_vmcnt_lgkm0<0>();
         barrier_fenced();
     };
 
-    // Pipeline: stage st + 3 is loaded while stage st runs. Each step waits for its own stage, refills the
-    // buffer of stage st - 1 (which every wave has finished reading before the barrier of step st) with stage
-    // st + 3, reads its fragments and runs its MFMAs; the four wavefronts of a SIMD cover each other's
-    // fragment reads.
-    uint4 fa[FA][2], fb[FB][2];
-    auto buffer = [&](int64_t st) { return ring + (int)(st & 3) * kRingBuf; };
+    // Pipeline: stage s + 3 is loaded while stage s runs. Each step waits for its own stage, refills the buffer
+    // of stage s - 1 (which every wave has finished reading before the barrier of step s) with stage s + 3,
+    // reads its fragments and runs its MFMAs; the wavefronts sharing a SIMD cover each other's fragment reads.
+    auto buffer = [&](int64_t s) { return ring + (int)(s & 3) * R::kBuf; };
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-        if (i < stages) issue(i, ring + i * kRingBuf);
-    int64_t st = 0;
-    for (; st + 3 < stages; ++st) {  // steady: two later stages in flight, one more issued here
+        if (i < stages) issue(st0 + i, ring + i * R::kBuf);
+    int64_t s = 0;
+    for (; s + 3 < stages; ++s) {  // steady: two later stages in flight, one more issued here
         sync_stage(2);
-        issue(st + 3, buffer(st + 3));
-        read_frags(buffer(st), fa, fb);
-        mfmas(fa, fb);
+        issue(st0 + s + 3, buffer(s + 3));
+        read_frags(buffer(s));
+        mfmas();
     }
-    for (; st < stages; ++st) {  // the last (up to) three stages: nothing more to issue
-        sync_stage(stages - st - 1);
-        read_frags(buffer(st), fa, fb);
-        mfmas(fa, fb);
+    for (; s < stages; ++s) {  // the last (up to) three stages: nothing more to issue
+        sync_stage(stages - s - 1);
+        read_frags(buffer(s));
+        mfmas();
     }
     wait_vmcnt<0>();  // no load may still be writing LDS when the wave ends
 
-    // epilogue: y = acc * x_scale[row] * w_scale[col], the scales loaded together from clamped indices
-    const int64_t wrow0 = m0 + wm * kRingWaveM, wcol0 = n0 + wn * kRingWaveN;
-    float sw[FB];
+    const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 64;
+    if (splits > 1) {
+        // split-K: this split's raw accumulators into its slice of the partial sums, [split][m][n]
+        typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
+        part_t *P = static_cast<part_t *>(partial) + (int64_t)split * m * n;
 #pragma unroll
-    for (int j = 0; j < FB; ++j) {
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t col = wcol0 + j * 32 + fr;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                    if (row < m && col < n) P[row * n + col] = acc[i][j][e];
+                }
+            }
+        return;
+    }
+
+    // epilogue: y = acc * x_scale[row] * w_scale[col], the scales loaded together from clamped indices
+    float sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
         const int64_t col = wcol0 + j * 32 + fr;
         sw[j] = ws[col < n ? col : n - 1];
     }
     // uniform over the workgroup (the barrier below is reached by every wavefront or by none)
-    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + kRingTile <= n;
+    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + kRingN <= n;
     if (fast) {
-        // bf16 tile through LDS: each wave converts its outputs into its own part of the ring (row stride
-        // 2 kRingWaveN bytes), then writes 16-byte row pieces with buffer stores (rows past m fall outside the
+        // bf16 tile through LDS: each wave converts its 64 x 64 outputs into its own 8 KiB of the ring (row
+        // stride 128 bytes), then writes 16-byte row pieces with buffer stores (rows past m fall outside the
         // buffer and are dropped) instead of scattered 2-byte stores
-        constexpr int kStride = 2 * kRingWaveN;
-        constexpr int kPieces = kRingWaveM * kStride / 16 / 64;  // 16-byte stores per lane
+        constexpr int kStride = 128;
         __syncthreads();  // every wave is done with the ring
-        uint8_t *stage = ring + wave * (kRingWaveM * kStride);
-        unroll<FA>([&](auto I) {
+        uint8_t *stage = ring + wave * (64 * kStride);
+        unroll<2>([&](auto I) {
             constexpr int i = decltype(I)::value;
             float sx[16];
 #pragma unroll
@@ -473,7 +499,7 @@ __global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, i
                 const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
                 sx[e] = xs[row < m ? row : m - 1];
             }
-            unroll<FB>([&](auto J) {
+            unroll<2>([&](auto J) {
                 constexpr int j = decltype(J)::value;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -485,10 +511,10 @@ __global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, i
         });
         const __amdgpu_buffer_rsrc_t ry =
             __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)(m * n * 2), kBufferFlags);
-#pragma unroll 8
-        for (int q = 0; q < kPieces; ++q) {
-            const int c = lane + 64 * q;  // 16-byte piece: row c / (kStride / 16), 8 columns from 8 (c % ...)
-            const int r = c / (kStride / 16), c8 = (c % (kStride / 16)) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = lane + 64 * q;  // 16-byte piece: row c / 8, columns 8 (c % 8) ..
+            const int r = c >> 3, c8 = (c & 7) * 8;
             const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kStride + c8 * 2);
             const int64_t row = wrow0 + r;
             const uint32_t off = row < m ? (uint32_t)((row * n + wcol0 + c8) * 2) : kOutOfRange;
@@ -496,7 +522,7 @@ __global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, i
         }
         return;
     }
-    unroll<FA>([&](auto I) {
+    unroll<2>([&](auto I) {
         constexpr int i = decltype(I)::value;
         float sx[16];
 #pragma unroll
@@ -504,7 +530,7 @@ __global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, i
             const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
             sx[e] = xs[row < m ? row : m - 1];
         }
-        unroll<FB>([&](auto J) {
+        unroll<2>([&](auto J) {
             constexpr int j = decltype(J)::value;
             const int64_t col = wcol0 + j * 32 + fr;
 #pragma unroll
@@ -528,14 +554,70 @@ __global__ __launch_bounds__(kRingThreads, 1) void gemm_ring_kernel(int64_t m, i
     });
 }
 
-template <int QT>
-hipError_t launch_ring(int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs, const uint8_t *wq,
-                       const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
-    const int tiles_m = (int)((m + kRingTile - 1) / kRingTile), tiles_n = (int)((n + kRingTile - 1) / kRingTile);
-    const int total = tiles_m * tiles_n;
+// Split-K: acc = the partial sums of the splits added in split order (exact for INT32; a fixed order for FP32,
+// so repeated calls agree bit for bit), then the epilogue y = acc * x_scale[row] * w_scale[col]. Four
+// consecutive outputs per thread when n is a multiple of 4, one otherwise.
+template <int QT, int VEC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n, int splits,
+                                                            const void *__restrict__ partial,
+                                                            const float *__restrict__ xs,
+                                                            const float *__restrict__ ws, void *__restrict__ y,
+                                                            int y_bf16, void *__restrict__ acc_out) {
+    typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
+    const int64_t total = m * n;
+    const part_t *P = static_cast<const part_t *>(partial);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * VEC;
+    for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC; base < total; base += stride) {
+        part_t a[VEC];
+        if constexpr (VEC == 4) {
+            typedef typename std::conditional<QT == kInt8, int4, float4>::type vec_t;
+            vec_t v = *reinterpret_cast<const vec_t *>(P + base);
+            a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
+            for (int sp = 1; sp < splits; ++sp) {
+                v = *reinterpret_cast<const vec_t *>(P + (int64_t)sp * total + base);
+                a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
+            }
+        } else {
+            a[0] = P[base];
+            for (int sp = 1; sp < splits; ++sp) a[0] += P[(int64_t)sp * total + base];
+        }
+        const int64_t row = base / n;
+        const float sx = xs[row];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int64_t idx = base + e;
+            const float v = acc_to_f32(a[e]) * sx * ws[idx - row * n];
+            if (y_bf16)
+                static_cast<uint16_t *>(y)[idx] = f32_to_bf16(v);
+            else
+                static_cast<float *>(y)[idx] = v;
+            if (acc_out != nullptr) static_cast<part_t *>(acc_out)[idx] = a[e];
+        }
+    }
+}
+
+template <int QT, int BM>
+hipError_t launch_ring(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                       const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
+                       hipStream_t stream) {
+    const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + kRingN - 1) / kRingN);
+    const int total = tiles_m * tiles_n * g.splits;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_ring_kernel<QT>), dim3(grid), dim3(kRingThreads), 0, stream, m, n, k, xq, xs, wq, ws, y,
-                       y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_ring_kernel<QT, BM>), dim3(grid), dim3(Ring<BM>::kThreads), 0, stream, m, n, k, xq, xs,
+                       wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits, g.stages_per_split,
+                       workspace);
+    if (g.splits > 1) {
+        const int64_t total_out = m * n;
+        const bool vec = (n % 4) == 0;
+        const int64_t items = vec ? total_out / 4 : total_out;
+        const int blocks = (int)std::min<int64_t>((items + 255) / 256, 4096);
+        if (vec)
+            hipLaunchKernelGGL((splitk_reduce_kernel<QT, 4>), dim3(blocks), dim3(256), 0, stream, m, n, g.splits,
+                               workspace, xs, ws, y, y_bf16 ? 1 : 0, acc_out);
+        else
+            hipLaunchKernelGGL((splitk_reduce_kernel<QT, 1>), dim3(blocks), dim3(256), 0, stream, m, n, g.splits,
+                               workspace, xs, ws, y, y_bf16 ? 1 : 0, acc_out);
+    }
     return hipGetLastError();
 }
 
@@ -551,10 +633,14 @@ hipError_t launch_t(int64_t m, int64_t n, int64_t k, const uint8_t *xq, const fl
 }
 
 template <int QT>
-hipError_t launch_q(int tile, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs, const uint8_t *wq,
-                    const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
-    switch (tile) {
-        case kGemmRing: return launch_ring<QT>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+hipError_t launch_q(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                    const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
+                    hipStream_t stream) {
+    switch (g.tile) {
+        case kGemmRing:
+            if (g.bm == 128)
+                return launch_ring<QT, 128>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+            return launch_ring<QT, 256>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
         case 1: return launch_t<QT, 256, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
         case 2: return launch_t<QT, 128, 256>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
         default: return launch_t<QT, 128, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
@@ -569,25 +655,58 @@ bool gemm_ring_fits(int64_t m, int64_t n, int64_t k) {
     return m * k < lim && n * k < lim && m * n * 2 < lim;
 }
 
-int gemm_pick_tile(int64_t m, int64_t n, int64_t k) {
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
+    GemmPlan g{};
+    g.splits = 1;
     auto count = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-    const bool ring = gemm_ring_fits(m, n, k);
     const int forced = env_int("QR_GEMM_TILE", -1);
-    if (forced >= 1 && forced <= 3) return forced;
-    if (forced == kGemmRing && ring) return kGemmRing;
-    // the ring kernel once a quarter of the CUs get a 256 x 256 tile; below that, 128 x 128 tiles keep more
-    // CUs busy
-    if (ring && count(256, 256) >= 64) return kGemmRing;
-    if (count(256, 128) >= 256) return 1;
-    if (count(128, 256) >= 256) return 2;
-    return 3;
+    const bool ring = gemm_ring_fits(m, n, k) && !(forced >= 1 && forced <= 3);
+    if (!ring) {
+        if (forced >= 1 && forced <= 3)
+            g.tile = forced;
+        else
+            g.tile = count(256, 128) >= 256 ? 1 : (count(128, 256) >= 256 ? 2 : 3);
+        return g;
+    }
+    g.tile = kGemmRing;
+    // Cost model, fitted to the 7B-shaped FP8 linears at m = 128, 512, 2048 on MI355X: a workgroup takes about
+    // 0.65 us per 64-byte stage with 128 activation rows per tile and 0.83 us with 256; workgroups beyond the
+    // 256 CUs run in further rounds; a split adds its partial sums (written and read back, about 5 TB/s) and
+    // the reduction launch (about 5 us). The cheapest (rows per tile, splits) wins; splits keep >= 4 stages.
+    const int64_t stages = (k + kRingK - 1) / kRingK;
+    const int fbm = env_int("QR_GEMM_BM", 0);
+    const int fs = env_int("QR_GEMM_SPLITS", 0);
+    const int64_t forced_sp = fs >= 1 ? std::min<int64_t>(fs, stages) : 0;
+    g.bm = m <= 128 ? 128 : 256;
+    g.stages_per_split = (int)stages;
+    double best = 1e30;
+    for (int bm : {128, 256}) {
+        if ((fbm == 128 || fbm == 256) && fbm != bm) continue;
+        const int64_t tiles = count(bm, kRingN);
+        for (int64_t sp = forced_sp ? forced_sp : 1; sp <= (forced_sp ? forced_sp : 16); ++sp) {
+            if (!forced_sp && sp > 1 && (stages + sp - 1) / sp < 4) break;
+            const int64_t sps = (stages + sp - 1) / sp;
+            const int64_t used = (stages + sps - 1) / sps;  // no split without a stage
+            const int64_t rounds = (tiles * used + 255) / 256;
+            double t = (double)rounds * (double)sps * (bm == 128 ? 0.65 : 0.83);
+            if (used > 1) t += 5.0 + (double)used * (double)m * (double)n * 8.0 / 5.0e6;
+            if (t < best) {
+                best = t;
+                g.bm = bm;
+                g.stages_per_split = (int)sps;
+                g.splits = (int)used;
+            }
+        }
+    }
+    g.ws_bytes = g.splits > 1 ? (size_t)g.splits * (size_t)m * (size_t)n * 4 : 0;
+    return g;
 }
 
-hipError_t launch_gemm_tiled(int tile, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
-                             const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
-                             hipStream_t stream) {
-    if (qtype == kInt8) return launch_q<kInt8>(tile, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
-    return launch_q<kFp8>(tile, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+hipError_t launch_gemm(const GemmPlan &g, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
+                       const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                       void *workspace, hipStream_t stream) {
+    if (qtype == kInt8) return launch_q<kInt8>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+    return launch_q<kFp8>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
 }
 
 }  // namespace qr

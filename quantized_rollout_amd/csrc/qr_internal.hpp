@@ -15,6 +15,20 @@ hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int6
                                 int qtype, uint8_t *codes, float *scales, hipStream_t stream);
 
 // Plan of a W8A8 linear (which kernel, its split of K and the workspace it needs).
+// Tiled MFMA GEMM for large m (qr_gemm.hip).
+constexpr int kGemmRing = 0;
+struct GemmPlan {
+    int tile;              // kGemmRing = LDS-ring kernel; register-staged 1 = 256x128, 2 = 128x256, 3 = 128x128
+    int bm;                // ring: activation rows per tile (128 or 256)
+    int splits;            // ring: K splits (1 = none; else partial sums in the workspace + a reduction)
+    int stages_per_split;  // ring: 64-byte K stages per split
+    size_t ws_bytes;       // splits x m x n x 4 when split, else 0
+};
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm(const GemmPlan &g, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
+                       const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                       void *workspace, hipStream_t stream);
+
 struct LinearPlan {
     int kind;          // 0 = small-M MFMA GEMV, 1 = LDS-tiled MFMA GEMM
     int m_tiles;       // GEMV: 16-token tiles per block
@@ -22,10 +36,9 @@ struct LinearPlan {
     int unroll;        // GEMV: 1-KiB load instructions per wave step
     int tiles;         // GEMV: 16-channel tiles per block
     bool prefetch;     // GEMV: software-pipelined loads
-    int gemm_tile;     // GEMM: kGemmRing = 256x256 ring kernel, register-staged 1 = 256x128,
-                       // 2 = 128x256, 3 = 128x128 (tokens x channels)
     int splits;        // GEMV: blocks along K, 1 = none
     int64_t n_tiles;   // GEMV: 16-channel tiles
+    GemmPlan gemm;     // GEMM (kind 1)
     size_t ws_bytes;   // workspace bytes
 };
 
@@ -34,13 +47,6 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          void *workspace, hipStream_t stream);
-
-// Tiled MFMA GEMM for large m (qr_gemm.hip).
-constexpr int kGemmRing = 0;
-int gemm_pick_tile(int64_t m, int64_t n, int64_t k);
-hipError_t launch_gemm_tiled(int tile, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
-                             const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
-                             hipStream_t stream);
 
 size_t grouped_workspace_bytes(int qtype, int64_t total_rows, int64_t n, int64_t k, int64_t num_experts);
 

@@ -286,7 +286,8 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     p.splits = 1;
     if (!gemv) {
         p.kind = 1;
-        p.gemm_tile = gemm_pick_tile(m, n, k);
+        p.gemm = gemm_plan(m, n, k);
+        p.ws_bytes = p.gemm.ws_bytes;
         return p;
     }
     p.kind = 0;
@@ -327,14 +328,13 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          void *workspace, hipStream_t stream) {
-    (void)workspace;
     if (p.kind == 0) {
         if (qtype == kInt8)
             launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
         else
             launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
     } else {
-        return launch_gemm_tiled(p.gemm_tile, qtype, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+        return launch_gemm(p.gemm, qtype, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
     }
     return hipGetLastError();
 }

@@ -63,6 +63,12 @@ def test_linear_validation():
     assert call(w=MIS) == B.QR_ERR_ALIGN
     assert call(y=MIS) == B.QR_ERR_ALIGN
     assert call(acc=MIS) == B.QR_ERR_ALIGN
+    # a split-K plan needs its workspace, 256-byte aligned
+    big = dict(m=512, n=3584, k=18944)
+    need = B.qr_workspace_bytes(0, 512, 3584, 18944)
+    assert call(**big) == B.QR_ERR_WORKSPACE and "workspace" in _err()
+    assert call(wsp=P, wsb=need - 1, **big) == B.QR_ERR_WORKSPACE
+    assert call(wsp=MIS, wsb=need, **big) == B.QR_ERR_ALIGN
     # empty problems are no-ops that launch nothing
     assert call(m=0) == B.QR_OK and _err() == ""
     assert call(n=0, x=NULL) == B.QR_OK
@@ -107,11 +113,23 @@ def test_count_validation():
     assert L.qr_count_code_changes(P, P, 64, 3, NULL, NULL, 0, P, S0) == B.QR_ERR_ARG
 
 
-def test_workspace_sizes():
-    # every current plan reduces inside its blocks: no call needs device workspace
+def test_workspace_sizes(monkeypatch):
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
-        for m, n, k in ((1, 1536, 8960), (16, 2048, 1536), (64, 37888, 3584), (2048, 37888, 3584)):
+        # GEMV plans, and GEMM plans with a tile for at least half the CUs, reduce inside their workgroups
+        for m, n, k in ((1, 1536, 8960), (16, 2048, 1536), (64, 37888, 3584), (2048, 37888, 3584),
+                        (128, 37888, 3584)):
             assert B.qr_workspace_bytes(q, m, n, k) == 0
+        # few tiles: the planner's cost model splits K (runs of at least 4 stages of 64 bytes); the partial sums
+        # take splits x m x n x 4 bytes
+        assert B.qr_workspace_bytes(q, 512, 3584, 18944) == 9 * 512 * 3584 * 4    # 28 tiles of 256 x 256
+        assert B.qr_workspace_bytes(q, 128, 4608, 3584) == 7 * 128 * 4608 * 4     # 18 tiles of 128 x 256
+        assert B.qr_workspace_bytes(q, 2048, 3584, 18944) == 2 * 2048 * 3584 * 4  # 112 tiles, 296 stages
+        # forced split counts never leave a split without a stage: 17 stages in 16 requested splits -> 9
+        monkeypatch.setenv("QR_GEMM_SPLITS", "3")
+        assert B.qr_workspace_bytes(q, 300, 333, 1040) == 3 * 300 * 333 * 4
+        monkeypatch.setenv("QR_GEMM_SPLITS", "16")
+        assert B.qr_workspace_bytes(q, 300, 333, 1040) == 9 * 300 * 333 * 4
+        monkeypatch.delenv("QR_GEMM_SPLITS")
         assert B.qr_workspace_bytes(q, 256, 1536, 2048, 128) == 0
     assert B.qr_workspace_bytes(B.QR_INT8, 0, 10, 16) == 0
 

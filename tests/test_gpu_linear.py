@@ -150,30 +150,44 @@ def test_every_gemv_variant(mt, u, tb, monkeypatch, capfd):
             assert "mt=%d" % mt in err and "unroll=%d tiles=%d" % (u, tb) in err, err
 
 
-# every large-batch GEMM kernel: 0 = the 256 x 256 LDS-ring kernel, 1..3 = register-staged 256x128,
-# 128x256, 128x128; shapes with ragged m and n, k with a partial last stage, a single partial stage and fewer
-# stages than the ring holds, n not a multiple of 8 (element-wise epilogue) and whole 256-column tiles (the
-# vectorized bf16 epilogue)
-GEMM_SHAPES = [(65, 264, 16), (300, 512, 1040), (257, 520, 176), (130, 333, 4160), (512, 768, 2048)]
+# every large-batch GEMM kernel: 0 = the LDS-ring kernel (256 or 128 activation rows per tile, with or without
+# split K), 1..3 = register-staged 256x128, 128x256, 128x128; shapes with ragged m and n, k with a partial last
+# stage, a single partial stage and fewer stages than the ring holds, n not a multiple of 8 (element-wise
+# epilogue) and whole 256-column tiles (the vectorized bf16 epilogue)
+GEMM_SHAPES = [(65, 264, 16), (300, 512, 1040), (257, 520, 176), (130, 333, 4160), (512, 768, 2048),
+               (100, 1000, 1552)]
+GEMM_CASES = [(0, None, None), (0, 1, 128), (0, 1, 256), (0, 3, 128), (0, 3, 256), (0, 64, 256), (1, None, None),
+              (2, None, None), (3, None, None)]
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
-def test_every_gemm_tile(tile, monkeypatch, capfd):
+@pytest.mark.parametrize("tile,splits,bm", GEMM_CASES)
+def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
     monkeypatch.setenv("QR_GEMM_TILE", str(tile))
+    if splits is not None:
+        monkeypatch.setenv("QR_GEMM_SPLITS", str(splits))
+    if bm is not None:
+        monkeypatch.setenv("QR_GEMM_BM", str(bm))
     monkeypatch.setenv("QR_TRACE", "1")
+    wsp = qr.Workspace()
     for i, (m, n, k) in enumerate(GEMM_SHAPES):
         for oq in (O.INT8, O.FP8):
             xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1300 + 10 * i + oq)
-            what = "gemm tile=%d %s m=%d n=%d k=%d" % (tile, oq, m, n, k)
+            what = "gemm tile=%s splits=%s bm=%s %s m=%d n=%d k=%d" % (tile, splits, bm, oq, m, n, k)
             log(what)
             _check(oq, xc, xs, wc, ws, what)
             err = capfd.readouterr().err
             assert "kind=1" in err and "gemm=%d" % tile in err, err
+            if bm is not None:
+                assert "bm=%d" % bm in err, err
+            if splits is not None:
+                stages = -(-k // 64)
+                sps = -(-stages // min(splits, stages))
+                assert "splits=%d" % (-(-stages // sps)) in err, err
             # without accumulators: the bf16 output takes the kernel's other epilogue where it has one, and
             # is bitwise the one written next to the accumulators
             y_ref, _, _ = O.linear(oq, xc, xs, wc, ws, O.BF16)
             y_acc, _ = _run(oq, xc, xs, wc, ws)
-            y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws))
+            y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
             torch.cuda.synchronize()
             y = host(y)
             assert_y_close(y, y_ref, what + " (no accumulators)")
