@@ -296,14 +296,26 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     const int64_t m_blocks = (m + 16 * p.m_tiles - 1) / (16 * p.m_tiles);
     // slices of 256 bytes (128 for four token tiles) unless overridden
     int u = p.m_tiles == 4 ? 2 : 4;
-    // more tiles per block share each activation load; keep at least ~1000 blocks in flight
-    const int64_t min_blocks = env_int("QR_GEMV_MIN_BLOCKS", 1024);
     int tb = 1;
-    for (int cand : {4, 2}) {
-        if (gemv_variant_waves(p.m_tiles, u, cand) == 0) continue;
-        if (((p.n_tiles + cand - 1) / cand) * m_blocks >= min_blocks) {
-            tb = cand;
-            break;
+    int wave_cap = 0;  // 0 = the variant's maximum
+    if (p.m_tiles == 1) {
+        // one token tile (m <= 16): the activation slice is small, so each block takes one weight tile and
+        // few wavefronts, 512-byte slices when K has at least three of them. Many small blocks keep more of
+        // them resident per CU and shorten the last, partly filled round of blocks (measured on MI355X: 7B
+        // gate/up at m = 1 from 31 to 26 us per call); only when there are few tiles (a short, deep K) do
+        // more wavefronts per block, on 256-byte slices, pay.
+        const bool few = p.n_tiles < 128;
+        if (k >= 1536 && !few) u = 8;
+        wave_cap = few ? 8 : 4;
+    } else {
+        // more tiles per block share each activation load; keep at least ~1000 blocks in flight
+        const int64_t min_blocks = env_int("QR_GEMV_MIN_BLOCKS", 1024);
+        for (int cand : {4, 2}) {
+            if (gemv_variant_waves(p.m_tiles, u, cand) == 0) continue;
+            if (((p.n_tiles + cand - 1) / cand) * m_blocks >= min_blocks) {
+                tb = cand;
+                break;
+            }
         }
     }
     const int fu = env_int("QR_GEMV_UNROLL", 0), ft = env_int("QR_GEMV_TILES", 0);
@@ -317,6 +329,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     // the reduction's LDS (waves x tb x m_tiles KiB) stays within 64 KiB
     int cap = gemv_variant_waves(p.m_tiles, u, tb);
     if (cap > 64 / (tb * p.m_tiles)) cap = 64 / (tb * p.m_tiles);
+    if (wave_cap > 0 && cap > wave_cap && env_int("QR_GEMV_WAVES", 0) == 0) cap = wave_cap;
     int64_t waves = slices < cap ? slices : cap;
     const int forced_w = env_int("QR_GEMV_WAVES", 0);
     if (forced_w >= 1 && forced_w <= cap) waves = forced_w;
