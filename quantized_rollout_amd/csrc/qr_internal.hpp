@@ -33,10 +33,8 @@ struct LinearPlan {
     int kind;          // 0 = small-M MFMA GEMV, 1 = LDS-tiled MFMA GEMM
     int m_tiles;       // GEMV: 16-token tiles per block
     int waves;         // GEMV: waves per block (they split K)
-    int unroll;        // GEMV: 1-KiB load instructions per wave step
+    int unroll;        // GEMV: 64-byte K steps per slice (1-KiB weight loads per tile per slice)
     int tiles;         // GEMV: 16-channel tiles per block
-    bool prefetch;     // GEMV: software-pipelined loads
-    int splits;        // GEMV: blocks along K, 1 = none
     int64_t n_tiles;   // GEMV: 16-channel tiles
     GemmPlan gemm;     // GEMM (kind 1)
     size_t ws_bytes;   // workspace bytes

@@ -6,14 +6,14 @@
 // weight scales and token-wise activation scales.
 //
 // Two kernels, chosen by the batch m:
-//  * gemv_kernel (m <= 64): the decode regime, bound by streaming the n*k weight bytes from HBM. A block owns
-//    one tile of 16 output channels; its waves split K. Each load instruction of a wave covers 64 contiguous K
-//    bytes of each of the 16 weight rows (four lanes per row, 16 bytes each), and a wave issues U of them back
-//    to back before its MFMAs, so every wave keeps U KiB of weights in flight. The waves of the block reduce
-//    their accumulators through LDS in wave order and wave 0 applies the epilogue: one launch, deterministic,
-//    no cross-block synchronization. The waves per block are chosen at launch so that even the narrow linears
-//    put a few thousand waves on the 256 CUs.
-//  * m > 64: the LDS-tiled MFMA GEMM of qr_gemm.hip.
+//  * gemv_kernel (m <= 64): the decode regime, bound by streaming the n*k weight bytes from HBM. K-slice-major:
+//    a block owns TB tiles of 16 output channels and all of K; wave w takes the 64U-byte K slices w, w + W, ...
+//    For each slice it loads the activation slice once (coalesced, then moved into the MFMA layout with
+//    ds_bpermute) and the slice of all TB weight tiles in one burst of 16-byte loads, then runs one MFMA per
+//    (token tile, weight tile, 64-byte step). The waves' partial sums meet in LDS and are added in wave order
+//    (deterministic, one launch, no cross-block synchronization); each wave finishes a share of the fragments
+//    with the epilogue.
+//  * m > 64: the LDS-ring MFMA GEMM of qr_gemm.hip.
 #include "qr_device.hpp"
 #include "qr_internal.hpp"
 
@@ -283,7 +283,6 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     const int force = env_int("QR_FORCE_VARIANT", -1);  // 0 = GEMV, 1 = tiled GEMM
     const bool gemv = force == 0 || (force != 1 && m <= 64);
     p.ws_bytes = 0;
-    p.splits = 1;
     if (!gemv) {
         p.kind = 1;
         p.gemm = gemm_plan(m, n, k);
@@ -334,7 +333,6 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     const int forced_w = env_int("QR_GEMV_WAVES", 0);
     if (forced_w >= 1 && forced_w <= cap) waves = forced_w;
     p.waves = (int)(waves < 1 ? 1 : waves);
-    p.prefetch = true;
     return p;
 }
 
