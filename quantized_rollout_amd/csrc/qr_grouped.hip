@@ -3,11 +3,14 @@
 // Grouped linear: the expert FFNs of a mixture-of-experts model (the Qwen3-30B-A3B model of "QaRL:
 // Rollout-Aligned Quantization-Aware RL ...", abstract) run in W8A8 (QaRL section 3.1). Output rows are
 // grouped by expert in CSR form; expert e owns rows [offsets[e], offsets[e+1]) and row j reads activation
-// row row_ids[j]. With top-8 routing of 256 tokens over 128 experts an expert sees ~16 rows, so the kernel
-// is the GEMV of qr_linear.hip per expert: a wave owns 16 output channels of one expert and streams that
-// expert's weight rows once per 32 gathered activation rows (two MFMA token tiles). Every expert's weights
-// are read, which is the HBM traffic that bounds the call (QaRL section 3.1 notes MoE rollout is
-// memory-bound). No split of K is needed: experts x channel tiles give >10k waves.
+// row row_ids[j]. With top-8 routing of 256 tokens over 128 experts an expert sees ~16 rows, so each expert's
+// product is a decode-sized GEMV and every expert's weights are read once: the HBM traffic that bounds the call
+// (QaRL section 3.1 notes MoE rollout is memory-bound). The kernel is K-slice-major, like the dense GEMV: a
+// block owns TB 16-channel tiles of one expert and all of K; wave w takes the 64U-byte K slices w, w + W, ...,
+// loads the slice of up to 32 gathered activation rows once (coalesced, then moved into the MFMA layout with
+// ds_bpermute) and the slice of its TB weight tiles in one burst, and runs one MFMA per (token tile, weight
+// tile, 64-byte step). The waves' partial sums meet in LDS and are added in wave order. An expert with more
+// than 32 rows takes further passes over the same weight tiles (served from L2).
 //
 // Changed-code counter: how many published codes (and scales) differ between two quantizations of the same
 // tensor ("QuRL: Efficient Reinforcement Learning with Quantized Rollout", section 4.3: an RL update is much
@@ -15,104 +18,211 @@
 #include "qr_device.hpp"
 #include "qr_internal.hpp"
 
+#include <algorithm>
+
 namespace qr {
 namespace {
 
-constexpr int kStep = 256;
-constexpr int kGroupedWaves = 4;
-constexpr int kGroupedMT = 2;
+constexpr int kGroupedMT = 2;  // 16-row token tiles per pass
 
-__device__ __forceinline__ void load_step_g(uint4 *dst, const uint8_t *__restrict__ row_ptr, int64_t kb, int64_t k) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int64_t off = kb + 16 * t;
-        if (row_ptr != nullptr && off < k)
-            dst[t] = *reinterpret_cast<const uint4 *>(row_ptr + off);
-        else
-            dst[t] = make_uint4(0, 0, 0, 0);
-    }
+__device__ __forceinline__ uint4 gload16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ v4i gv4(const uint4 &a) { return v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w}; }
+__device__ __forceinline__ v8i gv8(const uint4 &a, const uint4 &b) {
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-template <int QT>
-__global__ __launch_bounds__(kGroupedWaves * 64) void grouped_kernel(
+template <int QT, int U, int TB, int WMAX>
+__global__ __launch_bounds__(WMAX * 64) void grouped_kernel(
     int64_t n, int64_t k, const int32_t *__restrict__ offsets, const int32_t *__restrict__ row_ids,
     int64_t total_rows, int64_t x_rows, const uint8_t *__restrict__ xq, const float *__restrict__ xs,
     const uint8_t *__restrict__ wq, const float *__restrict__ ws, void *__restrict__ y, int y_bf16) {
     typedef typename Acc<QT>::type acc_t;
     constexpr int MT = kGroupedMT;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    static_assert(QT == kInt8 || U % 2 == 0, "FP8 pairs load instructions");
+    extern __shared__ int32_t red[];  // [waves][TB][MT][4][64]
+    const int waves = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, g = lane >> 4;
     const int64_t e = blockIdx.y;
-    const int64_t tile = (int64_t)blockIdx.x * kGroupedWaves + wave;
-    const int64_t ncol = tile * 16 + j;
-    if (tile * 16 >= n) return;
+    const int64_t tile0 = (int64_t)blockIdx.x * TB;
+    constexpr int64_t kSlice = 64 * U;
+    const int64_t slices = (k + kSlice - 1) / kSlice;
+    const int64_t full = k / kSlice;
 
+    // the expert's rows (offsets are clamped into [0, total_rows]; an empty expert leaves the block at once)
     int64_t r0 = offsets[e], r1 = offsets[e + 1];
     r0 = r0 < 0 ? 0 : (r0 > total_rows ? total_rows : r0);
     r1 = r1 < 0 ? 0 : (r1 > total_rows ? total_rows : r1);
     if (r1 <= r0) return;
 
-    const uint8_t *__restrict__ wrow = ncol < n ? wq + (e * n + ncol) * k : nullptr;
-    const float sw = ncol < n ? ws[e * n + ncol] : 0.0f;
-    const int64_t steps = (k + kStep - 1) / kStep;
+    // weight rows of this lane (channels past n re-read channel n-1; those columns are never stored)
+    const uint8_t *__restrict__ wrow[TB];
+#pragma unroll
+    for (int r = 0; r < TB; ++r) {
+        const int64_t col = (tile0 + r) * 16 + j;
+        wrow[r] = wq + (e * n + (col < n ? col : n - 1)) * k + 16 * g;
+    }
+    // activation row of output row jr: row_ids[jr] (or jr), -1 when out of range (its outputs are zero)
+    auto xrow_of = [&](int64_t jr) -> int64_t {
+        const int64_t xr = row_ids != nullptr ? (int64_t)row_ids[jr] : jr;
+        return (xr >= 0 && xr < x_rows) ? xr : -1;
+    };
+    const int xr_lane = lane >> 2, xp = lane & 3;  // coalesced activation loads: token row l / 4, piece l % 4
+    const int src_lane = 4 * j + g;                 // the lane that loads what lane (j, g) needs
 
-    for (int64_t mc = r0; mc < r1; mc += 16 * MT) {
-        // activation rows this lane feeds into the two token tiles
+    for (int64_t c0 = r0; c0 < r1; c0 += 16 * MT) {
         const uint8_t *__restrict__ xrow[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int64_t jr = mc + mt * 16 + j;
-            xrow[mt] = nullptr;
-            if (jr < r1) {
-                const int64_t xr = row_ids != nullptr ? (int64_t)row_ids[jr] : jr;
-                if (xr >= 0 && xr < x_rows) xrow[mt] = xq + xr * k;
-            }
+            const int64_t jr = c0 + mt * 16 + xr_lane;
+            const int64_t xr = jr < r1 ? xrow_of(jr) : -1;
+            // rows past the expert's list, or with an out-of-range id, read activation row 0 instead: they only
+            // feed outputs that are never stored (or stored as zero)
+            xrow[mt] = xq + (xr >= 0 ? xr : 0) * k + 16 * xp;
         }
-        acc_t acc[MT];
+        acc_t acc[TB][MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = acc_t{0, 0, 0, 0};
+        for (int r = 0; r < TB; ++r)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[r][mt] = acc_t{0, 0, 0, 0};
 
-        uint4 wcur[4], xcur[MT][4];
-        load_step_g(wcur, wrow, g * 64, k);
+        auto transpose = [&](uint4 (&xv)[MT][U]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) load_step_g(xcur[mt], xrow[mt], g * 64, k);
-        for (int64_t st = 0;; ++st) {
-            uint4 wnxt[4], xnxt[MT][4];
-            const bool more = st + 1 < steps;
-            if (more) {
-                load_step_g(wnxt, wrow, (st + 1) * kStep + g * 64, k);
+            for (int t = 0; t < U; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) load_step_g(xnxt[mt], xrow[mt], (st + 1) * kStep + g * 64, k);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) mma_step(acc[mt], xcur[mt], wcur);
-            if (!more) break;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                wcur[t] = wnxt[t];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xcur[mt][t] = xnxt[mt][t];
-            }
-        }
-
-        if (ncol < n) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t jr = mc + mt * 16 + 4 * g + r;
-                    if (jr >= r1) continue;
-                    const int64_t xr = row_ids != nullptr ? (int64_t)row_ids[jr] : jr;
-                    float v = 0.0f;
-                    if (xr >= 0 && xr < x_rows) v = acc_to_f32(acc[mt][r]) * xs[xr] * sw;
-                    if (y_bf16)
-                        static_cast<uint16_t *>(y)[jr * n + ncol] = f32_to_bf16(v);
-                    else
-                        static_cast<float *>(y)[jr * n + ncol] = v;
+                for (int mt = 0; mt < MT; ++mt) {
+                    xv[mt][t].x = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].x);
+                    xv[mt][t].y = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].y);
+                    xv[mt][t].z = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].z);
+                    xv[mt][t].w = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)xv[mt][t].w);
                 }
+        };
+        auto mma = [&](acc_t (&a)[MT], const uint4 (&xv)[MT][U], const uint4 (&wv)[U]) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (QT == kInt8) {
+#pragma unroll
+                    for (int t = 0; t < U; ++t)
+                        a[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(gv4(xv[mt][t]), gv4(wv[t]), a[mt], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < U; t += 2)
+                        // format 0 = E4M3 for both operands; scale exponents 127 = 2^0 (no block scaling)
+                        a[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            gv8(xv[mt][t], xv[mt][t + 1]), gv8(wv[t], wv[t + 1]), a[mt], 0, 0, 0, 127, 0, 127);
+                }
+            }
+        };
+        for (int64_t sl = wave; sl < full; sl += waves) {
+            const int64_t kb = sl * kSlice;
+            uint4 xv[MT][U], wv[TB][U];
+#pragma unroll
+            for (int t = 0; t < U; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) xv[mt][t] = gload16(xrow[mt] + kb + 64 * t);
+#pragma unroll
+            for (int r = 0; r < TB; ++r)
+#pragma unroll
+                for (int t = 0; t < U; ++t) wv[r][t] = gload16(wrow[r] + kb + 64 * t);
+            transpose(xv);
+#pragma unroll
+            for (int r = 0; r < TB; ++r) mma(acc[r], xv, wv[r]);
         }
+        if (full < slices && wave == full % waves) {  // the partial last slice: bytes past k are zero
+            const int64_t kb = full * kSlice;
+            uint4 xv[MT][U], wv[TB][U];
+#pragma unroll
+            for (int t = 0; t < U; ++t) {
+                const bool in = kb + 64 * t + 16 * xp < k;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    xv[mt][t] = in ? gload16(xrow[mt] + kb + 64 * t) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < TB; ++r)
+#pragma unroll
+                for (int t = 0; t < U; ++t) {
+                    const bool in = kb + 64 * t + 16 * g < k;
+                    wv[r][t] = in ? gload16(wrow[r] + kb + 64 * t) : make_uint4(0, 0, 0, 0);
+                }
+            transpose(xv);
+#pragma unroll
+            for (int r = 0; r < TB; ++r) mma(acc[r], xv, wv[r]);
+        }
+
+        // every wave publishes its partials; each wave then reduces a share of the fragments in wave order
+        constexpr int kFrags = TB * MT;
+        if (waves > 1) {
+            int32_t *mine = red + (int64_t)wave * (kFrags * 256);
+#pragma unroll
+            for (int r = 0; r < TB; ++r)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int idx = (r * MT + mt) * 256 + i * 64 + lane;
+                        if constexpr (QT == kInt8)
+                            mine[idx] = acc[r][mt][i];
+                        else
+                            mine[idx] = __float_as_int(acc[r][mt][i]);
+                    }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < TB; ++r)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int f = r * MT + mt;
+                if (waves > 1) {
+                    if (f % waves != wave) continue;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int idx = f * 256 + i * 64 + lane;
+                        if constexpr (QT == kInt8) {
+                            int32_t sum = red[idx];
+                            for (int w = 1; w < waves; ++w) sum += red[(int64_t)w * (kFrags * 256) + idx];
+                            acc[r][mt][i] = sum;
+                        } else {
+                            float sum = __int_as_float(red[idx]);
+                            for (int w = 1; w < waves; ++w)
+                                sum += __int_as_float(red[(int64_t)w * (kFrags * 256) + idx]);
+                            acc[r][mt][i] = sum;
+                        }
+                    }
+                }
+                // epilogue: y[jr, col] = acc * x_scale[row_ids[jr]] * w_scale[e, col]
+                const int64_t col = (tile0 + r) * 16 + j;
+                if (col >= n) continue;
+                const float sw = ws[e * n + col];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t jr = c0 + mt * 16 + 4 * g + i;
+                    if (jr >= r1) continue;
+                    const int64_t xr = xrow_of(jr);
+                    const float v = xr >= 0 ? acc_to_f32(acc[r][mt][i]) * xs[xr] * sw : 0.0f;
+                    if (y_bf16)
+                        static_cast<uint16_t *>(y)[jr * n + col] = f32_to_bf16(v);
+                    else
+                        static_cast<float *>(y)[jr * n + col] = v;
+                }
+            }
+        if (waves > 1) __syncthreads();  // the next pass reuses the LDS
     }
+}
+
+// (slice steps U, weight tiles per block TB, maximum waves)
+#define QR_GROUPED_VARIANTS(X) X(4, 1, 8) X(4, 2, 8) X(4, 4, 8) X(8, 1, 8) X(8, 2, 8) X(2, 2, 8)
+
+template <int QT, int U, int TB, int WMAX>
+void launch_grouped_t(int waves, int64_t num_experts, int64_t n, int64_t k, const int32_t *offsets,
+                      const int32_t *row_ids, int64_t total_rows, int64_t x_rows, const uint8_t *xq,
+                      const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16,
+                      hipStream_t stream) {
+    const int64_t n_tiles = (n + 15) / 16;
+    const dim3 grid((unsigned)((n_tiles + TB - 1) / TB), (unsigned)num_experts);
+    const size_t lds = waves > 1 ? (size_t)waves * TB * kGroupedMT * 256 * 4 : 0;
+    hipLaunchKernelGGL((grouped_kernel<QT, U, TB, WMAX>), grid, dim3(waves * 64), lds, stream, n, k, offsets, row_ids,
+                       total_rows, x_rows, xq, xs, wq, ws, y, y_bf16 ? 1 : 0);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -207,14 +317,34 @@ hipError_t launch_grouped(int qtype, int64_t num_experts, int64_t n, int64_t k, 
                           const int32_t *row_ids, int64_t total_rows, int64_t x_rows, const uint8_t *xq,
                           const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16,
                           hipStream_t stream) {
-    const int64_t n_tiles = (n + 15) / 16;
-    const dim3 grid((unsigned)((n_tiles + kGroupedWaves - 1) / kGroupedWaves), (unsigned)num_experts);
-    if (qtype == kInt8)
-        hipLaunchKernelGGL((grouped_kernel<kInt8>), grid, dim3(kGroupedWaves * 64), 0, stream, n, k, offsets,
-                           row_ids, total_rows, x_rows, xq, xs, wq, ws, y, y_bf16 ? 1 : 0);
-    else
-        hipLaunchKernelGGL((grouped_kernel<kFp8>), grid, dim3(kGroupedWaves * 64), 0, stream, n, k, offsets,
-                           row_ids, total_rows, x_rows, xq, xs, wq, ws, y, y_bf16 ? 1 : 0);
+    // 128-byte K slices, two 16-channel tiles per block, about four slices per wave and at most four waves
+    // (measured on MI355X for the 128-expert FP8 MoE linears: fewer, longer-running waves per block beat the
+    // LDS reduction of many)
+    int u = env_int("QR_GROUPED_UNROLL", 2), tb = env_int("QR_GROUPED_TILES", 2);
+    bool known = false;
+#define QR_GROUPED_KNOWN(U_, TB_, W_) known = known || (u == U_ && tb == TB_);
+    QR_GROUPED_VARIANTS(QR_GROUPED_KNOWN)
+#undef QR_GROUPED_KNOWN
+    if (!known) {  // overrides that name no compiled variant fall back to the default
+        u = 2;
+        tb = 2;
+    }
+    const int64_t slices = (k + 64 * u - 1) / (64 * u);
+    int waves = env_int("QR_GROUPED_WAVES", 0);
+    if (waves < 1 || waves > 8) waves = (int)std::min<int64_t>(4, std::max<int64_t>(1, slices / 4));
+    bool done = false;
+#define QR_GROUPED_CASE(U_, TB_, W_)                                                                             \
+    if (!done && u == U_ && tb == TB_) {                                                                         \
+        if (qtype == kInt8)                                                                                      \
+            launch_grouped_t<kInt8, U_, TB_, W_>(waves, num_experts, n, k, offsets, row_ids, total_rows, x_rows, \
+                                                 xq, xs, wq, ws, y, y_bf16, stream);                             \
+        else                                                                                                     \
+            launch_grouped_t<kFp8, U_, TB_, W_>(waves, num_experts, n, k, offsets, row_ids, total_rows, x_rows,  \
+                                                xq, xs, wq, ws, y, y_bf16, stream);                              \
+        done = true;                                                                                             \
+    }
+    QR_GROUPED_VARIANTS(QR_GROUPED_CASE)
+#undef QR_GROUPED_CASE
     return hipGetLastError();
 }
 

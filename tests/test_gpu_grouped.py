@@ -64,6 +64,44 @@ def test_grouped_identity_rows_and_many_rows_per_expert(oq, gq):
     assert_y_close(host(y), y_ref, "grouped identity")
 
 
+# every compiled grouped variant: (64-byte steps per K slice, 16-channel tiles per block)
+GROUPED_VARIANTS = [(4, 1), (4, 2), (4, 4), (8, 1), (8, 2), (2, 2)]
+
+
+@pytest.mark.parametrize("u,tb", GROUPED_VARIANTS)
+@pytest.mark.parametrize("waves", [None, 1])
+def test_every_grouped_variant(u, tb, waves, monkeypatch):
+    """Each variant forced through the launch overrides, with the LDS reduction over several waves and with one
+    wave: channels not a multiple of the block's 16 tb, K with a partial last slice, experts with 0, 1, 17 and
+    more than 32 rows (several passes over their weights), gathered rows and one row id out of range (its
+    output row is zero)."""
+    monkeypatch.setenv("QR_GROUPED_UNROLL", str(u))
+    monkeypatch.setenv("QR_GROUPED_TILES", str(tb))
+    if waves is not None:
+        monkeypatch.setenv("QR_GROUPED_WAVES", str(waves))
+    for oq, gq in QT:
+        rng = np.random.default_rng(320 + 10 * u + tb + oq)
+        T, E = 48, 5
+        n, k = 16 * tb * 3 + 5, 64 * u * 3 + 48
+        counts = [1, 0, 40, 17, 33]
+        total = sum(counts)
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        rows = rng.integers(0, T, total).astype(np.int32)
+        x = rng.standard_normal((T, k)).astype(np.float32)
+        xc, xs = O.quantize_rows(x, oq, s_mode=O.S_MUL_RECIP)
+        wc, ws = _expert_weights(E, n, k, oq, rng)
+        log("grouped variant u=%d tb=%d waves=%s %s n=%d k=%d" % (u, tb, waves, oq, n, k))
+        y_ref = O.grouped_linear(oq, off, rows, xc, xs, wc, ws)
+        bad = rows.copy()
+        bad[20] = T + 3  # out of range: that output row must be zero
+        y = qr.qr_w8a8_grouped_linear(gq, dev(off), dev(bad), total, dev(xc), dev(xs), dev(wc), dev(ws))
+        torch.cuda.synchronize()
+        y = host(y)
+        assert not y[20].any()
+        y_ref[20] = 0
+        assert_y_close(y, y_ref, "grouped variant u=%d tb=%d" % (u, tb))
+
+
 def test_grouped_full_size_qwen3_moe_fp8_sampled():
     """The Qwen3-30B-A3B-shaped MoE layer: 128 experts, top-8 of 256 tokens, gate/up 2048->2x768 and down
     768->2048, FP8; every expert's full weights in one launch, the oracle checks sampled channels."""
