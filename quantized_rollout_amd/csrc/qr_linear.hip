@@ -307,7 +307,8 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
         if (k >= 1536 && !few) u = 8;
         wave_cap = few ? 8 : 4;
     } else {
-        // more tiles per block share each activation load; keep at least ~1000 blocks in flight
+        // more tiles per block share each activation load (at m = 64 the activation slices a block reads
+        // outweigh its weights); keep at least ~1000 blocks in flight
         const int64_t min_blocks = env_int("QR_GEMV_MIN_BLOCKS", 1024);
         for (int cand : {4, 2}) {
             if (gemv_variant_waves(p.m_tiles, u, cand) == 0) continue;
@@ -315,6 +316,15 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
                 tb = cand;
                 break;
             }
+        }
+        if (p.m_tiles == 4) {
+            // four token tiles (32 < m <= 64): with enough blocks, one wave each (no reduction, the most blocks
+            // resident); with few, 256-byte slices over up to 8 waves (measured on MI355X: 1.5B gate/up at
+            // m = 64 from 25 to 16 us, the few-tile 1.5B / 7B linears 5-15% faster)
+            if (((p.n_tiles + tb - 1) / tb) * m_blocks >= 1024)
+                wave_cap = 1;
+            else if (tb == 1)
+                u = 4;
         }
     }
     const int fu = env_int("QR_GEMV_UNROLL", 0), ft = env_int("QR_GEMV_TILES", 0);
