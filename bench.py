@@ -16,9 +16,15 @@ replayed; inputs are resident in HBM before the timed region starts.
 
 value = algorithmic HBM bytes of one step (what the method must move: codes, scales, bf16 inputs and
 outputs) x steps / elapsed seconds. The JSON line also carries, per step of the path, the average launch
-duration from HIP events on the stream the kernels run on, the roofline of the dominant kernel, the CPU
+duration from HIP events on the stream the kernels run on, the roofline of the dominant kernel (its measured
+HBM traffic when profiles/ holds a FETCH_SIZE / WRITE_SIZE summary taken on the current kernel sources), the CPU
 oracle timed on a bounded sample of the same step, and (unless --quick) the FP8 7B-shaped linears at the
 MFMA-bound batches and the grouped MoE FFN linears.
+
+Counter runs for the traffic figure (each counter in a run of its own):
+  rocprofv3 --pmc FETCH_SIZE -d DIR_F -o t --output-format csv -- python3 bench.py --profile-row ROW
+  rocprofv3 --pmc WRITE_SIZE -d DIR_W -o t --output-format csv -- python3 bench.py --profile-row ROW
+  python3 bench.py --profile-row ROW --traffic-summary DIR_F DIR_W > profiles/traffic_ROW.md
 """
 import argparse
 import json
@@ -399,6 +405,144 @@ def cpu_baseline(stack, budget_s):
 
 
 # ----------------------------------------------------------------------------------------------------------
+# ----------------------------------------------------------------------------------------------------------
+# measured HBM traffic of a row (rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a plain copy)
+# ----------------------------------------------------------------------------------------------------------
+TRAFFIC_COPY_BYTES = 256 << 20  # the scale reference: a device copy of 256 MiB (reads and writes that many)
+
+
+def row_pieces(stack):
+    """{row: function that launches that row's kernels once}, as timed in `rows`."""
+    pieces = {"a1_quantize_weights": stack.publish_quantize, "a5_count_changes": stack.publish_count}
+    for m in BATCHES:
+        pieces["a2_quantize_acts_m%d" % m] = lambda m=m: stack.decode_acts(m)
+        pieces["a3_linear_m%d" % m] = lambda m=m: stack.decode_linears(m)
+    return pieces
+
+
+def sources_digest():
+    """sha256 over the library's kernel sources: a traffic figure is only reported for the sources it was
+    measured on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_rollout_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def profile_row(stack, name, reps):
+    """The launches the counter runs look at: a plain device copy, `reps` eager passes of one row, the copy
+    again (the copies bracket the row and give the counters' scale)."""
+    import torch
+
+    fn = row_pieces(stack)[name]
+    # an elementwise kernel (never a DMA-engine copy): reads and writes TRAFFIC_COPY_BYTES of fp32
+    src = torch.ones(TRAFFIC_COPY_BYTES // 4, dtype=torch.float32, device=stack.dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_dispatches(directory, counter):
+    """[(dispatch id, kernel name, value)] of one counter from a rocprofv3 csv output directory."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % directory)
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                name, v = per.get(key, (r["Kernel_Name"], 0.0))
+                per[key] = (name, v + float(r["Counter_Value"]))
+    return [(k, per[k][0], per[k][1]) for k in sorted(per)]
+
+
+def traffic_summary(fetch_dir, write_dir, name, reps, command):
+    """Markdown summary of the two counter runs of `profile_row`: per-dispatch FETCH_SIZE / WRITE_SIZE of the
+    row's launches between the two copies, each scaled by what the counter reads for the copy."""
+    launches = DecoderStack.row_work()[name][2]
+    nbytes = DecoderStack.row_work()[name][0]
+    out = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        ds = _counter_dispatches(directory, counter)
+        copies = [i for i, (_, kname, _) in enumerate(ds) if "qr::" not in kname and "neg" in kname]
+        if len(copies) < 2:
+            raise SystemExit("copy markers not found in %s" % directory)
+        a, b = copies[-2], copies[-1]
+        row = [d for d in ds[a + 1:b] if "qr::" in d[1]]
+        if len(row) != reps * launches:
+            raise SystemExit("%s: %d row dispatches between the copies, expected %d" % (counter, len(row),
+                                                                                      reps * launches))
+        copy_kib = (ds[a][2] + ds[b][2]) / 2
+        scale = TRAFFIC_COPY_BYTES / (copy_kib * 1024.0)
+        out[counter] = (sum(v for _, _, v in row) / len(row), copy_kib, scale)
+    per_launch = sum(v * 1024.0 * sc for v, _, sc in out.values())
+    lines = [
+        "# HBM traffic of `%s` (rocprofv3 FETCH_SIZE / WRITE_SIZE), one MI355X" % name,
+        "",
+        "Commands (from the repository root):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "The row's %d launches are run %d times between two elementwise passes over %d MiB of fp32 (a plain copy "
+        "that reads and writes %d MiB); each counter's per-dispatch reading (KiB) is scaled by the copy's to bytes." % (
+            launches, reps, TRAFFIC_COPY_BYTES >> 20, TRAFFIC_COPY_BYTES >> 20),
+        "",
+        "| counter | mean per row launch (KiB) | copy reading (KiB) | scale to bytes per KiB |",
+        "|---|---|---|---|",
+    ]
+    for counter, (v, ck, sc) in out.items():
+        lines.append("| %s | %.1f | %.1f | %.4f x 1024 |" % (counter, v, ck, sc))
+    lines += [
+        "",
+        "| | bytes per launch |",
+        "|---|---|",
+        "| algorithmic (what the method must move) | %d |" % (nbytes // launches),
+        "| measured HBM traffic (fetch + write, scaled) | %d |" % int(per_launch),
+        "",
+        "traffic_row: %s" % name,
+        "traffic_bytes_per_launch: %d" % int(per_launch),
+        "traffic_sources_sha256: %s" % sources_digest(),
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def read_traffic(name):
+    """Measured traffic per launch of `name` from profiles/, or None when absent or taken on other sources."""
+    import glob
+
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
+        fields = {}
+        with open(f) as fh:
+            for line in fh:
+                if line.startswith("traffic_") and ":" in line:
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("traffic_row") == name and fields.get("traffic_sources_sha256") == sources_digest():
+            return int(fields["traffic_bytes_per_launch"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,7 +552,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the FP8 7B and MoE side measurements")
+    ap.add_argument("--profile-row", metavar="ROW", help="only run ROW between two device copies (for the "
+                    "rocprofv3 counter runs) and exit")
+    ap.add_argument("--profile-reps", type=int, default=3)
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the markdown summary of the two counter runs of --profile-row ROW and exit")
+    ap.add_argument("--traffic-command", default="", help="the command lines recorded in that summary")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.profile_row,
+                              args.profile_reps, args.traffic_command))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no collectives or sharding); --gpus %d is not "
@@ -428,6 +583,9 @@ def main():
     log("device %s, libqr %s" % (torch.cuda.get_device_name(dev), qr.qr_version()))
 
     stack = DecoderStack(dev)
+    if args.profile_row:
+        profile_row(stack, args.profile_row, args.profile_reps)
+        return 0
     work = stack.row_work()
     step_bytes = sum(v[0] for v in work.values())
     step_ops = sum(v[1] for v in work.values())
@@ -464,11 +622,7 @@ def main():
 
     # per-row launch timing (HIP events on the stream the kernels run on)
     rows = {}
-    pieces = [("a1_quantize_weights", stack.publish_quantize), ("a5_count_changes", stack.publish_count)]
-    for m in BATCHES:
-        pieces.append(("a2_quantize_acts_m%d" % m, lambda m=m: stack.decode_acts(m)))
-        pieces.append(("a3_linear_m%d" % m, lambda m=m: stack.decode_linears(m)))
-    for name, fn in pieces:
+    for name, fn in row_pieces(stack).items():
         nb, no, launches = work[name]
         g = TimedGraph(fn, launches)
         ms = g.time_ms(args.reps)
@@ -482,8 +636,9 @@ def main():
     d = rows[dominant]
     nb = work[dominant][0]
     achieved = nb / (d["us_total"] * 1e3)  # GB/s
+    traffic = read_traffic(dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dominant,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dominant,
                 "bytes_per_launch": int(nb // d["launches"]), "us_per_launch": d["us_per_launch"]}
 
     extra = {}

@@ -1,0 +1,57 @@
+"""bench.py host logic on the CPU: the one-GPU contract and the traffic summary built from counter CSVs."""
+import csv
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _write_counters(directory, counter, rows):
+    os.makedirs(directory, exist_ok=True)
+    with open(os.path.join(directory, "t_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_traffic_summary_scales_by_the_copy(tmp_path):
+    row = "a3_linear_m64"
+    nbytes, _, launches = bench.DecoderStack.row_work()[row]
+    copy_kib = bench.TRAFFIC_COPY_BYTES / 1024
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel>"
+    # an earlier copy-like kernel from set-up, then the two markers around 2 passes of the row; the fetch
+    # counter reads half of the copy's bytes, the write counter all of them
+    fetch = [(neg, 7.0)] + [(neg, copy_kib / 2)] + [("qr::gemv_kernel", 100.0)] * (2 * launches) + [(neg, copy_kib / 2)]
+    write = [(neg, 7.0)] + [(neg, copy_kib)] + [("qr::gemv_kernel", 10.0)] * (2 * launches) + [(neg, copy_kib)]
+    _write_counters(str(tmp_path / "f"), "FETCH_SIZE", fetch)
+    _write_counters(str(tmp_path / "w"), "WRITE_SIZE", write)
+    md = bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), row, 2, "cmd")
+    fields = dict(line.split(": ", 1) for line in md.splitlines() if line.startswith("traffic_"))
+    assert fields["traffic_row"] == row
+    assert int(fields["traffic_bytes_per_launch"]) == (100 * 2 + 10) * 1024
+    assert fields["traffic_sources_sha256"] == bench.sources_digest()
+    assert "| algorithmic (what the method must move) | %d |" % (nbytes // launches) in md
+
+
+def test_traffic_is_only_reported_for_the_current_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "quantized_rollout_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "quantized_rollout_amd" / "csrc" / "k.hip").write_text("kernel v1")
+    digest = bench.sources_digest()
+    (tmp_path / "profiles" / "traffic_x.md").write_text(
+        "traffic_row: a3_linear_m64\ntraffic_bytes_per_launch: 123\ntraffic_sources_sha256: %s\n" % digest)
+    assert bench.read_traffic("a3_linear_m64") == 123
+    assert bench.read_traffic("a1_quantize_weights") is None
+    (tmp_path / "quantized_rollout_amd" / "csrc" / "k.hip").write_text("kernel v2")
+    assert bench.read_traffic("a3_linear_m64") is None
