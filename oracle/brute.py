@@ -128,3 +128,41 @@ def linear(qtype, x_codes, x_scales, w_codes, w_scales):
         acc.append(ar)
         y.append(yr)
     return acc, y
+
+
+# ---- next row: W4A16 ------------------------------------------------------------------------------------
+def quantize_w4_row(row, group, s=None):
+    """Group-wise symmetric INT4 codes of one row of fp32 values (Python floats): per group of ``group``
+    channels, S = fl32(max|w'| / 7) (1 when zero), q = nearest integer of fl32(w' / S), ties to even, clamped
+    to [-7, 7]; w' = fl32(w * s_j) with an invariant scale. Returns (list of ints, list of Fraction scales)."""
+    qs, scales = [], []
+    for g0 in range(0, len(row), group):
+        wp = []
+        for j in range(g0, g0 + group):
+            v = f32_value(row[j])
+            if s is not None:
+                v = round_f32(v * f32_value(s[j]))
+            wp.append(v)
+        S = round_f32(max(abs(v) for v in wp) / 7)
+        if S == 0:
+            S = Fraction(1)
+        scales.append(S)
+        for v in wp:
+            q = round_f32(v / S)
+            q = max(Fraction(-7), min(Fraction(7), q))
+            qs.append(int(round(q)))
+    return qs, scales
+
+
+def w4a16_linear(x_rows, w_codes, w_scales, group):
+    """Exact y[m][n] = sum_g S[n][g] * sum_{j in g} x[m][j] * q[n][j] (x given as exact values), as Fractions."""
+    y = []
+    for xr in x_rows:
+        yr = []
+        for qr, sr in zip(w_codes, w_scales):
+            acc = Fraction(0)
+            for g, S in enumerate(sr):
+                acc += S * sum((Fraction(xr[j]) * qr[j] for j in range(g * group, (g + 1) * group)), Fraction(0))
+            yr.append(acc)
+        y.append(yr)
+    return y

@@ -52,6 +52,10 @@ def lib():
         L.or_grouped_linear.restype = ctypes.c_int
         L.or_count_code_changes.argtypes = [vp, vp, i64, i32, vp, vp, i64, vp]
         L.or_count_code_changes.restype = None
+        L.or_quantize_w4.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp]
+        L.or_quantize_w4.restype = None
+        L.or_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, i64, i32, vp, vp]
+        L.or_w4a16_linear.restype = None
         _lib = L
     return _lib
 
@@ -167,3 +171,46 @@ def count_code_changes(a, b, qtype, sa=None, sb=None):
     out = np.zeros(3, np.int64)
     lib().or_count_code_changes(_p(a), _p(b), a.size, qtype, _p(sa), _p(sb), ns, _p(out))
     return out
+
+
+# ---- next row: W4A16 ------------------------------------------------------------------------------------
+W4_GROUP = 128  # input channels per INT4 scale group
+
+
+def quantize_w4(w, s=None, group=W4_GROUP):
+    """Group-wise symmetric INT4 codes of w [rows, k] (fp32, or bfloat16 as uint16 bits): returns packed codes
+    [rows, k/2] (even channel in the low nibble) and scales [rows, k/group]."""
+    in_type = BF16 if w.dtype == np.uint16 else F32
+    w = _c(w, np.uint16 if in_type == BF16 else np.float32)
+    rows, k = w.shape
+    assert k % group == 0 and group % 2 == 0
+    s = None if s is None else _c(s, np.float32)
+    codes = np.zeros((rows, k // 2), np.uint8)
+    scales = np.zeros((rows, k // group), np.float32)
+    lib().or_quantize_w4(_p(w), in_type, rows, k, _p(s), group, _p(codes), _p(scales))
+    return codes, scales
+
+
+def unpack_w4(codes):
+    """Signed INT4 values [rows, 2 * bytes] of packed codes (for tests)."""
+    lo = (codes & 0x0F).astype(np.int8)
+    hi = (codes >> 4).astype(np.int8)
+    lo[lo >= 8] -= 16
+    hi[hi >= 8] -= 16
+    out = np.empty((codes.shape[0], codes.shape[1] * 2), np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def w4a16_linear(x_bf16, codes, scales, group=W4_GROUP, y_type=BF16):
+    """y [m, n] of bfloat16 activations (uint16 bits) and packed INT4 weights; returns (y, y_f64)."""
+    x_bf16 = _c(x_bf16, np.uint16)
+    codes, scales = _c(codes, np.uint8), _c(scales, np.float32)
+    m, k = x_bf16.shape
+    n = codes.shape[0]
+    assert codes.shape == (n, k // 2) and scales.shape == (n, k // group)
+    y = np.zeros((m, n), np.uint16 if y_type == BF16 else np.float32)
+    y64 = np.zeros((m, n), np.float64)
+    lib().or_w4a16_linear(m, n, k, _p(x_bf16), _p(codes), _p(scales), group, y_type, _p(y), _p(y64))
+    return y, y64

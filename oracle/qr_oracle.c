@@ -323,3 +323,82 @@ void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, in
     out3[1] = nv;
     out3[2] = ns;
 }
+
+/* ------------------------------------------------------------------------------------------------------
+ * next row: W4A16 (group-wise INT4 weights, bfloat16 activations)
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* [QaRL] 3.1 runs rollouts in W8A8 or W4A16 (weights only quantized, 4-bit), with the integer Quant of
+ * [QaRL] 2.2 (clamp(round(W / s) + z, q_min, q_max)); the pages fix neither the group size nor the range.
+ * Reading: symmetric (z = 0), q in [-7, 7], one scale per group of `group` consecutive input channels of a
+ * row. For every row and every group independently:
+ *  1. w'_j = w_j, or fl32(w_j * s_j) for W diag(s);
+ *  2. a = max_j |w'_j| over the group;  S = fl32(a / 7), or 1 when that is zero;
+ *  3. v_j = fl32(w'_j / S);  q_j = round-to-nearest-even of v_j clamped to [-7, 7].
+ * Codes are packed two per byte, channel 2i in the low nibble and 2i + 1 in the high nibble, each a 4-bit
+ * two's complement value: codes[r, k/2], scales[r, k/group]. k must be a multiple of group (even). */
+void or_quantize_w4(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int64_t group,
+                    uint8_t *codes, float *scales) {
+    int64_t r, g, j;
+    const int64_t groups = k / group;
+    float *wp = (float *)malloc((size_t)(group > 0 ? group : 1) * sizeof(float));
+    if (!wp) abort();
+    for (r = 0; r < rows; ++r) {
+        for (g = 0; g < groups; ++g) {
+            float a = 0.0f, S;
+            for (j = 0; j < group; ++j) {
+                float w = or_load(in, in_type, r * k + g * group + j);
+                if (s) w = w * s[g * group + j];
+                wp[j] = w;
+                if (fabsf(w) > a) a = fabsf(w);
+            }
+            S = a / 7.0f;
+            if (!(S > 0.0f)) S = 1.0f;
+            scales[r * groups + g] = S;
+            for (j = 0; j < group; ++j) {
+                const int64_t col = g * group + j;
+                float v = wp[j] / S;
+                int q;
+                uint8_t *byte = &codes[r * (k / 2) + col / 2];
+                if (v > 7.0f) v = 7.0f;
+                if (v < -7.0f) v = -7.0f;
+                q = (int)or_rne((double)v);
+                if (col % 2 == 0)
+                    *byte = (uint8_t)((*byte & 0xF0) | (q & 0x0F));
+                else
+                    *byte = (uint8_t)((*byte & 0x0F) | ((q & 0x0F) << 4));
+            }
+        }
+    }
+    free(wp);
+}
+
+/* The 4-bit code of channel j of a packed row, as a signed integer. */
+int or_w4_code(const uint8_t *row_codes, int64_t j) {
+    const int nib = (j % 2 == 0) ? (row_codes[j / 2] & 0x0F) : (row_codes[j / 2] >> 4);
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+/* Y[m,n] = sum_g S[n,g] * sum_{j in g} x[m,j] * q[n,j]: the W4A16 product with the dequantization of [QaRL] 2.2
+ * (W_hat = s * W_q) per group, activations in bfloat16 taken exactly. Each inner sum is a sum of products of
+ * an 8-bit and a 3-bit significand, formed in double; the result is the exact value up to double rounding, then
+ * rounded once to fp32 or bfloat16. */
+void or_w4a16_linear(int64_t m, int64_t n, int64_t k, const uint16_t *x, const uint8_t *codes,
+                     const float *scales, int64_t group, int y_type, void *y, double *y_f64) {
+    int64_t i, c, g, j;
+    const int64_t groups = k / group;
+    for (i = 0; i < m; ++i) {
+        for (c = 0; c < n; ++c) {
+            double acc = 0.0;
+            const uint8_t *wr = codes + c * (k / 2);
+            for (g = 0; g < groups; ++g) {
+                double inner = 0.0;
+                for (j = g * group; j < (g + 1) * group; ++j)
+                    inner += (double)or_bf16_to_f32(x[i * k + j]) * (double)or_w4_code(wr, j);
+                acc += (double)scales[c * groups + g] * inner;
+            }
+            if (y_f64) y_f64[i * n + c] = acc;
+            or_store_y(y_type, y, i * n + c, acc);
+        }
+    }
+}

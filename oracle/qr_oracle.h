@@ -73,6 +73,16 @@ int or_grouped_linear(int qtype, int64_t num_experts, int64_t n, int64_t k, cons
 void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
                            const float *sb, int64_t n_scales, int64_t *out3);
 
+/* ---- next row: W4A16 ------------------------------------------------------------------------------- */
+/* Group-wise symmetric INT4 weights, q in [-7, 7], S = max|w'| / 7 per group of `group` input channels;
+ * two codes per byte (even channel in the low nibble); scales[rows, k/group]. */
+void or_quantize_w4(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int64_t group,
+                    uint8_t *codes, float *scales);
+int  or_w4_code(const uint8_t *row_codes, int64_t j);
+/* y = sum_g S[n,g] * sum_{j in g} x[m,j] q[n,j] (x bfloat16), exact up to double rounding */
+void or_w4a16_linear(int64_t m, int64_t n, int64_t k, const uint16_t *x, const uint8_t *codes,
+                     const float *scales, int64_t group, int y_type, void *y, double *y_f64);
+
 #ifdef __cplusplus
 }
 #endif
