@@ -25,7 +25,9 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 
 # every symbol include/qr.h declares
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
-           "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version")
+           "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
+           "qr_w4a16_linear")
+W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
 
 class QRError(RuntimeError):
@@ -55,8 +57,10 @@ def lib():
                 L.qr_w8a8_grouped_linear.argtypes = [i32, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, vp, i32,
                                                      vp, sz, vp]
                 L.qr_count_code_changes.argtypes = [vp, vp, i64, i32, vp, vp, i64, vp, vp]
+                L.qr_quantize_weights_w4.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
+                L.qr_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
                 for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
-                          "qr_count_code_changes"):
+                          "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear"):
                     getattr(L, f).restype = ctypes.c_int
                 L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
                 L.qr_workspace_bytes.restype = sz
@@ -105,8 +109,8 @@ def qr_workspace_bytes(qtype, m, n, k, num_experts=1):
 
 
 class Workspace:
-    """Zero-filled device workspace, grown on demand. The library leaves it zero-filled after each call;
-    calls that may overlap (different streams) need separate workspaces."""
+    """Device workspace, grown on demand (its contents need no initialisation and are not preserved); calls
+    that may overlap (different streams) need separate workspaces."""
 
     def __init__(self, device=None):
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
@@ -154,6 +158,44 @@ def qr_quantize_weights(w, qtype, s=None, codes=None, scales=None, stream=None):
 def qr_quantize_acts(x, qtype, s=None, codes=None, scales=None, stream=None):
     """Per-token codes [m,k] and scales [m] of x [m,k] (optionally of X diag(1/s))."""
     return _quantize(lib().qr_quantize_acts, x, qtype, s, codes, scales, stream)
+
+
+def qr_quantize_weights_w4(w, s=None, codes=None, scales=None, stream=None):
+    """Group-wise INT4 codes [n, k/2] (two per byte, even channel in the low nibble) and scales [n, k/128] of
+    w [n,k] (optionally of W diag(s))."""
+    _need(w.is_cuda and w.dim() == 2 and w.is_contiguous(), "w must be a contiguous 2-D CUDA tensor")
+    n, k = w.shape
+    _need(k % W4_GROUP == 0, "k must be a multiple of %d" % W4_GROUP)
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // W4_GROUP), dtype=torch.float32, device=w.device)
+    if s is not None:
+        _need(s.is_cuda and s.dtype == torch.float32 and s.shape == (k,) and s.is_contiguous(),
+              "s must be a contiguous float32 CUDA vector of length k")
+    _need(codes.dtype == torch.uint8 and codes.shape == (n, k // 2) and codes.is_contiguous(), "bad codes tensor")
+    _need(scales.dtype == torch.float32 and scales.shape == (n, k // W4_GROUP) and scales.is_contiguous(),
+          "bad scales tensor")
+    _check(lib().qr_quantize_weights_w4(_ptr(w), _dtype_code(w), n, k, _ptr(s), _ptr(codes), _ptr(scales),
+                                        _stream(stream)))
+    return codes, scales
+
+
+def qr_w4a16_linear(x, w_codes, w_scales, y=None, y_dtype=torch.bfloat16, stream=None):
+    """y [m,n] = sum over groups of w_scales * (x . q) with bfloat16 activations x [m,k] and INT4 weights."""
+    m, k = x.shape
+    n = w_codes.shape[0]
+    for t in (x, w_codes, w_scales):
+        _need(t.is_cuda and t.is_contiguous(), "operands must be contiguous CUDA tensors")
+    _need(x.dtype == torch.bfloat16, "x must be bfloat16")
+    _need(w_codes.dtype == torch.uint8 and w_codes.shape == (n, k // 2), "bad w_codes")
+    _need(w_scales.dtype == torch.float32 and w_scales.shape == (n, k // W4_GROUP), "bad w_scales")
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype, device=x.device)
+    _need(y.shape == (m, n) and y.is_contiguous(), "bad y")
+    _check(lib().qr_w4a16_linear(m, n, k, _ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(y), _dtype_code(y),
+                                 _stream(stream)))
+    return y
 
 
 def qr_w8a8_linear(qtype, x_codes, x_scales, w_codes, w_scales, y=None, y_dtype=torch.bfloat16, acc_out=None,

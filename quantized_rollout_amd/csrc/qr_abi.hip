@@ -187,6 +187,51 @@ qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_
     return hip_status(e, "count launch");
 }
 
+qr_status qr_quantize_weights_w4(const void *w, qr_dtype w_type, int64_t n, int64_t k, const float *s,
+                                 void *w_codes, float *w_scales, void *stream) {
+    qr_status st;
+    if ((st = check_dtype(w_type, "input dtype")) != QR_OK) return st;
+    if (n < 0) return fail(QR_ERR_ARG, "negative row count %lld", (long long)n);
+    if (k <= 0) return fail(QR_ERR_ARG, "k must be positive (got %lld)", (long long)k);
+    if (k % qr::kW4Group != 0)
+        return fail(QR_ERR_UNSUPPORTED, "k must be a multiple of %d (got %lld)", (int)qr::kW4Group, (long long)k);
+    if (n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "row count %lld too large", (long long)n);
+    if (n == 0) return ok();
+    if (w == nullptr || w_codes == nullptr || w_scales == nullptr)
+        return fail(QR_ERR_ARG, "null input, code or scale pointer");
+    if (!aligned(w, 16) || !aligned(w_codes, 16) || (s != nullptr && !aligned(s, 16)))
+        return fail(QR_ERR_ALIGN, "input, codes and s must be 16-byte aligned");
+    if (!aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    const hipError_t e = qr::launch_quantize_w4(w, w_type == QR_BF16, n, k, s, static_cast<uint8_t *>(w_codes),
+                                                w_scales, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4 quantize launch");
+}
+
+qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const void *w_codes, const float *w_scales,
+                          void *y, qr_dtype y_type, void *stream) {
+    qr_status st;
+    if ((st = check_dtype(y_type, "output dtype")) != QR_OK) return st;
+    if (m < 0 || n < 0) return fail(QR_ERR_ARG, "negative size m=%lld n=%lld", (long long)m, (long long)n);
+    if (k <= 0) return fail(QR_ERR_ARG, "k must be positive (got %lld)", (long long)k);
+    if (k % qr::kW4Group != 0)
+        return fail(QR_ERR_UNSUPPORTED, "k must be a multiple of %d (got %lld)", (int)qr::kW4Group, (long long)k);
+    if (m > 65535 * 16 || n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "m or n too large");
+    if (m == 0 || n == 0) return ok();
+    if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
+        return fail(QR_ERR_ARG, "null operand pointer");
+    if (!aligned(x, 16) || !aligned(w_codes, 16)) return fail(QR_ERR_ALIGN, "x and codes must be 16-byte aligned");
+    if (!aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    if (!aligned(y, 16)) return fail(QR_ERR_ALIGN, "y must be 16-byte aligned");
+    const qr::W4Plan p = qr::plan_w4a16(m, n, k);
+    if (getenv("QR_TRACE") != nullptr)
+        fprintf(stderr, "[qr] w4a16 m=%lld n=%lld k=%lld unroll=%d waves=%d\n", (long long)m, (long long)n,
+                (long long)k, p.unroll, p.waves);
+    const hipError_t e = qr::launch_w4a16(p, m, n, k, static_cast<const uint16_t *>(x),
+                                          static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
+                                          static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a16 launch");
+}
+
 const char *qr_last_error(void) { return g_err; }
 
 const char *qr_version(void) { return "0.1.0"; }

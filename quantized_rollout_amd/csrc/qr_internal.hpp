@@ -56,6 +56,18 @@ hipError_t launch_grouped(int qtype, int64_t num_experts, int64_t n, int64_t k, 
 hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
                                 const float *sb, int64_t n_scales, int64_t *out3, hipStream_t stream);
 
+// W4A16 (qr_w4.hip): group-wise INT4 weights, bfloat16 activations.
+constexpr int64_t kW4Group = 128;  // input channels per INT4 scale group
+struct W4Plan {
+    int unroll;  // consecutive K groups per wave and round
+    int waves;   // waves per block (they split the K groups)
+};
+W4Plan plan_w4a16(int64_t m, int64_t n, int64_t k);
+hipError_t launch_w4a16(const W4Plan &p, int64_t m, int64_t n, int64_t k, const uint16_t *x, const uint8_t *codes,
+                        const float *scales, void *y, bool y_bf16, hipStream_t stream);
+hipError_t launch_quantize_w4(const void *in, bool bf16, int64_t rows, int64_t k, const float *s, uint8_t *codes,
+                              float *scales, hipStream_t stream);
+
 // Environment overrides used for tuning sweeps (0 / -1 = automatic).
 int env_int(const char *name, int dflt);
 

@@ -88,6 +88,24 @@ def test_quantize_validation():
         assert fn(P, 1, 0, 16, NULL, 0, NULL, NULL, S0) == B.QR_OK
 
 
+def test_w4_validation():
+    L = B.lib()
+    fn = L.qr_quantize_weights_w4
+    assert fn(P, 1, 8, 136, NULL, P, P, S0) == B.QR_ERR_UNSUPPORTED and "multiple of 128" in _err()
+    assert fn(P, 1, 8, 0, NULL, P, P, S0) == B.QR_ERR_ARG
+    assert fn(P, 1, -8, 128, NULL, P, P, S0) == B.QR_ERR_ARG
+    assert fn(P, 5, 8, 128, NULL, P, P, S0) == B.QR_ERR_ARG
+    assert fn(MIS, 1, 8, 128, NULL, P, P, S0) == B.QR_ERR_ALIGN
+    assert fn(P, 1, 8, 128, MIS, P, P, S0) == B.QR_ERR_ALIGN
+    assert fn(P, 1, 0, 128, NULL, NULL, NULL, S0) == B.QR_OK
+    lin = L.qr_w4a16_linear
+    assert lin(4, 16, 200, P, P, P, P, 1, S0) == B.QR_ERR_UNSUPPORTED
+    assert lin(4, 16, 128, NULL, P, P, P, 1, S0) == B.QR_ERR_ARG
+    assert lin(4, 16, 128, MIS, P, P, P, 1, S0) == B.QR_ERR_ALIGN
+    assert lin(4, 16, 128, P, P, P, P, 7, S0) == B.QR_ERR_ARG
+    assert lin(0, 16, 128, NULL, NULL, NULL, NULL, 1, S0) == B.QR_OK
+
+
 def test_grouped_validation():
     L = B.lib()
 
