@@ -179,7 +179,7 @@ W4_GROUP = 128  # input channels per INT4 scale group
 
 def quantize_w4(w, s=None, group=W4_GROUP):
     """Group-wise symmetric INT4 codes of w [rows, k] (fp32, or bfloat16 as uint16 bits): returns packed codes
-    [rows, k/2] (even channel in the low nibble) and scales [rows, k/group]."""
+    [rows, k/2] (even channel in the low nibble; sign and magnitude) and scales [rows, k/group]."""
     in_type = BF16 if w.dtype == np.uint16 else F32
     w = _c(w, np.uint16 if in_type == BF16 else np.float32)
     rows, k = w.shape
@@ -192,11 +192,12 @@ def quantize_w4(w, s=None, group=W4_GROUP):
 
 
 def unpack_w4(codes):
-    """Signed INT4 values [rows, 2 * bytes] of packed codes (for tests)."""
-    lo = (codes & 0x0F).astype(np.int8)
-    hi = (codes >> 4).astype(np.int8)
-    lo[lo >= 8] -= 16
-    hi[hi >= 8] -= 16
+    """Signed INT4 values [rows, 2 * bytes] of packed codes (sign-and-magnitude nibbles; for tests)."""
+    def nib(v):
+        mag = (v & 7).astype(np.int8)
+        return np.where(v & 8, -mag, mag).astype(np.int8)
+    lo = nib(codes & 0x0F)
+    hi = nib(codes >> 4)
     out = np.empty((codes.shape[0], codes.shape[1] * 2), np.int8)
     out[:, 0::2] = lo
     out[:, 1::2] = hi

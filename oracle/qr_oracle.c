@@ -335,8 +335,10 @@ void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, in
  *  1. w'_j = w_j, or fl32(w_j * s_j) for W diag(s);
  *  2. a = max_j |w'_j| over the group;  S = fl32(a / 7), or 1 when that is zero;
  *  3. v_j = fl32(w'_j / S);  q_j = round-to-nearest-even of v_j clamped to [-7, 7].
- * Codes are packed two per byte, channel 2i in the low nibble and 2i + 1 in the high nibble, each a 4-bit
- * two's complement value: codes[r, k/2], scales[r, k/group]. k must be a multiple of group (even). */
+ * Codes are packed two per byte, channel 2i in the low nibble and 2i + 1 in the high nibble. The pages fix no
+ * 4-bit storage either; reading: sign and magnitude (bit 3 set for a negative value, bits 0-2 = |q|), which
+ * holds [-7, 7] without loss and stores zero as 0000: codes[r, k/2], scales[r, k/group]. k must be a
+ * multiple of group (even). */
 void or_quantize_w4(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int64_t group,
                     uint8_t *codes, float *scales) {
     int64_t r, g, j;
@@ -358,25 +360,26 @@ void or_quantize_w4(const void *in, int in_type, int64_t rows, int64_t k, const 
             for (j = 0; j < group; ++j) {
                 const int64_t col = g * group + j;
                 float v = wp[j] / S;
-                int q;
+                int q, nib;
                 uint8_t *byte = &codes[r * (k / 2) + col / 2];
                 if (v > 7.0f) v = 7.0f;
                 if (v < -7.0f) v = -7.0f;
                 q = (int)or_rne((double)v);
+                nib = q < 0 ? (8 | -q) : q;
                 if (col % 2 == 0)
-                    *byte = (uint8_t)((*byte & 0xF0) | (q & 0x0F));
+                    *byte = (uint8_t)((*byte & 0xF0) | nib);
                 else
-                    *byte = (uint8_t)((*byte & 0x0F) | ((q & 0x0F) << 4));
+                    *byte = (uint8_t)((*byte & 0x0F) | (nib << 4));
             }
         }
     }
     free(wp);
 }
 
-/* The 4-bit code of channel j of a packed row, as a signed integer. */
+/* The 4-bit code of channel j of a packed row (sign and magnitude), as a signed integer. */
 int or_w4_code(const uint8_t *row_codes, int64_t j) {
     const int nib = (j % 2 == 0) ? (row_codes[j / 2] & 0x0F) : (row_codes[j / 2] >> 4);
-    return nib >= 8 ? nib - 16 : nib;
+    return (nib & 8) ? -(nib & 7) : (nib & 7);
 }
 
 /* Y[m,n] = sum_g S[n,g] * sum_{j in g} x[m,j] * q[n,j]: the W4A16 product with the dequantization of [QaRL] 2.2

@@ -67,8 +67,11 @@ def test_nibble_packing_by_hand():
     j = np.array(([-7, -6, 5, 7, 0, -1, 3, -8 + 1] * (G // 8)), np.float32)
     codes, scales = O.quantize_w4((j * np.float32(0.5))[None, :])
     assert scales[0, 0] == 0.5
-    # channel 0 (-7 = 0b1001) in the low nibble, channel 1 (-6 = 0b1010) in the high nibble, ...
-    assert list(codes[0, :4]) == [0xA9, 0x75, 0xF0, 0x93]
+    # sign and magnitude: channel 0 (-7 = 0b1111) in the low nibble, channel 1 (-6 = 0b1110) in the high
+    # nibble, ..., -1 = 0b1001; zero is 0000 (never the negative zero 1000)
+    assert list(codes[0, :4]) == [0xEF, 0x75, 0x90, 0xF3]
+    z, _ = O.quantize_w4(np.concatenate([np.full(G // 2, -1e-9, np.float32), np.full(G // 2, 1.0, np.float32)])[None])
+    assert (z[0, :G // 4] == 0).all() and (z[0, G // 4:] == 0x77).all()
 
 
 def test_bf16_input_equals_its_fp32_value():
