@@ -129,8 +129,9 @@ qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_
  *   w'_j = w[r,j] * s[j] rounded to fp32 (or w[r,j] when s == NULL)
  *   S    = max_{j in group} |w'_j| / 7 rounded to fp32 (S = 1 when that rounds to 0)
  *   q_j  = round-half-even(clamp(w'_j / S, -7, 7)) with IEEE fp32 division
- * Writes w_codes[n, k/2] (channel 2i in the low nibble of byte i, 2i + 1 in the high nibble, 4-bit two's
- * complement) and w_scales[n, k/QR_W4_GROUP] (fp32). w: device [n,k] fp32 or bf16; s: device fp32 [k] or NULL.
+ * Writes w_codes[n, k/2] (channel 2i in the low nibble of byte i, 2i + 1 in the high nibble; each nibble sign
+ * and magnitude: bit 3 set for a negative code, bits 0-2 = |q|, zero stored as 0) and w_scales[n, k/QR_W4_GROUP]
+ * (fp32). w: device [n,k] fp32 or bf16; s: device fp32 [k] or NULL.
  * k must be a positive multiple of QR_W4_GROUP; w, w_codes and s 16-byte aligned, w_scales 4-byte aligned.
  */
 #define QR_W4_GROUP 128
@@ -142,7 +143,8 @@ qr_status qr_quantize_weights_w4(const void *w, qr_dtype w_type, int64_t n, int6
  *   y[i,c] = sum_g w_scales[c,g] * sum_{j in g} x[i,j] * q[c,j]      (x bfloat16 [m,k], exact products,
  *                                                                      fp32 sums)
  * stored as y_type (bfloat16 rounded to nearest even, or fp32). x and w_codes 16-byte aligned, w_scales 4-byte
- * aligned, y 16-byte aligned; k a positive multiple of QR_W4_GROUP; m <= 1048560. No workspace. Deterministic.
+ * aligned, y 16-byte aligned; k a positive multiple of QR_W4_GROUP; m <= 1048560; the codes of one weight
+ * (n k / 2 bytes) under 4 GiB, else QR_ERR_UNSUPPORTED. No workspace. Deterministic.
  */
 qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const void *w_codes, const float *w_scales,
                           void *y, qr_dtype y_type, void *stream);

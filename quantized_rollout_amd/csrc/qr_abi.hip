@@ -216,6 +216,8 @@ qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const 
     if (k % qr::kW4Group != 0)
         return fail(QR_ERR_UNSUPPORTED, "k must be a multiple of %d (got %lld)", (int)qr::kW4Group, (long long)k);
     if (m > 65535 * 16 || n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "m or n too large");
+    if (n * (k / 2) > (int64_t)UINT32_MAX)
+        return fail(QR_ERR_UNSUPPORTED, "codes of %lld x %lld exceed 4 GiB", (long long)n, (long long)k);
     if (m == 0 || n == 0) return ok();
     if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
         return fail(QR_ERR_ARG, "null operand pointer");
@@ -224,8 +226,9 @@ qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const 
     if (!aligned(y, 16)) return fail(QR_ERR_ALIGN, "y must be 16-byte aligned");
     const qr::W4Plan p = qr::plan_w4a16(m, n, k);
     if (getenv("QR_TRACE") != nullptr)
-        fprintf(stderr, "[qr] w4a16 m=%lld n=%lld k=%lld unroll=%d waves=%d\n", (long long)m, (long long)n,
-                (long long)k, p.unroll, p.waves);
+        fprintf(stderr, "[qr] w4a16 m=%lld n=%lld k=%lld ring=%d tiles=%d waves=%d wk=%d depth=%d xlds=%d\n",
+                (long long)m, (long long)n, (long long)k, p.ring ? 1 : 0, p.tiles, p.waves, p.wk, p.depth,
+                p.x_lds ? 1 : 0);
     const hipError_t e = qr::launch_w4a16(p, m, n, k, static_cast<const uint16_t *>(x),
                                           static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
                                           static_cast<hipStream_t>(stream));

@@ -243,8 +243,6 @@ struct Ring {
     static constexpr int kLoadsB = kRowsB / 16;
     static constexpr int kLoads = 1 + kLoadsB;           // buffer loads per wavefront per stage
 };
-constexpr int kBufferFlags = 0x00020000;          // raw buffer descriptor word 3 (32-bit untyped data)
-constexpr uint32_t kOutOfRange = 0x80000000u;      // a buffer offset past every operand (they stay below 2 GiB)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -264,62 +262,6 @@ template <>
 struct Acc32<kFp8> {
     typedef float __attribute__((ext_vector_type(16))) type;
 };
-
-// One 16-byte-per-lane buffer load straight into LDS: lane l's 16 bytes land at lds_base + 16 l. Issued as
-// assembly so that the compiler neither tracks it nor inserts its own waits for the LDS it writes: the kernel
-// counts these loads itself (vmcnt) and orders them with the workgroup barrier. M0 (the LDS base register)
-// is restored afterwards.
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, uint32_t voffset) {
-    int saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_base), "v"(voffset), "s"(rsrc)
-        : "memory");
-}
-
-// Raw buffer descriptor (32-bit untyped elements, no stride): base, num_records bytes; loads at offsets
-// >= num_records return zero.
-__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    v4i r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffu));
-    r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = kBufferFlags;
-    return r;
-}
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-// LDS address of a wave-uniform pointer, as a scalar
-__device__ __forceinline__ uint32_t lds_addr(uint8_t *p) {
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)(lds_u8_t *)p);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt with the vector-memory counter at N and the LDS counter at zero
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
-
-// workgroup barrier that the compiler may not move memory accesses across (the loads into LDS it cannot see
-// are ordered by it)
-__device__ __forceinline__ void barrier_fenced() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 template <int QT, int BM>
 __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(

@@ -59,10 +59,17 @@ hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t coun
 // W4A16 (qr_w4.hip): group-wise INT4 weights, bfloat16 activations.
 constexpr int64_t kW4Group = 128;  // input channels per INT4 scale group
 struct W4Plan {
-    int unroll;  // consecutive K groups per wave and round
-    int waves;   // waves per block (they split the K groups)
+    int tiles;   // tiles of 16 output channels per wave (they share each activation operand)
+    int waves;   // waves per block
+    int wk;      // waves of a channel group that split K (divides waves)
+    int depth;   // stages of codes and scales in flight per wave (registers: 1 or 2; LDS ring: 2, 4 or 8)
+    bool x_lds;  // the token tile's activation rows staged in LDS
+    bool ring;   // codes and scales streamed through a per-wave LDS ring (needs x_lds, one tile per wave)
 };
+constexpr size_t kW4MaxLds = 65536;       // dynamic LDS bytes per block, register-stage kernel
+constexpr size_t kW4MaxRingLds = 163840;  // dynamic LDS bytes per block, LDS-ring kernel (all of a CU's LDS)
 W4Plan plan_w4a16(int64_t m, int64_t n, int64_t k);
+size_t w4_lds_bytes(const W4Plan &p, int64_t m, int64_t k);
 hipError_t launch_w4a16(const W4Plan &p, int64_t m, int64_t n, int64_t k, const uint16_t *x, const uint8_t *codes,
                         const float *scales, void *y, bool y_bf16, hipStream_t stream);
 hipError_t launch_quantize_w4(const void *in, bool bf16, int64_t rows, int64_t k, const float *s, uint8_t *codes,

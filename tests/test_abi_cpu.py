@@ -104,6 +104,8 @@ def test_w4_validation():
     assert lin(4, 16, 128, MIS, P, P, P, 1, S0) == B.QR_ERR_ALIGN
     assert lin(4, 16, 128, P, P, P, P, 7, S0) == B.QR_ERR_ARG
     assert lin(0, 16, 128, NULL, NULL, NULL, NULL, 1, S0) == B.QR_OK
+    # the codes of one weight must stay under 4 GiB (32-bit offsets in the kernel)
+    assert lin(1, 1 << 20, 1 << 13, P, P, P, P, 1, S0) == B.QR_ERR_UNSUPPORTED and "4 GiB" in _err()
 
 
 def test_grouped_validation():

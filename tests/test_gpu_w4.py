@@ -54,18 +54,45 @@ def _linear_case(m, n, k, seed):
 
 
 SHAPES = [(1, 16, 128), (1, 37, 384), (5, 200, 1536), (16, 1000, 3584), (17, 64, 1024), (40, 96, 2048),
-          (1, 1536, 8960)]
+          (1, 1536, 8960), (3, 300, 18944)]
 
 
-@pytest.mark.parametrize("unroll,waves", [(None, None), (1, 1), (1, 3), (2, 8), (4, 2), (4, 16)])
-def test_w4a16_linear_parity(unroll, waves, monkeypatch, capfd):
-    if unroll is not None:
-        monkeypatch.setenv("QR_W4_UNROLL", str(unroll))
-        monkeypatch.setenv("QR_W4_WAVES", str(waves))
+def _expected_plan(m, k, env):
+    """(ring, x_lds) the library must choose for forced knobs: the LDS ring when the activation rows, the waves'
+    rings and partials fit in 160 KiB; else activations in LDS when asked for (every register-stage plan here
+    sets QR_W4_XLDS; a ring plan falls back only where the rows alone exceed 64 KiB) and rows and partials fit
+    in 64 KiB."""
+    tiles, waves, wk = env.get("QR_W4_TILES", 1), env["QR_W4_WAVES"], env["QR_W4_WK"]
+    depth = env.get("QR_W4_DEPTH", 2)
+    xb = min(m, 16) * (2 * k + 16)
+    part = waves * 1024 if wk > 1 else 0
+    if env.get("QR_W4_RING", 1) and xb + waves * max(depth, 2) * 1280 + part <= 163840:
+        return 1, 1
+    return 0, int(env.get("QR_W4_XLDS", 1) != 0 and xb + part * tiles <= 65536)
+
+
+PLANS = [None,
+         dict(QR_W4_RING=1, QR_W4_WAVES=1, QR_W4_WK=1, QR_W4_DEPTH=2),
+         dict(QR_W4_RING=1, QR_W4_WAVES=8, QR_W4_WK=1, QR_W4_DEPTH=4),
+         dict(QR_W4_RING=1, QR_W4_WAVES=16, QR_W4_WK=16, QR_W4_DEPTH=4),
+         dict(QR_W4_RING=1, QR_W4_WAVES=6, QR_W4_WK=3, QR_W4_DEPTH=8),
+         dict(QR_W4_RING=1, QR_W4_WAVES=4, QR_W4_WK=2, QR_W4_DEPTH=2),
+         dict(QR_W4_RING=0, QR_W4_TILES=1, QR_W4_WAVES=3, QR_W4_WK=3, QR_W4_DEPTH=2, QR_W4_XLDS=1),
+         dict(QR_W4_RING=0, QR_W4_TILES=2, QR_W4_WAVES=8, QR_W4_WK=4, QR_W4_DEPTH=2, QR_W4_XLDS=0),
+         dict(QR_W4_RING=0, QR_W4_TILES=2, QR_W4_WAVES=5, QR_W4_WK=5, QR_W4_DEPTH=1, QR_W4_XLDS=1),
+         dict(QR_W4_RING=0, QR_W4_TILES=4, QR_W4_WAVES=2, QR_W4_WK=1, QR_W4_DEPTH=1, QR_W4_XLDS=1),
+         dict(QR_W4_RING=0, QR_W4_TILES=4, QR_W4_WAVES=16, QR_W4_WK=8, QR_W4_DEPTH=1, QR_W4_XLDS=0)]
+
+
+@pytest.mark.parametrize("plan", PLANS, ids=lambda p: "default" if p is None else "-".join(
+    "%s%d" % (k[6:].lower(), v) for k, v in p.items()))
+def test_w4a16_linear_parity(plan, monkeypatch, capfd):
+    for key, v in (plan or {}).items():
+        monkeypatch.setenv(key, str(v))
     monkeypatch.setenv("QR_TRACE", "1")
     for i, (m, n, k) in enumerate(SHAPES):
         xb, codes, scales = _linear_case(m, n, k, 700 + i)
-        log("w4a16 unroll=%s waves=%s m=%d n=%d k=%d" % (unroll, waves, m, n, k))
+        log("w4a16 plan=%s m=%d n=%d k=%d" % (plan, m, n, k))
         y_ref, y64 = O.w4a16_linear(xb, codes, scales)
         y = qr.qr_w4a16_linear(dev(xb), dev(codes), dev(scales))
         yf = qr.qr_w4a16_linear(dev(xb), dev(codes), dev(scales), y_dtype=torch.float32)
@@ -75,8 +102,11 @@ def test_w4a16_linear_parity(unroll, waves, monkeypatch, capfd):
         bound = 1e-5 * np.abs(y64).max() + 1e-30
         assert np.abs(host(yf).astype(np.float64) - y64).max() <= bound, (m, n, k)
         err = capfd.readouterr().err
-        if unroll is not None:
-            assert "unroll=%d waves=%d" % (unroll, waves) in err, err
+        if plan is not None:
+            ring, xlds = _expected_plan(m, k, plan)
+            want = "ring=%d tiles=%d waves=%d wk=%d" % (ring, plan.get("QR_W4_TILES", 1) if not ring else 1,
+                                                        plan["QR_W4_WAVES"], plan["QR_W4_WK"])
+            assert want in err and ("xlds=%d" % xlds) in err, (want, err)
 
 
 def test_w4a16_deterministic_and_batch_rows_independent():
