@@ -45,6 +45,7 @@ LINEARS = (("qkv", 2048, 1536), ("o", 1536, 1536), ("gate_up", 17920, 1536), ("d
 BATCHES = (1, 16, 64)
 M_MAX = max(BATCHES)
 WEIGHT_STD = 0.02
+W4_GROUP = 128                # input channels per INT4 scale group (W4A16)
 
 
 def log(msg):
@@ -294,6 +295,60 @@ def measure_fp8_7b(dev, reps):
                                          "mfma_frac": round(no / ms / 1e9 / MFMA_PEAK_TOPS, 3)}
             del g
     del wc, ws, xc, xs, y, wsp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def bytes_w4a16(m, n, k, out_bytes=2):
+    """HBM bytes a W4A16 linear must move: packed codes, group scales, bf16 activations, the output."""
+    return n * k // 2 + 4 * n * (k // W4_GROUP) + 2 * m * k + out_bytes * m * n
+
+
+def measure_w4a16_7b(dev, reps):
+    """7B-shaped W4A16 linears (the same four shapes as the FP8 ones), INT4 codes and group scales of 5
+    distinct layers (585 MB) rotated; the decode batches m = 1 and 16."""
+    import torch
+
+    import quantized_rollout_amd as qr
+
+    L = 5
+    lins = (("qkv", 4608, 3584), ("o", 3584, 3584), ("gate_up", 37888, 3584), ("down", 3584, 18944))
+    batches = (1, 16)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    wc, ws, x, y = {}, {}, {}, {}
+    for name, n, k in lins:
+        w = normal_bf16(gen, (L * n, k), WEIGHT_STD, dev)
+        wc[name], ws[name] = qr.qr_quantize_weights_w4(w)
+        del w
+        x[name] = activations_bf16(gen, 1, max(batches), k, dev)[0]
+        y[name] = torch.empty((max(batches), n), dtype=torch.bfloat16, device=dev)
+    out = {}
+    for m in batches:
+        def run(m=m):
+            for l in range(L):
+                for name, n, k in lins:
+                    qr.qr_w4a16_linear(x[name][:m], wc[name][l * n:(l + 1) * n], ws[name][l * n:(l + 1) * n],
+                                       y=y[name][:m])
+        g = TimedGraph(run, L * len(lins))
+        ms = g.time_ms(reps)
+        nb = L * sum(bytes_w4a16(m, n, k) for _, n, k in lins)
+        out["m%d" % m] = {"us_per_layer": round(ms * 1e3 / L, 2), "GB/s": round(nb / ms / 1e6, 1),
+                          "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 3)}
+        del g
+        for name, n, k in lins:
+            def run1(m=m, name=name, n=n):
+                for l in range(L):
+                    qr.qr_w4a16_linear(x[name][:m], wc[name][l * n:(l + 1) * n], ws[name][l * n:(l + 1) * n],
+                                       y=y[name][:m])
+            g = TimedGraph(run1, L)
+            ms = g.time_ms(reps)
+            nb = L * bytes_w4a16(m, n, k)
+            out["m%d_%s" % (m, name)] = {"us": round(ms * 1e3 / L, 2), "GB/s": round(nb / ms / 1e6, 1),
+                                         "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 3)}
+            del g
+    del wc, ws, x, y
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
@@ -649,6 +704,8 @@ def main():
         extra["fp8_7b_linears"] = measure_fp8_7b(dev, max(5, args.reps // 5))
         log("MoE grouped linears")
         extra["moe_fp8_grouped"] = measure_moe(dev, max(5, args.reps // 5))
+        log("W4A16 7B-shaped linears")
+        extra["w4a16_7b_linears"] = measure_w4a16_7b(dev, max(5, args.reps // 5))
 
     cpu = None
     if not args.no_cpu_baseline:
