@@ -548,18 +548,7 @@ hipError_t launch_ring(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const
     hipLaunchKernelGGL((gemm_ring_kernel<QT, BM>), dim3(grid), dim3(Ring<BM>::kThreads), 0, stream, m, n, k, xq, xs,
                        wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits, g.stages_per_split,
                        workspace);
-    if (g.splits > 1) {
-        const int64_t total_out = m * n;
-        const bool vec = (n % 4) == 0;
-        const int64_t items = vec ? total_out / 4 : total_out;
-        const int blocks = (int)std::min<int64_t>((items + 255) / 256, 4096);
-        if (vec)
-            hipLaunchKernelGGL((splitk_reduce_kernel<QT, 4>), dim3(blocks), dim3(256), 0, stream, m, n, g.splits,
-                               workspace, xs, ws, y, y_bf16 ? 1 : 0, acc_out);
-        else
-            hipLaunchKernelGGL((splitk_reduce_kernel<QT, 1>), dim3(blocks), dim3(256), 0, stream, m, n, g.splits,
-                               workspace, xs, ws, y, y_bf16 ? 1 : 0, acc_out);
-    }
+    if (g.splits > 1) launch_splitk_reduce(QT, m, n, g.splits, workspace, xs, ws, y, y_bf16, acc_out, stream);
     return hipGetLastError();
 }
 
@@ -642,6 +631,23 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
     }
     g.ws_bytes = g.splits > 1 ? (size_t)g.splits * (size_t)m * (size_t)n * 4 : 0;
     return g;
+}
+
+void launch_splitk_reduce(int qtype, int64_t m, int64_t n, int splits, const void *partial, const float *xs,
+                          const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+    const int64_t total_out = m * n;
+    const bool vec = (n % 4) == 0;
+    const int64_t items = vec ? total_out / 4 : total_out;
+    const int blocks = (int)std::min<int64_t>((items + 255) / 256, 4096);
+#define QR_REDUCE(QT, V)                                                                                       \
+    hipLaunchKernelGGL((splitk_reduce_kernel<QT, V>), dim3(blocks), dim3(256), 0, stream, m, n, splits, partial, \
+                       xs, ws, y, y_bf16 ? 1 : 0, acc_out)
+    if (qtype == kInt8) {
+        if (vec) QR_REDUCE(kInt8, 4); else QR_REDUCE(kInt8, 1);
+    } else {
+        if (vec) QR_REDUCE(kFp8, 4); else QR_REDUCE(kFp8, 1);
+    }
+#undef QR_REDUCE
 }
 
 hipError_t launch_gemm(const GemmPlan &g, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,

@@ -25,6 +25,9 @@ struct GemmPlan {
     size_t ws_bytes;       // splits x m x n x 4 when split, else 0
 };
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k);
+// adds splits x [m, n] partial sums (int32 for INT8, fp32 for FP8) in split order, then the epilogue
+void launch_splitk_reduce(int qtype, int64_t m, int64_t n, int splits, const void *partial, const float *xs,
+                          const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream);
 hipError_t launch_gemm(const GemmPlan &g, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                        const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                        void *workspace, hipStream_t stream);
@@ -36,6 +39,7 @@ struct LinearPlan {
     int unroll;        // GEMV: 64-byte K steps per slice (1-KiB weight loads per tile per slice)
     int tiles;         // GEMV: 16-channel tiles per block
     int64_t n_tiles;   // GEMV: 16-channel tiles
+    int splits;        // GEMV: K splits across blocks (> 1: partial sums in the workspace, then a reduction)
     GemmPlan gemm;     // GEMM (kind 1)
     size_t ws_bytes;   // workspace bytes
 };

@@ -62,7 +62,8 @@ template <int QT, int MT, int U, int TB, int WMAX>
 __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq,
                                                          const float *__restrict__ xs, const uint8_t *__restrict__ wq,
                                                          const float *__restrict__ ws, void *__restrict__ y,
-                                                         int y_bf16, void *__restrict__ acc_out) {
+                                                         int y_bf16, void *__restrict__ acc_out, int splits,
+                                                         void *__restrict__ partial) {
     typedef typename Acc<QT>::type acc_t;
     static_assert(QT == kInt8 || U % 2 == 0, "FP8 pairs load instructions");
     extern __shared__ int32_t red[];  // [waves][TB][MT][4][64]
@@ -75,6 +76,11 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
     const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
     constexpr int64_t kSlice = 64 * U;
     const int64_t slices = (k + kSlice - 1) / kSlice;
+    // split-K across blocks (blockIdx.z): this block's slices [lo, hi); with splits > 1 the raw sums go to
+    // partial[split][m][n] and a separate reduction adds the splits in order and applies the epilogue
+    const int64_t per_split = (slices + splits - 1) / splits;
+    const int64_t lo = (int64_t)blockIdx.z * per_split;
+    const int64_t hi = lo + per_split < slices ? lo + per_split : slices;
 
     // weight rows of this lane (rows past n re-read row n-1; those columns are never stored)
     const uint8_t *__restrict__ wrow[TB];
@@ -132,7 +138,8 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
         }
     };
     const int64_t full = k / kSlice;
-    for (int64_t sl = wave; sl < full; sl += waves) {
+    const int64_t full_hi = hi < full ? hi : full;
+    for (int64_t sl = lo + wave; sl < full_hi; sl += waves) {
         const int64_t kb = sl * kSlice;
         uint4 xv[MT][U], wv[TB][U];
 #pragma unroll
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
 #pragma unroll
         for (int r = 0; r < TB; ++r) mma(acc[r], xv, wv[r]);
     }
-    if (full < slices && wave == full % waves) {  // the partial last slice
+    if (full < slices && full >= lo && full < hi && wave == (full - lo) % waves) {  // the partial last slice
         const int64_t kb = full * kSlice;
         uint4 xv[MT][U], wv[TB][U];
 #pragma unroll
@@ -207,9 +214,19 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
                     }
                 }
             }
+            const int64_t col = (tile0 + r) * 16 + j;
+            if (splits > 1) {
+                // raw sums of this split; the reduction applies the epilogue
+                if (col >= n) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m0 + mt * 16 + 4 * g + i;
+                    if (row < m) store_acc(partial, ((int64_t)blockIdx.z * m + row) * n + col, acc[r][mt][i]);
+                }
+                continue;
+            }
             // epilogue: y = acc * x_scale[row] * w_scale[col]; the scales are loaded together from clamped
             // indices (one round trip), then the stores are predicated
-            const int64_t col = (tile0 + r) * 16 + j;
             const float sw = ws[col < n ? col : n - 1];
             float sx[4];
 #pragma unroll
@@ -232,12 +249,14 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
 
 template <int QT, int MT, int U, int TB, int WMAX>
 void launch_gemv_t(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
-                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
+                   hipStream_t stream) {
     const int64_t m_blocks = (m + 16 * MT - 1) / (16 * MT);
-    const dim3 grid((unsigned)((p.n_tiles + TB - 1) / TB), (unsigned)m_blocks);
+    const dim3 grid((unsigned)((p.n_tiles + TB - 1) / TB), (unsigned)m_blocks, (unsigned)p.splits);
     const size_t lds = p.waves > 1 ? (size_t)p.waves * TB * MT * 256 * 4 : 0;
     hipLaunchKernelGGL((gemv_kernel<QT, MT, U, TB, WMAX>), grid, dim3(p.waves * 64), lds, stream, m, n, k, xq, xs, wq,
-                       ws, y, y_bf16 ? 1 : 0, acc_out);
+                       ws, y, y_bf16 ? 1 : 0, acc_out, p.splits, workspace);
+    if (p.splits > 1) launch_splitk_reduce(QT, m, n, p.splits, workspace, xs, ws, y, y_bf16, acc_out, stream);
 }
 
 // (m_tiles, unroll, tiles per block, most waves per block); the planner further limits the waves so that the
@@ -257,10 +276,11 @@ int gemv_variant_waves(int mt, int u, int tb) {
 
 template <int QT>
 void launch_gemv_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
-                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
+                   const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
+                   hipStream_t stream) {
 #define QR_GEMV_CASE(MT_, U_, TB_, W_)                                                                          \
     if (p.m_tiles == MT_ && p.unroll == U_ && p.tiles == TB_) {                                                 \
-        launch_gemv_t<QT, MT_, U_, TB_, W_>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);            \
+        launch_gemv_t<QT, MT_, U_, TB_, W_>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream); \
         return;                                                                                                 \
     }
     QR_GEMV_VARIANTS(QR_GEMV_CASE)
@@ -339,10 +359,24 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     int cap = gemv_variant_waves(p.m_tiles, u, tb);
     if (cap > 64 / (tb * p.m_tiles)) cap = 64 / (tb * p.m_tiles);
     if (wave_cap > 0 && cap > wave_cap && env_int("QR_GEMV_WAVES", 0) == 0) cap = wave_cap;
-    int64_t waves = slices < cap ? slices : cap;
+    // split K across blocks when four token tiles make each block long, the blocks would leave most CUs idle
+    // and K is deep: two splits; the partial sums (splits x m x n x 4 bytes) go to the workspace and a separate
+    // reduction adds them in split order. The reduction's launch costs more than it saves at m <= 32
+    // (measured on MI355X: 1.5B down at m = 64 from 19.3 to 14.8 us; at m = 1 and 16 8.7 -> 9.6, 10.2 -> 10.5)
+    const int64_t blocks = ((p.n_tiles + tb - 1) / tb) * m_blocks;
+    int64_t splits = 1;
+    const int64_t waves_cap = cap;
+    if (p.m_tiles == 4 && blocks < 128 && slices >= 16) splits = 2;
+    const int fs = env_int("QR_GEMV_SPLITS", 0);
+    if (fs >= 1) splits = std::min<int64_t>(fs, slices);
+    const int64_t per_split = (slices + splits - 1) / splits;
+    splits = (slices + per_split - 1) / per_split;  // no split without a slice
+    int64_t waves = per_split < waves_cap ? per_split : waves_cap;
     const int forced_w = env_int("QR_GEMV_WAVES", 0);
     if (forced_w >= 1 && forced_w <= cap) waves = forced_w;
     p.waves = (int)(waves < 1 ? 1 : waves);
+    p.splits = (int)splits;
+    p.ws_bytes = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * 4 : 0;
     return p;
 }
 
@@ -351,9 +385,9 @@ hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, i
                          void *workspace, hipStream_t stream) {
     if (p.kind == 0) {
         if (qtype == kInt8)
-            launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+            launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
         else
-            launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
+            launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
     } else {
         return launch_gemm(p.gemm, qtype, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
     }

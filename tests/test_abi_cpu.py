@@ -135,10 +135,22 @@ def test_count_validation():
 
 def test_workspace_sizes(monkeypatch):
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
-        # GEMV plans, and GEMM plans with a tile for at least half the CUs, reduce inside their workgroups
-        for m, n, k in ((1, 1536, 8960), (16, 2048, 1536), (64, 37888, 3584), (2048, 37888, 3584),
-                        (128, 37888, 3584)):
+        # GEMV plans with enough blocks, and GEMM plans with a tile for at least half the CUs, reduce inside
+        # their workgroups
+        for m, n, k in ((1, 1536, 8960), (16, 2048, 1536), (64, 37888, 3584), (1, 3584, 18944),
+                        (2048, 37888, 3584), (128, 37888, 3584)):
             assert B.qr_workspace_bytes(q, m, n, k) == 0
+        # GEMV with four token tiles, few channel tiles and a deep K (1.5B down at m = 64: 96 tiles, 35 slices
+        # of 256 bytes): K split over 2 blocks per tile, the partial sums in the workspace; none at m <= 32
+        for m in (1, 16, 32):
+            assert B.qr_workspace_bytes(q, m, 1536, 8960) == 0
+        for m in (33, 64):
+            assert B.qr_workspace_bytes(q, m, 1536, 8960) == 2 * m * 1536 * 4
+        monkeypatch.setenv("QR_GEMV_SPLITS", "7")
+        assert B.qr_workspace_bytes(q, 5, 1536, 8960) == 7 * 5 * 1536 * 4
+        monkeypatch.setenv("QR_GEMV_SPLITS", "64")  # never a split without a slice: 35 slices -> 35 splits
+        assert B.qr_workspace_bytes(q, 5, 1536, 8960) == 35 * 5 * 1536 * 4
+        monkeypatch.delenv("QR_GEMV_SPLITS")
         # few tiles: the planner's cost model splits K (runs of at least 4 stages of 64 bytes); the partial sums
         # take splits x m x n x 4 bytes
         assert B.qr_workspace_bytes(q, 512, 3584, 18944) == 9 * 512 * 3584 * 4    # 28 tiles of 256 x 256

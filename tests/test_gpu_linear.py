@@ -111,20 +111,49 @@ def test_fp8_determinism():
 
 
 def test_no_workspace_needed():
-    """Every plan reduces inside its blocks: the call works with no workspace at all."""
-    xc, xs, wc, ws = _quantized_operands(16, 1536, 8960, O.INT8, seed=79)
-    assert qr.qr_workspace_bytes(qr.QR_INT8, 16, 1536, 8960) == 0
+    """A plan that reduces inside its blocks works with no workspace at all (7B o shape at m = 16)."""
+    xc, xs, wc, ws = _quantized_operands(16, 3584, 3584, O.INT8, seed=79)
+    assert qr.qr_workspace_bytes(qr.QR_INT8, 16, 3584, 3584) == 0
     y_ref, acc_i, _ = O.linear(O.INT8, xc, xs, wc, ws, O.BF16)
-    y = torch.empty((16, 1536), dtype=torch.bfloat16, device="cuda")
-    acc = torch.empty((16, 1536), dtype=torch.int32, device="cuda")
+    y = torch.empty((16, 3584), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty((16, 3584), dtype=torch.int32, device="cuda")
     L = qr.lib()
     ops = [dev(a) for a in (xc, xs, wc, ws)]  # kept alive until the kernel has run
-    rc = L.qr_w8a8_linear(qr.QR_INT8, 16, 1536, 8960, *[t.data_ptr() for t in ops], y.data_ptr(), qr.QR_BF16,
+    rc = L.qr_w8a8_linear(qr.QR_INT8, 16, 3584, 3584, *[t.data_ptr() for t in ops], y.data_ptr(), qr.QR_BF16,
                           acc.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     torch.cuda.synchronize()
     assert np.array_equal(host(acc), acc_i)
     assert_y_close(host(y), y_ref, "no workspace")
+
+
+@pytest.mark.parametrize("splits", [None, 2, 3, 16])
+def test_gemv_split_k(splits, monkeypatch, capfd):
+    """The GEMV with K split across blocks (partial sums in the workspace, added in split order): INT8
+    accumulators bit-exact, FP8 within the fp32 bound and deterministic, on the 1.5B down shape at every
+    decode batch and on a ragged shape with a partial last slice."""
+    if splits is not None:
+        monkeypatch.setenv("QR_GEMV_SPLITS", str(splits))
+    monkeypatch.setenv("QR_TRACE", "1")
+    for i, (m, n, k) in enumerate([(1, 1536, 8960), (16, 1536, 8960), (64, 1536, 8960), (37, 200, 4368)]):
+        for oq in (O.INT8, O.FP8):
+            xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1500 + 10 * i + oq)
+            what = "gemv split=%s %s m=%d n=%d k=%d" % (splits, oq, m, n, k)
+            log(what)
+            _check(oq, xc, xs, wc, ws, what)
+            if oq == O.FP8:
+                a, _ = _run(oq, xc, xs, wc, ws)
+                b, _ = _run(oq, xc, xs, wc, ws)
+                assert np.array_equal(a, b), what
+            err = capfd.readouterr().err
+            assert "kind=0" in err, err
+            if splits is not None:
+                u = 4 if "unroll=4" in err else int(err.split("unroll=")[1].split()[0])
+                slices = -(-k // (64 * u))
+                per = -(-slices // min(splits, slices))
+                assert "splits=%d " % (-(-slices // per)) in err, err
+            elif n == 1536:
+                assert ("splits=2 " if m > 32 else "splits=1 ") in err, err
 
 
 # every compiled GEMV variant: (token tiles, 64-byte loads per slice, weight tiles per block)
