@@ -52,6 +52,8 @@ def lib():
         L.or_grouped_linear.restype = ctypes.c_int
         L.or_count_code_changes.argtypes = [vp, vp, i64, i32, vp, vp, i64, vp]
         L.or_count_code_changes.restype = None
+        L.or_requantize_weights.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.or_requantize_weights.restype = None
         L.or_quantize_w4.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp]
         L.or_quantize_w4.restype = None
         L.or_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, i64, i32, vp, vp]
@@ -171,6 +173,26 @@ def count_code_changes(a, b, qtype, sa=None, sb=None):
     out = np.zeros(3, np.int64)
     lib().or_count_code_changes(_p(a), _p(b), a.size, qtype, _p(sa), _p(sb), ns, _p(out))
     return out
+
+
+# ---- next row: requantize + diff -----------------------------------------------------------------------
+def requantize_weights(w, qtype, prev_codes, prev_scales, s=None):
+    """One publish of W + dW: the weight quantizer of ``w`` [rows, k] (fp32, or bfloat16 as uint16 bits), and
+    per row the changed-code triple against the previous publish. Returns (codes, scales, row_counts [rows, 3]
+    int32, out3 [3] int64)."""
+    in_type = BF16 if np.asarray(w).dtype == np.uint16 else F32
+    w = _c(w, np.uint16 if in_type == BF16 else np.float32)
+    rows, k = w.shape
+    prev_codes, prev_scales = _c(prev_codes, np.uint8), _c(prev_scales, np.float32)
+    assert prev_codes.shape == (rows, k) and prev_scales.shape == (rows,)
+    s = None if s is None else _c(s, np.float32)
+    codes = np.empty((rows, k), np.uint8)
+    scales = np.empty((rows,), np.float32)
+    row_counts = np.empty((rows, 3), np.int32)
+    out3 = np.empty(3, np.int64)
+    lib().or_requantize_weights(_p(w), in_type, rows, k, _p(s), qtype, _p(prev_codes), _p(prev_scales), _p(codes),
+                                _p(scales), _p(row_counts), _p(out3))
+    return codes, scales, row_counts, out3
 
 
 # ---- next row: W4A16 ------------------------------------------------------------------------------------

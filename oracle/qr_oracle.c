@@ -325,6 +325,34 @@ void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, in
 }
 
 /* ------------------------------------------------------------------------------------------------------
+ * next row: requantize + diff (one publish of W + dW)
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* [QaRL] 3.1 publishes the low-bit weights to the inference engine after every optimizer step and [QuRL] 4.3
+ * observes that such an update changes few codes: the publish of W + dW is the weight quantizer (a1) followed
+ * by the changed-code count (a5) against the previous publish, here per row. For every row r:
+ *   codes[r,:], scales[r] = the a1 quantizer of w[r,:] (with W diag(s) when s is given);
+ *   row_counts[r] = {#j: prev_codes[r,j] != codes[r,j],  #j: value(prev_codes[r,j]) != value(codes[r,j]),
+ *                    bits(prev_scales[r]) != bits(scales[r])}
+ * and out3 = the sums of row_counts over the rows (the a5 triple of the whole tensor). */
+void or_requantize_weights(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int qtype,
+                           const uint8_t *prev_codes, const float *prev_scales, uint8_t *codes, float *scales,
+                           int32_t *row_counts, int64_t *out3) {
+    int64_t r, c[3];
+    or_quantize_rows(in, in_type, rows, k, s, s ? OR_S_MUL : OR_S_NONE, qtype, codes, scales);
+    out3[0] = out3[1] = out3[2] = 0;
+    for (r = 0; r < rows; ++r) {
+        or_count_code_changes(prev_codes + r * k, codes + r * k, k, qtype, prev_scales + r, scales + r, 1, c);
+        row_counts[3 * r + 0] = (int32_t)c[0];
+        row_counts[3 * r + 1] = (int32_t)c[1];
+        row_counts[3 * r + 2] = (int32_t)c[2];
+        out3[0] += c[0];
+        out3[1] += c[1];
+        out3[2] += c[2];
+    }
+}
+
+/* ------------------------------------------------------------------------------------------------------
  * next row: W4A16 (group-wise INT4 weights, bfloat16 activations)
  * ---------------------------------------------------------------------------------------------------- */
 

@@ -73,9 +73,15 @@ int or_grouped_linear(int qtype, int64_t num_experts, int64_t n, int64_t k, cons
 void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
                            const float *sb, int64_t n_scales, int64_t *out3);
 
+/* next row: one publish of W + dW: the a1 quantizer, then per row the a5 triple against the previous
+ * publish (row_counts [rows][3]: bytes, values, scale changed) and its sums in out3 */
+void or_requantize_weights(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int qtype,
+                           const uint8_t *prev_codes, const float *prev_scales, uint8_t *codes, float *scales,
+                           int32_t *row_counts, int64_t *out3);
+
 /* ---- next row: W4A16 ------------------------------------------------------------------------------- */
 /* Group-wise symmetric INT4 weights, q in [-7, 7], S = max|w'| / 7 per group of `group` input channels;
- * two codes per byte (even channel in the low nibble); scales[rows, k/group]. */
+ * two codes per byte (even channel in the low nibble), each sign and magnitude; scales[rows, k/group]. */
 void or_quantize_w4(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int64_t group,
                     uint8_t *codes, float *scales);
 int  or_w4_code(const uint8_t *row_codes, int64_t j);
