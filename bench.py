@@ -300,6 +300,42 @@ def measure_fp8_7b(dev, reps):
     return out
 
 
+def measure_publish_fused(stack, reps):
+    """The publish of the 1.5B stack (112 matrices, bf16 masters -> INT8) as one fused requantize + diff pass per
+    weight (codes, scales, per-row change triples and their sums) against the step's separate quantize (a1) and
+    changed-code count (a5); both out of place against the same previous publish, so they can be compared."""
+    import torch
+
+    qr = stack.qr
+    rc = {name: torch.empty((LAYERS * n, 3), dtype=torch.int32, device=stack.dev) for name, n, _ in LINEARS}
+    o3 = torch.empty((len(LINEARS), 3), dtype=torch.int64, device=stack.dev)
+
+    def fused():
+        for i, (name, n, k) in enumerate(LINEARS):
+            qr.qr_requantize_weights(stack.w[name], qr.QR_INT8, stack.pc[name], stack.ps[name],
+                                     codes=stack.wc[name], scales=stack.ws[name], row_counts=rc[name], out3=o3[i])
+
+    def separate():
+        stack.publish_quantize()
+        stack.publish_count()
+
+    gs, gf = TimedGraph(separate, len(LINEARS) + 2), TimedGraph(fused, 2 * len(LINEARS))
+    ms_sep, ms_fused = gs.time_ms(reps), gf.time_ms(reps)
+    gs.replay()
+    torch.cuda.synchronize()
+    sep_codes, sep_count = stack.codes.clone(), stack.count.clone()
+    gf.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(stack.codes, sep_codes) and torch.equal(o3.sum(dim=0), sep_count))
+    codes, rows = stack.codes_total, stack.rows_total
+    nb = 2 * codes + codes + codes + 4 * rows + 4 * rows + 12 * rows  # masters, previous codes, new codes, scales
+    del gs, gf
+    return {"us_fused": round(ms_fused * 1e3, 1), "us_separate": round(ms_sep * 1e3, 1),
+            "speedup": round(ms_sep / ms_fused, 3), "GB/s": round(nb / ms_fused / 1e6, 1),
+            "hbm_frac": round(nb / ms_fused / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nb),
+            "changed": [int(v) for v in sep_count.tolist()], "matches_separate": same}
+
+
 def bytes_w4a16(m, n, k, out_bytes=2):
     """HBM bytes a W4A16 linear must move: packed codes, group scales, bf16 activations, the output."""
     return n * k // 2 + 4 * n * (k // W4_GROUP) + 2 * m * k + out_bytes * m * n
@@ -706,6 +742,8 @@ def main():
         extra["moe_fp8_grouped"] = measure_moe(dev, max(5, args.reps // 5))
         log("W4A16 7B-shaped linears")
         extra["w4a16_7b_linears"] = measure_w4a16_7b(dev, max(5, args.reps // 5))
+        log("fused requantize + diff publish")
+        extra["publish_fused_requant_diff"] = measure_publish_fused(stack, max(5, args.reps // 5))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -124,6 +124,24 @@ qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_
                                 const float *sb, int64_t n_scales, int64_t *out3, void *stream);
 
 /*
+ * One publish of updated weights (next row: [QaRL] 3.1 publishes the low-bit weights to the inference engine
+ * after every optimizer step; [QuRL] 4.3: the update between steps is much smaller than the quantization error,
+ * so few codes change). In one pass over w it does two things:
+ *   - it quantizes w exactly as qr_quantize_weights does (same codes and scales, written to w_codes, w_scales);
+ *   - it compares each row with the previous publish (prev_codes [n,k], prev_scales [n]):
+ *       row_counts[r] = { #j: prev_codes[r,j] != w_codes[r,j],
+ *                         #j: value(prev_codes[r,j]) != value(w_codes[r,j])   (FP8 +0 and -0 are one value),
+ *                         bits(prev_scales[r]) != bits(w_scales[r]) }          (device int32 [n][3])
+ *       out3 = the sums of row_counts over the rows (device int64 [3], overwritten), which equals
+ *              qr_count_code_changes(prev_codes, w_codes, n*k, q, prev_scales, w_scales, n).
+ * prev_codes may be w_codes and prev_scales may be w_scales (publish in place); otherwise they must not overlap.
+ * k: a positive multiple of 16. Alignment as for qr_quantize_weights, row_counts 4-byte, out3 8-byte aligned.
+ */
+qr_status qr_requantize_weights(const void *w, qr_dtype w_type, int64_t n, int64_t k, const float *s, qr_qtype q,
+                                const void *prev_codes, const float *prev_scales, void *w_codes, float *w_scales,
+                                int32_t *row_counts, int64_t *out3, void *stream);
+
+/*
  * W4A16 weight quantization ([QaRL] 3.1: W4A16 rollouts; the integer Quant of [QaRL] 2.2 with z = 0). Group-wise
  * symmetric INT4 over groups of QR_W4_GROUP consecutive input channels of each row:
  *   w'_j = w[r,j] * s[j] rounded to fp32 (or w[r,j] when s == NULL)

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 # every symbol include/qr.h declares
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
            "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
-           "qr_w4a16_linear")
+           "qr_w4a16_linear", "qr_requantize_weights")
 W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
 
@@ -59,8 +59,10 @@ def lib():
                 L.qr_count_code_changes.argtypes = [vp, vp, i64, i32, vp, vp, i64, vp, vp]
                 L.qr_quantize_weights_w4.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
                 L.qr_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
+                L.qr_requantize_weights.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
                 for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
-                          "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear"):
+                          "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear",
+                          "qr_requantize_weights"):
                     getattr(L, f).restype = ctypes.c_int
                 L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
                 L.qr_workspace_bytes.restype = sz
@@ -158,6 +160,35 @@ def qr_quantize_weights(w, qtype, s=None, codes=None, scales=None, stream=None):
 def qr_quantize_acts(x, qtype, s=None, codes=None, scales=None, stream=None):
     """Per-token codes [m,k] and scales [m] of x [m,k] (optionally of X diag(1/s))."""
     return _quantize(lib().qr_quantize_acts, x, qtype, s, codes, scales, stream)
+
+
+def qr_requantize_weights(w, qtype, prev_codes, prev_scales, s=None, codes=None, scales=None, row_counts=None,
+                          out3=None, in_place=False, stream=None):
+    """One publish of w [n,k]: the codes and scales of qr_quantize_weights, and against the previous publish
+    (prev_codes [n,k], prev_scales [n]) the per-row triples row_counts [n,3] (int32: bytes, values, scale
+    changed) and their sums out3 [3] (int64). With in_place the new codes and scales overwrite prev_codes and
+    prev_scales. Returns (codes, scales, row_counts, out3)."""
+    _need(w.is_cuda and w.dim() == 2 and w.is_contiguous(), "w must be a contiguous 2-D CUDA tensor")
+    n, k = w.shape
+    _need(prev_codes.dtype == torch.uint8 and tuple(prev_codes.shape) == (n, k) and prev_codes.is_contiguous(),
+          "prev_codes must be contiguous uint8 [n,k]")
+    _need(prev_scales.dtype == torch.float32 and prev_scales.numel() == n, "prev_scales must be float32 [n]")
+    if in_place:
+        codes, scales = prev_codes, prev_scales
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n,), dtype=torch.float32, device=w.device)
+    if row_counts is None:
+        row_counts = torch.empty((n, 3), dtype=torch.int32, device=w.device)
+    if out3 is None:
+        out3 = torch.empty(3, dtype=torch.int64, device=w.device)
+    if s is not None:
+        _need(s.dtype == torch.float32 and s.numel() == k, "s must be float32 [k]")
+    _check(lib().qr_requantize_weights(_ptr(w), _dtype_code(w), n, k, _ptr(s), int(qtype), _ptr(prev_codes),
+                                       _ptr(prev_scales), _ptr(codes), _ptr(scales), _ptr(row_counts), _ptr(out3),
+                                       _stream(stream)))
+    return codes, scales, row_counts, out3
 
 
 def qr_quantize_weights_w4(w, s=None, codes=None, scales=None, stream=None):

@@ -187,6 +187,42 @@ qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_
     return hip_status(e, "count launch");
 }
 
+qr_status qr_requantize_weights(const void *w, qr_dtype w_type, int64_t n, int64_t k, const float *s, qr_qtype q,
+                                const void *prev_codes, const float *prev_scales, void *w_codes, float *w_scales,
+                                int32_t *row_counts, int64_t *out3, void *stream) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if ((st = check_dtype(w_type, "input dtype")) != QR_OK) return st;
+    if (n < 0) return fail(QR_ERR_ARG, "negative row count %lld", (long long)n);
+    if (n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "row count %lld too large", (long long)n);
+    if (k <= 0) return fail(QR_ERR_ARG, "k must be positive (got %lld)", (long long)k);
+    if (k % 16 != 0) return fail(QR_ERR_UNSUPPORTED, "k must be a multiple of 16 (got %lld)", (long long)k);
+    if (k > INT32_MAX) return fail(QR_ERR_UNSUPPORTED, "k %lld too large for the per-row counts", (long long)k);
+    if (out3 == nullptr) return fail(QR_ERR_ARG, "null out3");
+    if (!aligned(out3, 8)) return fail(QR_ERR_ALIGN, "out3 must be 8-byte aligned");
+    if (n > 0 && (w == nullptr || prev_codes == nullptr || prev_scales == nullptr || w_codes == nullptr ||
+                  w_scales == nullptr || row_counts == nullptr))
+        return fail(QR_ERR_ARG, "null input, code, scale or count pointer");
+    if (n > 0) {
+        if (!aligned(w, 16) || !aligned(prev_codes, 16) || !aligned(w_codes, 16) || (s != nullptr && !aligned(s, 4)))
+            return fail(QR_ERR_ALIGN, "input and codes must be 16-byte aligned, s 4-byte aligned");
+        if (!aligned(prev_scales, 4) || !aligned(w_scales, 4) || !aligned(row_counts, 4))
+            return fail(QR_ERR_ALIGN, "scales and row counts must be 4-byte aligned");
+        // the previous publish is either the output itself (in place) or disjoint from it
+        auto overlap = [](const void *a, const void *b, int64_t bytes) {
+            const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+            return x != y && x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
+        };
+        if (overlap(prev_codes, w_codes, n * k) || overlap(prev_scales, w_scales, n * 4))
+            return fail(QR_ERR_ARG, "previous and new codes (or scales) overlap without being the same buffer");
+    }
+    const hipError_t e = qr::launch_requantize(w, w_type == QR_BF16, n, k, s, (int)q,
+                                               static_cast<const uint8_t *>(prev_codes), prev_scales,
+                                               static_cast<uint8_t *>(w_codes), w_scales, row_counts, out3,
+                                               static_cast<hipStream_t>(stream));
+    return hip_status(e, "requantize launch");
+}
+
 qr_status qr_quantize_weights_w4(const void *w, qr_dtype w_type, int64_t n, int64_t k, const float *s,
                                  void *w_codes, float *w_scales, void *stream) {
     qr_status st;

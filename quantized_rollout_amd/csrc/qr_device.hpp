@@ -153,6 +153,28 @@ __device__ __forceinline__ float acc_to_f32(int a) { return (float)a; }
 __device__ __forceinline__ float acc_to_f32(float a) { return a; }
 
 // ---------------------------------------------------------------------------------------------------------
+// Changed-code counting, four code bytes at a time
+// ---------------------------------------------------------------------------------------------------------
+// Bytes of a 32-bit word that are nonzero, as a mask with 0x80 in each such byte.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+    return (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+}
+
+__device__ __forceinline__ void count_word(uint32_t a, uint32_t b, bool fp8, unsigned long long &nb,
+                                           unsigned long long &nv) {
+    const uint32_t diff = nonzero_bytes(a ^ b);
+    const int d = __popc(diff);
+    nb += d;
+    if (fp8) {
+        // +0 (0x00) and -0 (0x80) are one value: a byte pair whose magnitudes are both zero
+        const uint32_t both_zero = ~nonzero_bytes((a | b) & 0x7F7F7F7Fu) & 0x80808080u;
+        nv += d - __popc(diff & both_zero);
+    } else {
+        nv += d;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------------
 // Buffer loads straight into LDS (the compiler does not track them: kernels count them with vmcnt themselves)
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kBufferFlags = 0x00020000;          // raw buffer descriptor word 3 (32-bit untyped data)

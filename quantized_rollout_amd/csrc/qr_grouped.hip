@@ -232,25 +232,6 @@ __global__ void zero3_kernel(unsigned long long *out3) {
     if (threadIdx.x < 3) out3[threadIdx.x] = 0ull;
 }
 
-// Bytes of a 32-bit word that are nonzero, as a mask with 0x80 in each such byte.
-__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
-    return (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
-}
-
-__device__ __forceinline__ void count_word(uint32_t a, uint32_t b, bool fp8, unsigned long long &nb,
-                                           unsigned long long &nv) {
-    const uint32_t diff = nonzero_bytes(a ^ b);
-    const int d = __popc(diff);
-    nb += d;
-    if (fp8) {
-        // +0 (0x00) and -0 (0x80) are one value: a byte pair whose magnitudes are both zero
-        const uint32_t both_zero = ~nonzero_bytes((a | b) & 0x7F7F7F7Fu) & 0x80808080u;
-        nv += d - __popc(diff & both_zero);
-    } else {
-        nv += d;
-    }
-}
-
 // One streaming pass over both code sets: each lane keeps kCountUnroll pairs of 16-byte loads in flight (grid-
 // stride over 16-byte words), compares bytes four at a time, and the counts are summed over the wave and added
 // with one 64-bit atomic per wave and count.

@@ -13,6 +13,11 @@ enum SMode { kSNone = 0, kSMul = 1, kSMulRecip = 2 };
 // Row quantizer: one absmax scale per row of in[rows, k] (k % 16 == 0).
 hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode,
                                 int qtype, uint8_t *codes, float *scales, hipStream_t stream);
+// the weight quantizer with the changed-code triple of every row against the previous publish (which may be
+// the output itself), then out3 = the triples' sums
+hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int qtype,
+                             const uint8_t *prev_codes, const float *prev_scales, uint8_t *codes, float *scales,
+                             int32_t *row_counts, int64_t *out3, hipStream_t stream);
 
 // Plan of a W8A8 linear (which kernel, its split of K and the workspace it needs).
 // Tiled MFMA GEMM for large m (qr_gemm.hip).

@@ -16,10 +16,13 @@
 #include "qr_device.hpp"
 #include "qr_internal.hpp"
 
+#include <type_traits>
+
 namespace qr {
 namespace {
 
 constexpr int kCMax = 8;  // 16-byte chunks held in registers per lane
+constexpr int kCDiff = 4;  // the same with the previous publish's codes held too (keeps occupancy at 8 waves/SIMD)
 
 template <bool BF16, int SMODE>
 __device__ __forceinline__ void expand_chunk(const uint4 &c, const float *__restrict__ s, int64_t k0, float *w) {
@@ -49,14 +52,20 @@ __device__ __forceinline__ void expand_chunk(const uint4 &c, const float *__rest
     }
 }
 
-// THREADS lanes per row, RPB rows per workgroup (RPB > 1 only with one-wavefront rows)
-template <bool BF16, int QT, int SMODE, int THREADS, int RPB>
+// THREADS lanes per row, RPB rows per workgroup (RPB > 1 only with one-wavefront rows). With DIFF the kernel also
+// compares every new code and the row's scale with the previous publish (prev_codes / prev_scales, which may be
+// codes / scales themselves: each lane reads the previous bytes it then overwrites) and writes the row's
+// changed-code triple {bytes, values, scale} to row_counts[row].
+template <bool BF16, int QT, int SMODE, int THREADS, int RPB, bool DIFF>
 __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void *__restrict__ in, int64_t rows,
                                                                        int64_t k, const float *__restrict__ s,
-                                                                       uint8_t *__restrict__ codes,
-                                                                       float *__restrict__ scales) {
+                                                                       uint8_t *codes, float *scales,
+                                                                       const uint8_t *prev_codes,
+                                                                       const float *prev_scales,
+                                                                       int32_t *row_counts) {
     static_assert(RPB == 1 || THREADS == 64, "several rows per workgroup only with one-wavefront rows");
     constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    constexpr int kC = DIFF ? kCDiff : kCMax;  // chunks per lane held in registers
     constexpr float qmax = QMax<QT>::value;
     const int64_t row = (int64_t)blockIdx.x * RPB + (RPB > 1 ? (int)(threadIdx.x >> 6) : 0);
     if (row >= rows) return;  // whole wavefronts only (RPB > 1 implies one wavefront per row)
@@ -65,10 +74,23 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
     const uint4 *__restrict__ src =
         reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(in) + row * k * (BF16 ? 2 : 4));
 
-    uint4 keep[kCMax];
+    // the previous codes of the chunks held in registers, requested first (their latency overlaps the first
+    // pass) and all loaded before any store (the stores may overwrite them)
+    typedef typename std::conditional<BF16, uint2, uint32_t>::type cword_t;
+    const uint8_t *prev = DIFF ? prev_codes + row * k : nullptr;
+    cword_t old_keep[DIFF ? kC : 1];
+    if constexpr (DIFF) {
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            const int64_t c = t + (int64_t)i * THREADS;
+            if (c < nch) old_keep[i] = *reinterpret_cast<const cword_t *>(prev + c * E);
+        }
+    }
+
+    uint4 keep[kC];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kCMax; ++i) {
+    for (int i = 0; i < kC; ++i) {
         const int64_t c = t + (int64_t)i * THREADS;
         if (c < nch) {
             keep[i] = src[c];
@@ -78,7 +100,7 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
             for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(w[j]));
         }
     }
-    for (int64_t c = t + (int64_t)kCMax * THREADS; c < nch; c += THREADS) {
+    for (int64_t c = t + (int64_t)kC * THREADS; c < nch; c += THREADS) {
         float w[E];
         expand_chunk<BF16, SMODE>(src[c], s, c * E, w);
 #pragma unroll
@@ -99,10 +121,21 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
     if (!(S > 0.0f)) S = 1.0f;  // all-zero row, or a scale that underflows to zero
     const float r = 1.0f / S;
     const bool fast = S >= 0x1p-90f;
-    if (t == 0) scales[row] = S;
+    uint32_t scale_changed = 0;
+    if (t == 0) {
+        if constexpr (DIFF) {
+            scale_changed = __float_as_uint(prev_scales[row]) != __float_as_uint(S) ? 1u : 0u;
+            // in place the store below overwrites the previous scale. The read above is a scalar load (the
+            // address is uniform), which is not ordered with a vector store: the comparison has to be complete
+            // (so the load has returned) before the store is issued
+            asm volatile("" ::"v"(scale_changed) : "memory");
+        }
+        scales[row] = S;
+    }
 
-    uint8_t *__restrict__ dst = codes + row * k;
-    auto emit = [&](const uint4 &chunk, int64_t c) {
+    uint8_t *dst = codes + row * k;
+    unsigned long long nb = 0, nv = 0;
+    auto emit = [&](const uint4 &chunk, int64_t c, const cword_t &old) {
         float w[E];
         expand_chunk<BF16, SMODE>(chunk, s, c * E, w);
         uint32_t q[E];
@@ -116,68 +149,147 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
             uint2 o;
             o.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
             o.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+            if constexpr (DIFF) {
+                count_word(old.x, o.x, QT == kFp8, nb, nv);
+                count_word(old.y, o.y, QT == kFp8, nb, nv);
+            }
             *reinterpret_cast<uint2 *>(dst + c * 8) = o;
         } else {
-            *reinterpret_cast<uint32_t *>(dst + c * 4) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            const uint32_t o = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            if constexpr (DIFF) count_word(old, o, QT == kFp8, nb, nv);
+            *reinterpret_cast<uint32_t *>(dst + c * 4) = o;
         }
     };
 #pragma unroll
-    for (int i = 0; i < kCMax; ++i) {
+    for (int i = 0; i < kC; ++i) {
         const int64_t c = t + (int64_t)i * THREADS;
-        if (c < nch) emit(keep[i], c);
+        if (c < nch) emit(keep[i], c, DIFF ? old_keep[i] : cword_t{});
     }
-    for (int64_t c = t + (int64_t)kCMax * THREADS; c < nch; c += THREADS) emit(src[c], c);
+    for (int64_t c = t + (int64_t)kC * THREADS; c < nch; c += THREADS)
+        emit(src[c], c, DIFF ? *reinterpret_cast<const cword_t *>(prev + c * E) : cword_t{});
+
+    if constexpr (DIFF) {
+        // the row's triple: sums over its lanes (and wavefronts), written by lane 0
+        nb = wave_sum_u64(nb);
+        nv = wave_sum_u64(nv);
+        if constexpr (THREADS > 64) {
+            __shared__ unsigned long long cnt[2][THREADS / 64];
+            if ((t & 63) == 0) {
+                cnt[0][t >> 6] = nb;
+                cnt[1][t >> 6] = nv;
+            }
+            __syncthreads();
+            if (t == 0) {
+                for (int i = 1; i < THREADS / 64; ++i) {
+                    nb += cnt[0][i];
+                    nv += cnt[1][i];
+                }
+            }
+        }
+        if (t == 0) {
+            row_counts[3 * row + 0] = (int32_t)nb;
+            row_counts[3 * row + 1] = (int32_t)nv;
+            row_counts[3 * row + 2] = (int32_t)scale_changed;
+        }
+    }
 }
 
-template <bool BF16, int QT, int SMODE>
+// out3 = the column sums of row_counts [rows][3]: one workgroup, 64-bit sums in a fixed order per lane, then
+// over the lanes and wavefronts
+__global__ __launch_bounds__(1024) void sum_row_counts_kernel(const int32_t *__restrict__ row_counts, int64_t rows,
+                                                              int64_t *__restrict__ out3) {
+    unsigned long long a[3] = {0, 0, 0};
+    for (int64_t r = threadIdx.x; r < rows; r += blockDim.x)
+#pragma unroll
+        for (int e = 0; e < 3; ++e) a[e] += (unsigned long long)(uint32_t)row_counts[3 * r + e];
+    __shared__ unsigned long long part[3][16];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+        a[e] = wave_sum_u64(a[e]);
+        if ((threadIdx.x & 63) == 0) part[e][threadIdx.x >> 6] = a[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        unsigned long long sum = 0;
+        for (unsigned w = 0; w < blockDim.x / 64; ++w) sum += part[threadIdx.x][w];
+        out3[threadIdx.x] = (int64_t)sum;
+    }
+}
+
+struct DiffArgs {
+    const uint8_t *prev_codes;
+    const float *prev_scales;
+    int32_t *row_counts;
+};
+
+template <bool BF16, int QT, int SMODE, bool DIFF>
 hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uint8_t *codes, float *scales,
-                    hipStream_t stream) {
+                    const DiffArgs &d, hipStream_t stream) {
     constexpr int E = BF16 ? 8 : 4;
+    constexpr int kC = DIFF ? kCDiff : kCMax;
     const int64_t nch = k / E;
     const dim3 grid((unsigned)rows);
-    if (nch <= 64 * kCMax) {
+#define QR_QROWS(T, R, G)                                                                                      \
+    hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, T, R, DIFF>), G, dim3(T * R), 0, stream, in, rows, \
+                       k, s, codes, scales, d.prev_codes, d.prev_scales, d.row_counts)
+    if (nch <= 64 * kC) {
         constexpr int kRows = 4;
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 64, kRows>), dim3((unsigned)((rows + kRows - 1) / kRows)),
-                           dim3(64 * kRows), 0, stream, in, rows, k, s, codes, scales);
-    } else if (nch <= 128 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 128, 1>), grid, dim3(128), 0, stream, in, rows, k, s,
-                           codes, scales);
-    } else if (nch <= 256 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 256, 1>), grid, dim3(256), 0, stream, in, rows, k, s,
-                           codes, scales);
-    } else if (nch <= 512 * kCMax) {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 512, 1>), grid, dim3(512), 0, stream, in, rows, k, s,
-                           codes, scales);
+        QR_QROWS(64, kRows, dim3((unsigned)((rows + kRows - 1) / kRows)));
+    } else if (nch <= 128 * kC) {
+        QR_QROWS(128, 1, grid);
+    } else if (nch <= 256 * kC) {
+        QR_QROWS(256, 1, grid);
+    } else if (nch <= 512 * kC) {
+        QR_QROWS(512, 1, grid);
     } else {
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, 1024, 1>), grid, dim3(1024), 0, stream, in, rows, k,
-                           s, codes, scales);
+        QR_QROWS(1024, 1, grid);
     }
+#undef QR_QROWS
     return hipGetLastError();
 }
 
-template <bool BF16, int QT>
+template <bool BF16, int QT, bool DIFF>
 hipError_t launch_s(const void *in, int64_t rows, int64_t k, const float *s, int s_mode, uint8_t *codes,
-                    float *scales, hipStream_t stream) {
+                    float *scales, const DiffArgs &d, hipStream_t stream) {
     switch (s_mode) {
         case kSMul:
-            return launch_t<BF16, QT, kSMul>(in, rows, k, s, codes, scales, stream);
+            return launch_t<BF16, QT, kSMul, DIFF>(in, rows, k, s, codes, scales, d, stream);
         case kSMulRecip:
-            return launch_t<BF16, QT, kSMulRecip>(in, rows, k, s, codes, scales, stream);
+            return launch_t<BF16, QT, kSMulRecip, DIFF>(in, rows, k, s, codes, scales, d, stream);
         default:
-            return launch_t<BF16, QT, kSNone>(in, rows, k, s, codes, scales, stream);
+            return launch_t<BF16, QT, kSNone, DIFF>(in, rows, k, s, codes, scales, d, stream);
     }
+}
+
+template <bool DIFF>
+hipError_t launch_q(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode, int qtype,
+                    uint8_t *codes, float *scales, const DiffArgs &d, hipStream_t stream) {
+    if (in_bf16) {
+        return qtype == kInt8 ? launch_s<true, kInt8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream)
+                              : launch_s<true, kFp8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream);
+    }
+    return qtype == kInt8 ? launch_s<false, kInt8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream)
+                          : launch_s<false, kFp8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode,
                                 int qtype, uint8_t *codes, float *scales, hipStream_t stream) {
-    if (in_bf16) {
-        return qtype == kInt8 ? launch_s<true, kInt8>(in, rows, k, s, s_mode, codes, scales, stream)
-                              : launch_s<true, kFp8>(in, rows, k, s, s_mode, codes, scales, stream);
+    return launch_q<false>(in, in_bf16, rows, k, s, s_mode, qtype, codes, scales, DiffArgs{nullptr, nullptr, nullptr},
+                           stream);
+}
+
+hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int qtype,
+                             const uint8_t *prev_codes, const float *prev_scales, uint8_t *codes, float *scales,
+                             int32_t *row_counts, int64_t *out3, hipStream_t stream) {
+    if (rows > 0) {  // no rows: out3 is still written (zeros)
+        const hipError_t e = launch_q<true>(in, in_bf16, rows, k, s, s == nullptr ? kSNone : kSMul, qtype, codes,
+                                            scales, DiffArgs{prev_codes, prev_scales, row_counts}, stream);
+        if (e != hipSuccess) return e;
     }
-    return qtype == kInt8 ? launch_s<false, kInt8>(in, rows, k, s, s_mode, codes, scales, stream)
-                          : launch_s<false, kFp8>(in, rows, k, s, s_mode, codes, scales, stream);
+    hipLaunchKernelGGL(sum_row_counts_kernel, dim3(1), dim3(1024), 0, stream, row_counts, rows, out3);
+    return hipGetLastError();
 }
 
 }  // namespace qr

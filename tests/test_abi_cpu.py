@@ -133,6 +133,27 @@ def test_count_validation():
     assert L.qr_count_code_changes(P, P, 64, 3, NULL, NULL, 0, P, S0) == B.QR_ERR_ARG
 
 
+def test_requantize_validation():
+    L = B.lib()
+
+    def call(w=P, wt=1, n=8, k=128, s=NULL, q=0, pc=P, ps=P, c=P, sc=P, rc=P, o3=P):
+        return L.qr_requantize_weights(w, wt, n, k, s, q, pc, ps, c, sc, rc, o3, S0)
+
+    assert call(k=136) == B.QR_ERR_UNSUPPORTED
+    assert call(k=0) == B.QR_ERR_ARG
+    assert call(n=-1) == B.QR_ERR_ARG
+    assert call(q=5) == B.QR_ERR_ARG
+    assert call(o3=NULL) == B.QR_ERR_ARG
+    assert call(rc=NULL) == B.QR_ERR_ARG
+    assert call(pc=NULL) == B.QR_ERR_ARG
+    assert call(w=MIS) == B.QR_ERR_ALIGN
+    assert call(pc=MIS) == B.QR_ERR_ALIGN
+    # the previous publish is the output itself, or disjoint from it; a partial overlap is refused
+    base = 1 << 20
+    assert call(pc=base, c=base + 512, ps=P, sc=P) == B.QR_ERR_ARG and "overlap" in _err()
+    assert call(pc=base, c=base + 8 * 128, n=8, k=128, ps=1 << 22, sc=(1 << 22) + 16) == B.QR_ERR_ARG
+
+
 def test_workspace_sizes(monkeypatch):
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
         # GEMV plans with enough blocks, and GEMM plans with a tile for at least half the CUs, reduce inside
