@@ -336,6 +336,34 @@ def measure_publish_fused(stack, reps):
             "changed": [int(v) for v in sep_count.tolist()], "matches_separate": same}
 
 
+def measure_decode_fused(stack, reps):
+    """The m = 1 decode of the 1.5B stack (112 linears) on bfloat16 activations with the activation quantization
+    inside the linear (qr_w8a8_linear_bf16) against the step's two launches per linear (a2 then a3); both are
+    replayed as HIP graphs and their outputs compared bit for bit."""
+    import torch
+
+    qr = stack.qr
+
+    def fused():
+        for l in range(LAYERS):
+            for name, n, k in LINEARS:
+                qr.qr_w8a8_linear_bf16(qr.QR_INT8, stack.x[name][l, :1], stack.wc[name][l * n:(l + 1) * n],
+                                       stack.ws[name][l * n:(l + 1) * n], y=stack.y[name][:1], workspace=stack.wsp)
+
+    g2, gf = TimedGraph(lambda: stack.decode(1), 2 * LAYERS * len(LINEARS)), TimedGraph(fused, LAYERS * len(LINEARS))
+    ms2, msf = g2.time_ms(reps), gf.time_ms(reps)
+    outs = []
+    for g in (g2, gf):
+        g.replay()
+        torch.cuda.synchronize()
+        outs.append([stack.y[name][:1].clone() for name, _, _ in LINEARS])
+    same = all(torch.equal(a, b) for a, b in zip(*outs))
+    del g2, gf
+    return {"us_two_launches": round(ms2 * 1e3, 1), "us_fused": round(msf * 1e3, 1),
+            "speedup": round(ms2 / msf, 3), "us_per_layer_fused": round(msf * 1e3 / LAYERS, 2),
+            "y_matches_two_launches": same}
+
+
 def bytes_w4a16(m, n, k, out_bytes=2):
     """HBM bytes a W4A16 linear must move: packed codes, group scales, bf16 activations, the output."""
     return n * k // 2 + 4 * n * (k // W4_GROUP) + 2 * m * k + out_bytes * m * n
@@ -744,6 +772,8 @@ def main():
         extra["w4a16_7b_linears"] = measure_w4a16_7b(dev, max(5, args.reps // 5))
         log("fused requantize + diff publish")
         extra["publish_fused_requant_diff"] = measure_publish_fused(stack, max(5, args.reps // 5))
+        log("decode at m = 1 with the activation quantization fused")
+        extra["decode_m1_fused_act_quant"] = measure_decode_fused(stack, max(5, args.reps // 5))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -82,9 +82,10 @@ qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k,
  *   y[i,c]   = acc[i,c] * x_scales[i] * w_scales[c], stored as y_type (bfloat16 rounded to nearest even).
  * acc_out: optional [m,n] int32 (INT8) or fp32 (FP8) copy of the accumulators, or NULL.
  * workspace: device memory of at least qr_workspace_bytes(q, m, n, k, 1) bytes, 256-byte aligned, or NULL when
- * that is 0. It is nonzero only for large batches with too few output tiles to occupy the GPU: there K is
- * split and the workspace holds the int32 (INT8) or fp32 (FP8) partial sums, splits x m x n x 4 bytes, which a
- * second kernel adds in a fixed order. Its contents need no initialisation and are not preserved.
+ * that is 0. It is nonzero only where K is split across workgroups: large batches with too few output tiles
+ * to occupy the GPU, and decode batches of 33..64 tokens on few output tiles with a deep K. The workspace
+ * then holds the int32 (INT8) or fp32 (FP8) partial sums, splits x m x n x 4 bytes, which a second kernel
+ * adds in a fixed order. Its contents need no initialisation and are not preserved.
  * INT8 results are bitwise independent of m (row i depends only on row i of the inputs) and deterministic;
  * FP8 results are deterministic for a given (m, n, k).
  * Limits: k <= 131072 (INT8 accumulators stay below 2^31).
@@ -92,6 +93,23 @@ qr_status qr_quantize_acts(const void *x, qr_dtype x_type, int64_t m, int64_t k,
 qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes, const float *x_scales,
                          const void *w_codes, const float *w_scales, void *y, qr_dtype y_type, void *acc_out,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The W8A8 linear on bfloat16 activations (next row: the activation quantization fused with the linear):
+ * the same result, bit for bit, as qr_quantize_acts(x, QR_BF16, m, k, s, q, ...) followed by qr_w8a8_linear on
+ * its codes and scales (including acc_out). For single-token decode (m = 1; with FP8 for k <= 8192) the
+ * activation quantization runs inside the linear's kernel (each workgroup quantizes the token row into its
+ * LDS), saving one launch and the codes' round trip through memory; otherwise the two steps run one after the
+ * other, the activation codes in the workspace. x: device bfloat16 [m,k], 16-byte aligned; s: device fp32 [k] or NULL (X diag(1/s)).
+ * workspace: at least qr_w8a8_linear_bf16_workspace_bytes(q, m, n, k) bytes, 256-byte aligned, or NULL when
+ * that is 0. Other arguments and limits as for qr_w8a8_linear.
+ */
+qr_status qr_w8a8_linear_bf16(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x, const float *s,
+                              const void *w_codes, const float *w_scales, void *y, qr_dtype y_type, void *acc_out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device bytes of workspace qr_w8a8_linear_bf16 needs (0 when the activation quantization runs inside it). */
+size_t qr_w8a8_linear_bf16_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k);
 
 /*
  * Grouped (MoE) W8A8 linear over per-expert token lists (the expert FFNs of the Qwen3-30B-A3B model in the

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 # every symbol include/qr.h declares
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
            "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
-           "qr_w4a16_linear", "qr_requantize_weights")
+           "qr_w4a16_linear", "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_w8a8_linear_bf16_workspace_bytes")
 W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
 
@@ -60,9 +60,12 @@ def lib():
                 L.qr_quantize_weights_w4.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
                 L.qr_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
                 L.qr_requantize_weights.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+                L.qr_w8a8_linear_bf16.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+                L.qr_w8a8_linear_bf16_workspace_bytes.argtypes = [i32, i64, i64, i64]
+                L.qr_w8a8_linear_bf16_workspace_bytes.restype = sz
                 for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
                           "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear",
-                          "qr_requantize_weights"):
+                          "qr_requantize_weights", "qr_w8a8_linear_bf16"):
                     getattr(L, f).restype = ctypes.c_int
                 L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
                 L.qr_workspace_bytes.restype = sz
@@ -254,6 +257,41 @@ def qr_w8a8_linear(qtype, x_codes, x_scales, w_codes, w_scales, y=None, y_dtype=
     ws = (workspace if workspace is not None else default_workspace(dev)).get(nbytes)
     _check(lib().qr_w8a8_linear(int(qtype), m, n, k, _ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales),
                                 _ptr(y), _dtype_code(y), _ptr(acc_out), _ptr(ws), nbytes, _stream(stream)))
+    return (y, acc_out) if want_acc else y
+
+
+def qr_w8a8_linear_bf16_workspace_bytes(qtype, m, n, k):
+    return int(lib().qr_w8a8_linear_bf16_workspace_bytes(int(qtype), int(m), int(n), int(k)))
+
+
+def qr_w8a8_linear_bf16(qtype, x, w_codes, w_scales, s=None, y=None, y_dtype=torch.bfloat16, acc_out=None,
+                        workspace=None, stream=None):
+    """The W8A8 linear on bfloat16 activations x [m,k] (quantized per token, optionally as X diag(1/s)): the
+    same y (and accumulators) as qr_quantize_acts then qr_w8a8_linear, with the activation quantization inside
+    the linear's kernel at decode batches. Returns y or (y, acc)."""
+    m, k = x.shape
+    n, k2 = w_codes.shape
+    _need(k == k2, "k mismatch")
+    dev = x.device
+    for t in (x, w_codes, w_scales):
+        _need(t.is_cuda and t.is_contiguous(), "operands must be contiguous CUDA tensors")
+    _need(x.dtype == torch.bfloat16, "x must be bfloat16")
+    _need(w_codes.dtype == torch.uint8 and w_scales.dtype == torch.float32 and w_scales.shape == (n,),
+          "weights must be uint8 codes [n,k] with float32 scales [n]")
+    if s is not None:
+        _need(s.dtype == torch.float32 and s.numel() == k and s.is_cuda, "s must be float32 [k]")
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype, device=dev)
+    _need(y.shape == (m, n) and y.is_contiguous(), "bad y")
+    want_acc = acc_out is not None and acc_out is not False
+    if acc_out is True:
+        acc_out = torch.empty((m, n), dtype=torch.int32 if qtype == QR_INT8 else torch.float32, device=dev)
+    elif acc_out is False:
+        acc_out = None
+    nbytes = qr_w8a8_linear_bf16_workspace_bytes(qtype, m, n, k)
+    ws = (workspace if workspace is not None else default_workspace(dev)).get(nbytes)
+    _check(lib().qr_w8a8_linear_bf16(int(qtype), m, n, k, _ptr(x), _ptr(s), _ptr(w_codes), _ptr(w_scales), _ptr(y),
+                                     _dtype_code(y), _ptr(acc_out), _ptr(ws), nbytes, _stream(stream)))
     return (y, acc_out) if want_acc else y
 
 

@@ -133,6 +133,48 @@ qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void
     return hip_status(e, "linear launch");
 }
 
+size_t qr_w8a8_linear_bf16_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k) {
+    if ((q != QR_INT8 && q != QR_FP8_E4M3) || m <= 0 || n <= 0 || k <= 0) return 0;
+    return qr::linear_bf16_workspace_bytes(qr::plan_linear_bf16((int)q, m, n, k), (int)q, m, k);
+}
+
+qr_status qr_w8a8_linear_bf16(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x, const float *s,
+                              const void *w_codes, const float *w_scales, void *y, qr_dtype y_type, void *acc_out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if ((st = check_dtype(y_type, "output dtype")) != QR_OK) return st;
+    if (m < 0 || n < 0) return fail(QR_ERR_ARG, "negative size m=%lld n=%lld", (long long)m, (long long)n);
+    if ((st = check_k(k)) != QR_OK) return st;
+    if (m > kMaxRows || n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "m or n too large");
+    if (m == 0 || n == 0) return ok();
+    if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
+        return fail(QR_ERR_ARG, "null operand pointer");
+    if (!aligned(x, 16) || !aligned(w_codes, 16)) return fail(QR_ERR_ALIGN, "x and codes must be 16-byte aligned");
+    if (!aligned(w_scales, 4) || (s != nullptr && !aligned(s, 4)))
+        return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+    if (!aligned(y, 16) || (acc_out != nullptr && !aligned(acc_out, 16)))
+        return fail(QR_ERR_ALIGN, "y and acc_out must be 16-byte aligned");
+    const qr::LinearPlan p = qr::plan_linear_bf16((int)q, m, n, k);
+    const size_t need = qr::linear_bf16_workspace_bytes(p, (int)q, m, k);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(QR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace == nullptr ? (size_t)0 : workspace_bytes);
+        if (!aligned(workspace, 256)) return fail(QR_ERR_ALIGN, "workspace must be 256-byte aligned");
+    }
+    if (getenv("QR_TRACE") != nullptr)
+        fprintf(stderr, "[qr] linear_bf16 q=%d m=%lld n=%lld k=%lld fused=%d kind=%d mt=%d waves=%d unroll=%d tiles=%d "
+                "ws=%zu\n",
+                (int)q, (long long)m, (long long)n, (long long)k, qr::linear_bf16_fused(p, (int)q, m, k) ? 1 : 0, p.kind,
+                p.m_tiles, p.waves, p.unroll, p.tiles, need);
+    const hipError_t e = qr::launch_linear_bf16(p, (int)q, m, n, k, static_cast<const uint16_t *>(x), s,
+                                                static_cast<const uint8_t *>(w_codes), w_scales, y,
+                                                y_type == QR_BF16, acc_out, workspace,
+                                                static_cast<hipStream_t>(stream));
+    return hip_status(e, "linear launch");
+}
+
 qr_status qr_w8a8_grouped_linear(qr_qtype q, int64_t num_experts, int64_t n, int64_t k,
                                  const int32_t *expert_offsets, const int32_t *row_ids, int64_t total_rows,
                                  int64_t x_rows, const void *x_codes, const float *x_scales, const void *w_codes,

@@ -49,11 +49,20 @@ struct LinearPlan {
     size_t ws_bytes;   // workspace bytes
 };
 
-LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k);
+LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll = 8);
 
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          void *workspace, hipStream_t stream);
+// the linear on bfloat16 activations: the activation quantization inside the GEMV for one-token-tile plans with
+// m <= QR_FUSE_MAX_M (default 1, at most 4) and, for FP8, k <= 8192; else the activation quantizer into the
+// workspace, then the linear
+LinearPlan plan_linear_bf16(int qtype, int64_t m, int64_t n, int64_t k);
+bool linear_bf16_fused(const LinearPlan &p, int qtype, int64_t m, int64_t k);
+size_t linear_bf16_workspace_bytes(const LinearPlan &p, int qtype, int64_t m, int64_t k);
+hipError_t launch_linear_bf16(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint16_t *xb,
+                              const float *s, const uint8_t *wq, const float *ws, void *y, bool y_bf16,
+                              void *acc_out, void *workspace, hipStream_t stream);
 
 size_t grouped_workspace_bytes(int qtype, int64_t total_rows, int64_t n, int64_t k, int64_t num_experts);
 

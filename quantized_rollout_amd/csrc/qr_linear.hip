@@ -19,6 +19,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace qr {
 namespace {
 
@@ -58,14 +60,25 @@ __device__ __forceinline__ v8i as_v8i(const uint4 &a, const uint4 &b) {
 // element i % 4. Per-tile partials of all waves meet in LDS; every wave then sums a share of the 16x16
 // fragments over the waves in wave order (deterministic) and applies the epilogue to them.
 // ---------------------------------------------------------------------------------------------------------
-template <int QT, int MT, int U, int TB, int WMAX>
+// Activation input of the GEMV: codes and scales from the activation quantizer (kXCodes), or bfloat16 rows
+// quantized inside the kernel (kXBf16, with X diag(1/s) for kXBf16S): in a prologue every block computes the
+// per-token scales of its token rows and their codes, all lanes sharing the work, into LDS (after the
+// reduction area), with the same IEEE steps as the activation quantizer (so the codes are the same bytes);
+// the slice loop then reads its activation codes from LDS. For m <= kFuseRows only.
+constexpr int kXCodes = 0, kXBf16 = 1, kXBf16S = 2;
+constexpr int kFuseRows = 4;
+
+template <int QT, int MT, int U, int TB, int WMAX, int XM = kXCodes>
 __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq,
                                                          const float *__restrict__ xs, const uint8_t *__restrict__ wq,
                                                          const float *__restrict__ ws, void *__restrict__ y,
                                                          int y_bf16, void *__restrict__ acc_out, int splits,
-                                                         void *__restrict__ partial) {
+                                                         void *__restrict__ partial,
+                                                         const uint16_t *__restrict__ xb = nullptr,
+                                                         const float *__restrict__ xsv = nullptr) {
     typedef typename Acc<QT>::type acc_t;
     static_assert(QT == kInt8 || U % 2 == 0, "FP8 pairs load instructions");
+    static_assert(XM == kXCodes || MT == 1, "in-kernel activation quantization for one token tile only");
     extern __shared__ int32_t red[];  // [waves][TB][MT][4][64]
     const int waves = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -106,6 +119,90 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[r][mt] = acc_t{0, 0, 0, 0};
 
+    // in-kernel activation quantization: the scale of each token row (absmax of X diag(1/s) / qmax, IEEE
+    // division, 1 when zero), then the codes of the token rows into LDS
+    __shared__ float xq_scale[XM != kXCodes ? kFuseRows : 1];
+    const int xrows = (int)(m - m0 < 16 ? m - m0 : 16);
+    uint8_t *xlds = reinterpret_cast<uint8_t *>(red) + (size_t)waves * TB * MT * 1024;
+    if constexpr (XM != kXCodes) {
+        constexpr float qmax = QMax<QT>::value;
+        auto x_elems = [&](int r, int64_t c, float *w) {  // 8 bfloat16 values of row r, chunk c, with 1/s applied
+            const uint4 v = *reinterpret_cast<const uint4 *>(xb + (m0 + r) * k + 8 * c);
+            const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[2 * i] = bf16_lo(p[i]);
+                w[2 * i + 1] = bf16_hi(p[i]);
+            }
+            if constexpr (XM == kXBf16S) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float rs = 1.0f / xsv[8 * c + i];
+                    w[i] = w[i] * rs;
+                }
+            }
+        };
+        __shared__ float xred[16][kFuseRows];
+        float a[kFuseRows];
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) a[r] = 0.0f;
+        for (int64_t c = threadIdx.x; c < k / 8; c += blockDim.x) {
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) {
+                if (r < xrows) {
+                    float w[8];
+                    x_elems(r, c, w);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) a[r] = fmaxf(a[r], fabsf(w[i]));
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) {
+            a[r] = wave_max(a[r]);
+            if (lane == 0) xred[wave][r] = a[r];
+        }
+        __syncthreads();
+        if (threadIdx.x < kFuseRows) {
+            float amax = 0.0f;
+            for (int w = 0; w < waves; ++w) amax = fmaxf(amax, xred[w][threadIdx.x]);
+            float S = amax / qmax;  // IEEE division
+            if (!(S > 0.0f)) S = 1.0f;
+            xq_scale[threadIdx.x] = S;
+        }
+        __syncthreads();
+        // the codes: 8 per thread and step, rows one after the other
+        for (int r = 0; r < xrows; ++r) {
+            const float S = xq_scale[r];
+            const float R = 1.0f / S;
+            const bool fast = S >= 0x1p-90f;
+            for (int64_t c = threadIdx.x; c < k / 8; c += blockDim.x) {
+                float w[8];
+                x_elems(r, c, w);
+                uint32_t q[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float v = fast ? div_by_scale(w[i], S, R) : w[i] / S;
+                    v = fminf(fmaxf(v, -qmax), qmax);
+                    q[i] = encode_code<QT>(v);
+                }
+                *reinterpret_cast<uint2 *>(xlds + r * k + 8 * c) =
+                    make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                               q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+            }
+        }
+        __syncthreads();
+    }
+    // 16 activation codes of this lane's token row at element j0 (global codes, or the block's LDS codes)
+    auto x_codes16 = [&](const uint8_t *codes_at, int64_t j0) -> uint4 {
+        if constexpr (XM == kXCodes) {
+            return load16(codes_at);
+        } else {
+            const int row = xr < xrows ? xr : xrows - 1;
+            return *reinterpret_cast<const uint4 *>(xlds + row * k + j0);
+        }
+    };
+
     // Per slice, one burst: the slice's activations and all TB weight tiles are requested together, then the
     // activations are moved to the MFMA layout (in place) and the tiles' MFMAs run. Few registers per wave
     // keep many waves resident, and the resident waves hide each other's latency. Loads in full slices are
@@ -145,7 +242,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
 #pragma unroll
         for (int t = 0; t < U; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) xv[mt][t] = load16(xrow[mt] + kb + 64 * t);
+            for (int mt = 0; mt < MT; ++mt) xv[mt][t] = x_codes16(xrow[mt] + kb + 64 * t, kb + 64 * t + 16 * xp);
 #pragma unroll
         for (int r = 0; r < TB; ++r)
 #pragma unroll
@@ -161,7 +258,8 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
         for (int t = 0; t < U; ++t) {
             const bool in = kb + 64 * t + 16 * xp < k;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) xv[mt][t] = in ? load16(xrow[mt] + kb + 64 * t) : make_uint4(0, 0, 0, 0);
+            for (int mt = 0; mt < MT; ++mt)
+                xv[mt][t] = in ? x_codes16(xrow[mt] + kb + 64 * t, kb + 64 * t + 16 * xp) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < TB; ++r)
@@ -232,7 +330,10 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t row = m0 + mt * 16 + 4 * g + i;
-                sx[i] = xs[row < m ? row : m - 1];
+                if constexpr (XM == kXCodes)
+                    sx[i] = xs[row < m ? row : m - 1];
+                else
+                    sx[i] = xq_scale[row < m ? row - m0 : xrows - 1];
             }
             if (col >= n) continue;
 #pragma unroll
@@ -289,6 +390,43 @@ void launch_gemv_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const u
     abort();
 }
 
+// dynamic LDS of the GEMV with in-kernel activation quantization: the reduction area (always reserved: the codes
+// sit after it) and the token rows' codes
+size_t gemv_fused_lds_bytes(const LinearPlan &p, int64_t m, int64_t k) {
+    return (size_t)p.waves * p.tiles * 1024 + (size_t)((m * k + 15) / 16 * 16);
+}
+
+// the GEMV with in-kernel activation quantization (bfloat16 x, optional X diag(1/s)); one token tile only
+template <int QT, int U, int TB, int WMAX>
+void launch_gemv_fused_t(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint16_t *xb, const float *s,
+                         const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                         hipStream_t stream) {
+    const dim3 grid((unsigned)((p.n_tiles + TB - 1) / TB), 1u, 1u);
+    const size_t lds = gemv_fused_lds_bytes(p, m, k);
+    if (s != nullptr)
+        hipLaunchKernelGGL((gemv_kernel<QT, 1, U, TB, WMAX, kXBf16S>), grid, dim3(p.waves * 64), lds, stream, m, n, k,
+                           nullptr, nullptr, wq, ws, y, y_bf16 ? 1 : 0, acc_out, 1, nullptr, xb, s);
+    else
+        hipLaunchKernelGGL((gemv_kernel<QT, 1, U, TB, WMAX, kXBf16>), grid, dim3(p.waves * 64), lds, stream, m, n, k,
+                           nullptr, nullptr, wq, ws, y, y_bf16 ? 1 : 0, acc_out, 1, nullptr, xb, s);
+}
+
+template <int QT>
+bool launch_gemv_fused_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint16_t *xb, const float *s,
+                         const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
+                         hipStream_t stream) {
+#define QR_GEMV_FUSED_CASE(MT_, U_, TB_, W_)                                                                    \
+    if constexpr (MT_ == 1 && U_ == 4) {                                                                        \
+        if (p.m_tiles == MT_ && p.unroll == U_ && p.tiles == TB_) {                                             \
+            launch_gemv_fused_t<QT, U_, TB_, W_>(p, m, n, k, xb, s, wq, ws, y, y_bf16, acc_out, stream);        \
+            return true;                                                                                        \
+        }                                                                                                       \
+    }
+    QR_GEMV_VARIANTS(QR_GEMV_FUSED_CASE)
+#undef QR_GEMV_FUSED_CASE
+    return false;
+}
+
 }  // namespace
 
 int env_int(const char *name, int dflt) {
@@ -297,7 +435,7 @@ int env_int(const char *name, int dflt) {
     return atoi(v);
 }
 
-LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
+LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll) {
     (void)qtype;
     LinearPlan p{};
     const int force = env_int("QR_FORCE_VARIANT", -1);  // 0 = GEMV, 1 = tiled GEMM
@@ -352,6 +490,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
         u = fu > 0 ? fu : u;
         tb = ft > 0 ? ft : tb;
     }
+    if (u > max_unroll && gemv_variant_waves(p.m_tiles, max_unroll, tb) > 0) u = max_unroll;
     p.unroll = u;
     p.tiles = tb;
     const int64_t slices = (k + 64 * u - 1) / (64 * u);
@@ -378,6 +517,51 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k) {
     p.splits = (int)splits;
     p.ws_bytes = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * 4 : 0;
     return p;
+}
+
+LinearPlan plan_linear_bf16(int qtype, int64_t m, int64_t n, int64_t k) {
+    // the in-kernel activation quantization holds a slice's activations as floats: at most 256-byte slices
+    const LinearPlan p = plan_linear(qtype, m, n, k, 4);
+    if (linear_bf16_fused(p, qtype, m, k)) return p;
+    return plan_linear(qtype, m, n, k);
+}
+
+bool linear_bf16_fused(const LinearPlan &p, int qtype, int64_t m, int64_t k) {
+    // Every workgroup quantizes the token rows itself, so the prologue is repeated per workgroup and only its
+    // own latency is hidden by other workgroups. Measured on MI355X (graph replay, weights past the caches):
+    // at m = 1 it beats the two launches on the 1.5B INT8 layer (39.3 -> 33.8 us) and on the 7B FP8 qkv, o and
+    // gate/up, but not on the 7B FP8 down (k = 18944: 22.7 -> 30.2 us, the software E4M3 encoder over a long
+    // row), nor at m = 2 or 4.
+    const int64_t max_m = env_int("QR_FUSE_MAX_M", 1);
+    if (qtype == kFp8 && k > env_int("QR_FUSE_MAX_K_FP8", 8192)) return false;
+    return p.kind == 0 && p.m_tiles == 1 && p.splits == 1 && p.unroll == 4 &&
+           m <= std::min<int64_t>(max_m, kFuseRows) && gemv_fused_lds_bytes(p, m, k) <= 65536;
+}
+
+size_t linear_bf16_workspace_bytes(const LinearPlan &p, int qtype, int64_t m, int64_t k) {
+    if (linear_bf16_fused(p, qtype, m, k)) return 0;
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    return up((size_t)(m * k)) + up((size_t)m * 4) + p.ws_bytes;
+}
+
+hipError_t launch_linear_bf16(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint16_t *xb,
+                              const float *s, const uint8_t *wq, const float *ws, void *y, bool y_bf16,
+                              void *acc_out, void *workspace, hipStream_t stream) {
+    if (linear_bf16_fused(p, qtype, m, k)) {
+        const bool ok = qtype == kInt8 ? launch_gemv_fused_q<kInt8>(p, m, n, k, xb, s, wq, ws, y, y_bf16, acc_out, stream)
+                                       : launch_gemv_fused_q<kFp8>(p, m, n, k, xb, s, wq, ws, y, y_bf16, acc_out, stream);
+        if (!ok) return hipErrorInvalidConfiguration;
+        return hipGetLastError();
+    }
+    // the activation quantizer into the workspace, then the linear on its codes
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    uint8_t *wsb = static_cast<uint8_t *>(workspace);
+    uint8_t *xq = wsb;
+    float *xs = reinterpret_cast<float *>(wsb + up((size_t)(m * k)));
+    void *rest = wsb + up((size_t)(m * k)) + up((size_t)m * 4);
+    hipError_t e = launch_quantize_rows(xb, true, m, k, s, s == nullptr ? kSNone : kSMulRecip, qtype, xq, xs, stream);
+    if (e != hipSuccess) return e;
+    return launch_linear(p, qtype, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, rest, stream);
 }
 
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,

@@ -154,6 +154,35 @@ def test_requantize_validation():
     assert call(pc=base, c=base + 8 * 128, n=8, k=128, ps=1 << 22, sc=(1 << 22) + 16) == B.QR_ERR_ARG
 
 
+def test_linear_bf16_validation_and_workspace(monkeypatch):
+    L = B.lib()
+
+    def call(q=0, m=4, n=64, k=256, x=P, s=NULL, wc=P, ws=P, y=P, yt=1, acc=NULL, wsp=NULL, wsb=0):
+        return L.qr_w8a8_linear_bf16(q, m, n, k, x, s, wc, ws, y, yt, acc, wsp, wsb, S0)
+
+    assert call(k=250) == B.QR_ERR_UNSUPPORTED
+    assert call(m=-1) == B.QR_ERR_ARG
+    assert call(x=NULL) == B.QR_ERR_ARG
+    assert call(x=MIS) == B.QR_ERR_ALIGN
+    assert call(q=4) == B.QR_ERR_ARG
+    assert call(m=0) == B.QR_OK
+    ws = B.qr_w8a8_linear_bf16_workspace_bytes if hasattr(B, "qr_w8a8_linear_bf16_workspace_bytes") else None
+    for q in (B.QR_INT8, B.QR_FP8_E4M3):
+        # m = 1: the activation quantization runs inside the linear, no workspace (FP8: for k <= 8192)
+        assert ws(q, 1, 17920, 1536) == 0 and ws(q, 1, 3584, 3584) == 0
+        assert ws(q, 1, 1536, 8960) == (0 if q == B.QR_INT8 else 8960 + 256)
+        # larger batches: the activation codes (m k bytes) and scales (4 m), each rounded up to 256 bytes,
+        # then the linear's own workspace
+        assert ws(q, 16, 2048, 1536) == 16 * 1536 + 256
+        assert ws(q, 64, 1536, 8960) == 64 * 8960 + 256 + 2 * 64 * 1536 * 4
+        monkeypatch.setenv("QR_FUSE_MAX_M", "4")
+        assert ws(q, 4, 2048, 1536) == 0
+        monkeypatch.delenv("QR_FUSE_MAX_M")
+        assert ws(q, 4, 2048, 1536) == 4 * 1536 + 256
+    # a call that needs workspace and gets none is refused before any launch
+    assert call(m=16, n=2048, k=1536) == B.QR_ERR_WORKSPACE
+
+
 def test_workspace_sizes(monkeypatch):
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
         # GEMV plans with enough blocks, and GEMM plans with a tile for at least half the CUs, reduce inside
