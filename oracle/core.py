@@ -54,6 +54,12 @@ def lib():
         L.or_count_code_changes.restype = None
         L.or_requantize_weights.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp]
         L.or_requantize_weights.restype = None
+        L.or_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.or_moe_route.restype = None
+        L.or_silu_mul.argtypes = [vp, i64, i64, vp]
+        L.or_silu_mul.restype = None
+        L.or_moe_combine.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.or_moe_combine.restype = None
         L.or_quantize_w4.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp]
         L.or_quantize_w4.restype = None
         L.or_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, i64, i32, vp, vp]
@@ -172,6 +178,40 @@ def count_code_changes(a, b, qtype, sa=None, sb=None):
         ns = sa.size
     out = np.zeros(3, np.int64)
     lib().or_count_code_changes(_p(a), _p(b), a.size, qtype, _p(sa), _p(sb), ns, _p(out))
+    return out
+
+
+# ---- next row: MoE glue -------------------------------------------------------------------------------
+def moe_route(logits, k):
+    """Routing of logits [T, E] (fp32): returns dict of topk_expert [T,k], topk_weight [T,k], offsets [E+1],
+    row_ids [T k], row_weights [T k], pair_rows [T,k]."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    out = dict(topk_expert=np.empty((T, k), np.int32), topk_weight=np.empty((T, k), np.float32),
+               offsets=np.empty(E + 1, np.int32), row_ids=np.empty(T * k, np.int32),
+               row_weights=np.empty(T * k, np.float32), pair_rows=np.empty((T, k), np.int32))
+    lib().or_moe_route(_p(logits), T, E, k, _p(out["topk_expert"]), _p(out["topk_weight"]), _p(out["offsets"]),
+                       _p(out["row_ids"]), _p(out["row_weights"]), _p(out["pair_rows"]))
+    return out
+
+
+def silu_mul(y_gu):
+    """h [R, I] = bf16(silu(g) u) of gate/up rows [R, 2I] (bfloat16 bits)."""
+    y_gu = _c(y_gu, np.uint16)
+    R, I2 = y_gu.shape
+    h = np.empty((R, I2 // 2), np.uint16)
+    lib().or_silu_mul(_p(y_gu), R, I2 // 2, _p(h))
+    return h
+
+
+def moe_combine(y_down, topk_weight, pair_rows):
+    """out [T, H] = bf16(sum_j topk_weight[t,j] y_down[pair_rows[t,j]]) (y_down bfloat16 bits [R, H])."""
+    y_down = _c(y_down, np.uint16)
+    topk_weight, pair_rows = _c(topk_weight, np.float32), _c(pair_rows, np.int32)
+    T, k = pair_rows.shape
+    H = y_down.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().or_moe_combine(_p(y_down), _p(topk_weight), _p(pair_rows), T, k, H, _p(out))
     return out
 
 

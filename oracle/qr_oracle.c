@@ -325,6 +325,83 @@ void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, in
 }
 
 /* ------------------------------------------------------------------------------------------------------
+ * next row: MoE glue (routing, SiLU-mul, combine) around the grouped linear
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* Routing of the MoE FFN whose expert linears [QaRL] runs in W8A8 (the Qwen3-30B-A3B model of its abstract);
+ * the pages give no routing rule, reading: each token takes its k largest logits (ties to the lower expert
+ * index); its weights are the softmax over those k logits (in double, rounded to fp32). Outputs:
+ *   topk_expert[t][j], topk_weight[t][j]: the k choices of token t, expert index ascending;
+ *   offsets[E+1], row_ids[T k], row_weights[T k]: the (token, expert) rows grouped by expert (ascending), tokens
+ *     ascending inside an expert, with each row's token and weight;
+ *   pair_rows[t][j]: the row of token t's j-th choice. */
+void or_moe_route(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_expert, float *topk_weight,
+                  int32_t *offsets, int32_t *row_ids, float *row_weights, int32_t *pair_rows) {
+    int64_t t, e, j, i;
+    char *taken = (char *)malloc((size_t)(E > 0 ? E : 1));
+    int64_t *fill = (int64_t *)calloc((size_t)(E > 0 ? E : 1), sizeof(int64_t));
+    if (!taken || !fill) abort();
+    for (e = 0; e <= E; ++e) offsets[e] = 0;
+    for (t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        double mx, sum = 0.0;
+        memset(taken, 0, (size_t)E);
+        /* k rounds of arg-max (first index wins a tie); then the choices in expert order */
+        for (j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+        }
+        for (e = 0, j = 0; e < E; ++e)
+            if (taken[e]) topk_expert[t * k + j++] = (int32_t)e;
+        mx = l[topk_expert[t * k]];
+        for (j = 1; j < k; ++j)
+            if (l[topk_expert[t * k + j]] > mx) mx = l[topk_expert[t * k + j]];
+        for (j = 0; j < k; ++j) sum += exp((double)l[topk_expert[t * k + j]] - mx);
+        for (j = 0; j < k; ++j) topk_weight[t * k + j] = (float)(exp((double)l[topk_expert[t * k + j]] - mx) / sum);
+        for (j = 0; j < k; ++j) offsets[topk_expert[t * k + j] + 1]++;
+    }
+    for (e = 0; e < E; ++e) offsets[e + 1] += offsets[e];
+    for (t = 0; t < T; ++t)  /* tokens in ascending order: appending keeps them ascending inside an expert */
+        for (j = 0; j < k; ++j) {
+            e = topk_expert[t * k + j];
+            i = offsets[e] + fill[e]++;
+            row_ids[i] = (int32_t)t;
+            row_weights[i] = topk_weight[t * k + j];
+            pair_rows[t * k + j] = (int32_t)i;
+        }
+    free(taken);
+    free(fill);
+}
+
+/* h = bf16(silu(g) u) for every row of the gate/up output (gate columns [0, I), up columns [I, 2I)), with
+ * silu(g) = g / (1 + exp(-g)) in double and one rounding to bfloat16 (the gated activation of the expert FFN;
+ * the pages give no formula, reading: the Qwen3 expert's SiLU-gated product). */
+void or_silu_mul(const uint16_t *y_gu, int64_t R, int64_t I, uint16_t *h) {
+    int64_t r, j;
+    for (r = 0; r < R; ++r)
+        for (j = 0; j < I; ++j) {
+            const double g = or_bf16_to_f32(y_gu[r * 2 * I + j]), u = or_bf16_to_f32(y_gu[r * 2 * I + I + j]);
+            h[r * I + j] = or_round_to_bf16(g / (1.0 + exp(-g)) * u);
+        }
+}
+
+/* out[t][c] = bf16(sum_j topk_weight[t][j] * y_down[pair_rows[t][j]][c]) in double, the routing-weighted
+ * combine of token t's k expert outputs. */
+void or_moe_combine(const uint16_t *y_down, const float *topk_weight, const int32_t *pair_rows, int64_t T,
+                    int64_t k, int64_t H, uint16_t *out) {
+    int64_t t, j, c;
+    for (t = 0; t < T; ++t)
+        for (c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (j = 0; j < k; ++j)
+                acc += (double)topk_weight[t * k + j] * (double)or_bf16_to_f32(y_down[pair_rows[t * k + j] * H + c]);
+            out[t * H + c] = or_round_to_bf16(acc);
+        }
+}
+
+/* ------------------------------------------------------------------------------------------------------
  * next row: requantize + diff (one publish of W + dW)
  * ---------------------------------------------------------------------------------------------------- */
 

@@ -73,6 +73,15 @@ int or_grouped_linear(int qtype, int64_t num_experts, int64_t n, int64_t k, cons
 void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
                            const float *sb, int64_t n_scales, int64_t *out3);
 
+/* next row: MoE glue. Routing (top-k by logit, ties to the lower expert; softmax weights over the k logits;
+ * CSR rows by expert then token), h = bf16(silu(g) u) over gate/up rows [g | u], and the routing-weighted
+ * combine out[t] = bf16(sum_j w[t][j] y_down[pair_rows[t][j]]). */
+void or_moe_route(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_expert, float *topk_weight,
+                  int32_t *offsets, int32_t *row_ids, float *row_weights, int32_t *pair_rows);
+void or_silu_mul(const uint16_t *y_gu, int64_t R, int64_t I, uint16_t *h);
+void or_moe_combine(const uint16_t *y_down, const float *topk_weight, const int32_t *pair_rows, int64_t T,
+                    int64_t k, int64_t H, uint16_t *out);
+
 /* next row: one publish of W + dW: the a1 quantizer, then per row the a5 triple against the previous
  * publish (row_counts [rows][3]: bytes, values, scale changed) and its sums in out3 */
 void or_requantize_weights(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int qtype,
