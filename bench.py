@@ -471,6 +471,53 @@ def measure_moe(dev, reps):
         out[name] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
                      "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 3), "TFLOP/s": round(no / ms / 1e9, 2)}
         del g
+
+    # the whole expert FFN, every step on the GPU: routing of the logits into the token lists, the tokens'
+    # activation codes, grouped gate/up, SiLU product fused with its per-row codes, grouped down, weighted
+    # combine; and the glue kernels alone
+    logits_d = torch.from_numpy(logits).to(dev)
+    route = qr.qr_moe_route(logits_d, TOPK)
+    xq = (torch.empty((T, H), dtype=torch.uint8, device=dev), torch.empty(T, dtype=torch.float32, device=dev))
+    hq = (torch.empty((R, I), dtype=torch.uint8, device=dev), torch.empty(R, dtype=torch.float32, device=dev))
+    y_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def ffn():
+        for c in range(C):
+            qr.qr_moe_route(logits_d, TOPK, out=route)
+            qr.qr_quantize_acts(x, qr.QR_FP8_E4M3, codes=xq[0], scales=xq[1])
+            qr.qr_w8a8_grouped_linear(qr.QR_FP8_E4M3, route["expert_offsets"], route["row_ids"], R, xq[0], xq[1],
+                                      wgu_c[c], wgu_s[c], y=ygu)
+            qr.qr_silu_mul_quantize(ygu, qr.QR_FP8_E4M3, codes=hq[0], scales=hq[1])
+            qr.qr_w8a8_grouped_linear(qr.QR_FP8_E4M3, route["expert_offsets"], None, R, hq[0], hq[1], wd_c[c],
+                                      wd_s[c], y=yd)
+            qr.qr_moe_combine(yd, route["topk_weight"], route["pair_rows"], out=y_out)
+
+    g = TimedGraph(ffn, 6 * C)
+    ms = g.time_ms(reps) / C
+    torch.cuda.synchronize()
+    replayed = y_out.clone()
+    ffn()  # eager: the replays must have produced the same bits
+    torch.cuda.synchronize()
+    same = bool(torch.equal(replayed.view(torch.int16), y_out.view(torch.int16)))
+    del g
+    nb = T * E * 4 + T * H * 2 + E * (2 * I * H + 2 * I * 4 + H * I + H * 4) + T * H * 2
+    ffn_out = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+               "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": nb,
+               "steps": "route, activation codes, grouped gate/up, SiLU product + codes, grouped down, combine",
+               "graph_replay_equals_eager": same}
+    reps_glue = 20
+    for name, fn in (("route", lambda: qr.qr_moe_route(logits_d, TOPK, out=route)),
+                     ("silu_mul_quantize", lambda: qr.qr_silu_mul_quantize(ygu, qr.QR_FP8_E4M3, codes=hq[0],
+                                                                           scales=hq[1])),
+                     ("combine", lambda: qr.qr_moe_combine(yd, route["topk_weight"], route["pair_rows"],
+                                                           out=y_out))):
+        def many(fn=fn):
+            for _ in range(reps_glue):
+                fn()
+        g = TimedGraph(many, reps_glue)
+        ffn_out[name + "_us"] = round(g.time_ms(max(2, reps // 4)) / reps_glue * 1e3, 2)
+        del g
+    out["ffn"] = ffn_out
     del wgu_c, wgu_s, wd_c, wd_s
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -185,6 +185,50 @@ qr_status qr_quantize_weights_w4(const void *w, qr_dtype w_type, int64_t n, int6
 qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const void *w_codes, const float *w_scales,
                           void *y, qr_dtype y_type, void *stream);
 
+/*
+ * MoE routing (next row: the glue around qr_w8a8_grouped_linear for the expert FFNs of the Qwen3-30B-A3B model in
+ * the [QaRL] abstract; the pages give no routing rule, so the library reads it as the usual top-k softmax router):
+ *   for each token t, its top_k largest logits[t, :] (fp32 [num_tokens, num_experts]); equal logits go to the
+ *   lower expert index, and -0 equals +0;
+ *   topk_expert[t, j] (int32 [num_tokens, top_k]): the chosen experts in ascending expert order;
+ *   topk_weight[t, j] (fp32): exp(l_j - max) / sum_i exp(l_i - max) over the chosen logits, in fp64 with the sum
+ *     taken in expert order, rounded once to fp32;
+ *   expert_offsets (int32 [num_experts + 1]), row_ids (int32 [num_tokens * top_k]): CSR lists of the
+ *     (token, expert) rows grouped by expert, tokens ascending within an expert -- the expert_offsets / row_ids
+ *     arguments of qr_w8a8_grouped_linear; row_weights (fp32 [num_tokens * top_k]): each row's weight;
+ *   pair_rows[t, j] (int32 [num_tokens, top_k]): the row of token t's j-th choice.
+ * Deterministic. Every output is device memory, 4-byte aligned; expert_offsets is written also when
+ * num_tokens == 0. Limits: 1 <= num_experts <= 512, 1 <= top_k <= min(num_experts, 32),
+ * num_tokens * top_k < 2^31. Logits must be finite.
+ */
+qr_status qr_moe_route(const float *logits, int64_t num_tokens, int64_t num_experts, int64_t top_k,
+                       int32_t *topk_expert, float *topk_weight, int32_t *expert_offsets, int32_t *row_ids,
+                       float *row_weights, int32_t *pair_rows, void *stream);
+
+/*
+ * SiLU-gated product of the expert FFN fused with the per-row activation quantization of the down projection's
+ * input (next row: MoE glue; per-row codes as qr_quantize_acts, the token-wise scales of [QuRL] 5):
+ *   h[r, j] = bf16(silu(g) * u) with g = y_gu[r, j], u = y_gu[r, inter + j], silu(g) = g / (1 + exp(-g)),
+ *             evaluated in fp64 and rounded once to bfloat16 (nearest even);
+ *   h_codes [rows, inter], h_scales [rows]: exactly qr_quantize_acts(h, QR_BF16, rows, inter, s, q, ...).
+ * y_gu: device bfloat16 [rows, 2 * inter] (the gate/up output, gate columns first), 16-byte aligned;
+ * h: device bfloat16 [rows, inter] or NULL (the product itself, when wanted), 16-byte aligned;
+ * s: device fp32 [inter] or NULL (h diag(1/s)). inter: a positive multiple of 16. rows == 0: nothing is launched.
+ */
+qr_status qr_silu_mul_quantize(const void *y_gu, int64_t rows, int64_t inter, const float *s, qr_qtype q,
+                               void *h_codes, float *h_scales, void *h, void *stream);
+
+/*
+ * Routing-weighted combine of the expert outputs (next row: MoE glue):
+ *   out[t, c] = bf16(sum_j topk_weight[t, j] * y_down[pair_rows[t, j], c]), j = 0 .. top_k-1 in order, in fp64,
+ *   rounded once to bfloat16 (nearest even).
+ * y_down: device bfloat16 [rows, hidden]; topk_weight: fp32 [num_tokens, top_k]; pair_rows: int32
+ * [num_tokens, top_k] (as written by qr_moe_route); out: bfloat16 [num_tokens, hidden]. A pair row outside
+ * [0, rows) adds nothing. hidden: a positive multiple of 8; y_down and out 16-byte aligned.
+ */
+qr_status qr_moe_combine(const void *y_down, int64_t rows, int64_t hidden, const float *topk_weight,
+                         const int32_t *pair_rows, int64_t num_tokens, int64_t top_k, void *out, void *stream);
+
 /* Device bytes of workspace a linear (num_experts == 1, m rows) or grouped call (m = total_rows) needs. */
 size_t qr_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k, int64_t num_experts);
 

@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 # every symbol include/qr.h declares
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
            "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
-           "qr_w4a16_linear", "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_w8a8_linear_bf16_workspace_bytes")
+           "qr_w4a16_linear", "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_w8a8_linear_bf16_workspace_bytes",
+           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine")
 W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
 
@@ -63,9 +64,13 @@ def lib():
                 L.qr_w8a8_linear_bf16.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
                 L.qr_w8a8_linear_bf16_workspace_bytes.argtypes = [i32, i64, i64, i64]
                 L.qr_w8a8_linear_bf16_workspace_bytes.restype = sz
+                L.qr_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+                L.qr_silu_mul_quantize.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, vp]
+                L.qr_moe_combine.argtypes = [vp, i64, i64, vp, vp, i64, i64, vp, vp]
                 for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
                           "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear",
-                          "qr_requantize_weights", "qr_w8a8_linear_bf16"):
+                          "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_moe_route", "qr_silu_mul_quantize",
+                          "qr_moe_combine"):
                     getattr(L, f).restype = ctypes.c_int
                 L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
                 L.qr_workspace_bytes.restype = sz
@@ -330,3 +335,68 @@ def qr_count_code_changes(a, b, qtype, sa=None, sb=None, out3=None, stream=None)
     _check(lib().qr_count_code_changes(_ptr(a), _ptr(b), a.numel(), int(qtype), _ptr(sa), _ptr(sb), ns, _ptr(out3),
                                        _stream(stream)))
     return out3
+
+
+def qr_moe_route(logits, top_k, out=None, stream=None):
+    """Top-k softmax routing of logits [T, E] (float32): a dict of device tensors topk_expert [T,k] (int32, expert
+    order), topk_weight [T,k] (float32), expert_offsets [E+1] and row_ids [T k] (the CSR lists of
+    qr_w8a8_grouped_linear), row_weights [T k] and pair_rows [T,k] (int32)."""
+    _need(logits.is_cuda and logits.dtype == torch.float32 and logits.dim() == 2 and logits.is_contiguous(),
+          "logits must be a contiguous float32 [T, E] CUDA tensor")
+    T, E = logits.shape
+    k = int(top_k)
+    dev = logits.device
+    if out is None:
+        out = dict(topk_expert=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   topk_weight=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   row_ids=torch.empty(T * k, dtype=torch.int32, device=dev),
+                   row_weights=torch.empty(T * k, dtype=torch.float32, device=dev),
+                   pair_rows=torch.empty((T, k), dtype=torch.int32, device=dev))
+    _check(lib().qr_moe_route(_ptr(logits), T, E, k, _ptr(out["topk_expert"]), _ptr(out["topk_weight"]),
+                              _ptr(out["expert_offsets"]), _ptr(out["row_ids"]), _ptr(out["row_weights"]),
+                              _ptr(out["pair_rows"]), _stream(stream)))
+    return out
+
+
+def qr_silu_mul_quantize(y_gu, qtype, s=None, codes=None, scales=None, h=None, want_h=False, stream=None):
+    """h = bf16(silu(g) u) of y_gu [rows, 2I] (bfloat16, gate columns first) and its per-row codes [rows, I] and
+    scales [rows] (as qr_quantize_acts of h). Returns (codes, scales) or, with want_h / h given, (codes, scales, h)."""
+    _need(y_gu.is_cuda and y_gu.dtype == torch.bfloat16 and y_gu.dim() == 2 and y_gu.is_contiguous(),
+          "y_gu must be a contiguous bfloat16 [rows, 2I] CUDA tensor")
+    rows, i2 = y_gu.shape
+    _need(i2 % 2 == 0, "y_gu must have an even number of columns")
+    inter = i2 // 2
+    dev = y_gu.device
+    if codes is None:
+        codes = torch.empty((rows, inter), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if h is None and want_h:
+        h = torch.empty((rows, inter), dtype=torch.bfloat16, device=dev)
+    if s is not None:
+        _need(s.is_cuda and s.dtype == torch.float32 and s.numel() == inter, "s must be float32 [I]")
+    _need(codes.dtype == torch.uint8 and tuple(codes.shape) == (rows, inter) and codes.is_contiguous(), "bad codes")
+    _need(scales.dtype == torch.float32 and scales.numel() == rows, "bad scales")
+    if h is not None:
+        _need(h.dtype == torch.bfloat16 and tuple(h.shape) == (rows, inter) and h.is_contiguous(), "bad h")
+    _check(lib().qr_silu_mul_quantize(_ptr(y_gu), rows, inter, _ptr(s), int(qtype), _ptr(codes), _ptr(scales), _ptr(h),
+                                      _stream(stream)))
+    return (codes, scales, h) if h is not None else (codes, scales)
+
+
+def qr_moe_combine(y_down, topk_weight, pair_rows, out=None, stream=None):
+    """out [T, H] = bf16(sum_j topk_weight[t,j] y_down[pair_rows[t,j]]) (y_down bfloat16 [rows, H])."""
+    _need(y_down.is_cuda and y_down.dtype == torch.bfloat16 and y_down.dim() == 2 and y_down.is_contiguous(),
+          "y_down must be a contiguous bfloat16 [rows, H] CUDA tensor")
+    rows, H = y_down.shape
+    T, k = pair_rows.shape
+    _need(pair_rows.dtype == torch.int32 and pair_rows.is_contiguous(), "pair_rows must be contiguous int32 [T,k]")
+    _need(topk_weight.dtype == torch.float32 and tuple(topk_weight.shape) == (T, k) and topk_weight.is_contiguous(),
+          "topk_weight must be contiguous float32 [T,k]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_down.device)
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (T, H) and out.is_contiguous(), "bad out")
+    _check(lib().qr_moe_combine(_ptr(y_down), rows, H, _ptr(topk_weight), _ptr(pair_rows), T, k, _ptr(out),
+                                _stream(stream)))
+    return out

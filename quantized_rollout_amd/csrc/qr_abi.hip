@@ -313,6 +313,73 @@ qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const 
     return hip_status(e, "w4a16 launch");
 }
 
+qr_status qr_moe_route(const float *logits, int64_t num_tokens, int64_t num_experts, int64_t top_k,
+                       int32_t *topk_expert, float *topk_weight, int32_t *expert_offsets, int32_t *row_ids,
+                       float *row_weights, int32_t *pair_rows, void *stream) {
+    if (num_tokens < 0) return fail(QR_ERR_ARG, "negative token count %lld", (long long)num_tokens);
+    if (num_experts < 1) return fail(QR_ERR_ARG, "at least one expert is needed");
+    if (num_experts > qr::moe_max_experts())
+        return fail(QR_ERR_UNSUPPORTED, "at most %d experts (got %lld)", qr::moe_max_experts(), (long long)num_experts);
+    if (top_k < 1 || top_k > num_experts || top_k > 32)
+        return fail(QR_ERR_ARG, "top_k must be in [1, min(num_experts, 32)] (got %lld)", (long long)top_k);
+    if (num_tokens * top_k > (int64_t)INT32_MAX)
+        return fail(QR_ERR_UNSUPPORTED, "num_tokens * top_k must stay below 2^31");
+    if (expert_offsets == nullptr) return fail(QR_ERR_ARG, "null expert_offsets");
+    if (!aligned(expert_offsets, 4)) return fail(QR_ERR_ALIGN, "expert_offsets must be 4-byte aligned");
+    if (num_tokens > 0) {
+        if (logits == nullptr || topk_expert == nullptr || topk_weight == nullptr || row_ids == nullptr ||
+            row_weights == nullptr || pair_rows == nullptr)
+            return fail(QR_ERR_ARG, "null pointer");
+        if (!aligned(logits, 4) || !aligned(topk_expert, 4) || !aligned(topk_weight, 4) || !aligned(row_ids, 4) ||
+            !aligned(row_weights, 4) || !aligned(pair_rows, 4))
+            return fail(QR_ERR_ALIGN, "routing arrays must be 4-byte aligned");
+    }
+    const hipError_t e = qr::launch_moe_route(logits, num_tokens, (int)num_experts, (int)top_k, topk_expert,
+                                              topk_weight, expert_offsets, row_ids, row_weights, pair_rows,
+                                              static_cast<hipStream_t>(stream));
+    return hip_status(e, "route launch");
+}
+
+qr_status qr_silu_mul_quantize(const void *y_gu, int64_t rows, int64_t inter, const float *s, qr_qtype q,
+                               void *h_codes, float *h_scales, void *h, void *stream) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if (rows < 0) return fail(QR_ERR_ARG, "negative row count %lld", (long long)rows);
+    if (rows > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "row count %lld too large", (long long)rows);
+    if ((st = check_k(inter)) != QR_OK) return st;
+    if (rows == 0) return ok();
+    if (y_gu == nullptr || h_codes == nullptr || h_scales == nullptr) return fail(QR_ERR_ARG, "null pointer");
+    if (!aligned(y_gu, 16) || !aligned(h_codes, 16) || (h != nullptr && !aligned(h, 16)))
+        return fail(QR_ERR_ALIGN, "y_gu, h_codes and h must be 16-byte aligned");
+    if (!aligned(h_scales, 4) || (s != nullptr && !aligned(s, 4)))
+        return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+    const hipError_t e = qr::launch_silu_mul_quant(static_cast<const uint16_t *>(y_gu), rows, inter, s, (int)q,
+                                                   static_cast<uint8_t *>(h_codes), h_scales,
+                                                   static_cast<uint16_t *>(h), static_cast<hipStream_t>(stream));
+    return hip_status(e, "silu launch");
+}
+
+qr_status qr_moe_combine(const void *y_down, int64_t rows, int64_t hidden, const float *topk_weight,
+                         const int32_t *pair_rows, int64_t num_tokens, int64_t top_k, void *out, void *stream) {
+    if (rows < 0 || num_tokens < 0) return fail(QR_ERR_ARG, "negative size");
+    if (hidden <= 0) return fail(QR_ERR_ARG, "hidden must be positive (got %lld)", (long long)hidden);
+    if (hidden % 8 != 0)
+        return fail(QR_ERR_UNSUPPORTED, "hidden must be a multiple of 8 (got %lld)", (long long)hidden);
+    if (top_k < 1 || top_k > 32) return fail(QR_ERR_ARG, "top_k must be in [1, 32] (got %lld)", (long long)top_k);
+    if (num_tokens > kMaxRows || rows > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "size too large");
+    if (num_tokens == 0) return ok();
+    if (topk_weight == nullptr || pair_rows == nullptr || out == nullptr || (rows > 0 && y_down == nullptr))
+        return fail(QR_ERR_ARG, "null pointer");
+    if ((y_down != nullptr && !aligned(y_down, 16)) || !aligned(out, 16))
+        return fail(QR_ERR_ALIGN, "y_down and out must be 16-byte aligned");
+    if (!aligned(topk_weight, 4) || !aligned(pair_rows, 4))
+        return fail(QR_ERR_ALIGN, "topk_weight and pair_rows must be 4-byte aligned");
+    const hipError_t e = qr::launch_moe_combine(static_cast<const uint16_t *>(y_down), rows, topk_weight, pair_rows,
+                                                num_tokens, (int)top_k, hidden, static_cast<uint16_t *>(out),
+                                                static_cast<hipStream_t>(stream));
+    return hip_status(e, "combine launch");
+}
+
 const char *qr_last_error(void) { return g_err; }
 
 const char *qr_version(void) { return "0.1.0"; }

@@ -93,6 +93,18 @@ hipError_t launch_w4a16(const W4Plan &p, int64_t m, int64_t n, int64_t k, const 
 hipError_t launch_quantize_w4(const void *in, bool bf16, int64_t rows, int64_t k, const float *s, uint8_t *codes,
                               float *scales, hipStream_t stream);
 
+// MoE glue (qr_moe.hip): routing into CSR token lists, SiLU-gated product fused with the per-row quantization of
+// the down projection's input, routing-weighted combine.
+int moe_max_experts();
+hipError_t launch_moe_route(const float *logits, int64_t T, int E, int k, int32_t *topk_expert, float *topk_weight,
+                            int32_t *offsets, int32_t *row_ids, float *row_weights, int32_t *pair_rows,
+                            hipStream_t stream);
+hipError_t launch_silu_mul_quant(const uint16_t *y_gu, int64_t rows, int64_t I, const float *s, int qtype,
+                                 uint8_t *codes, float *scales, uint16_t *h_out, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t *y_down, int64_t rows, const float *topk_weight,
+                              const int32_t *pair_rows, int64_t T, int k, int64_t H, uint16_t *out,
+                              hipStream_t stream);
+
 // Environment overrides used for tuning sweeps (0 / -1 = automatic).
 int env_int(const char *name, int dflt);
 

@@ -221,3 +221,39 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_moe_glue_validation():
+    L = B.lib()
+    i64 = ctypes.c_int64
+
+    def route(T=256, E=128, k=8, off=P, lg=P, ptr=P):
+        return L.qr_moe_route(lg, T, E, k, ptr, ptr, off, ptr, ptr, ptr, S0)
+
+    assert route(E=513) == B.QR_ERR_UNSUPPORTED and "512" in _err()
+    assert route(E=0) == B.QR_ERR_ARG
+    assert route(k=0) == B.QR_ERR_ARG and route(k=9, E=8) == B.QR_ERR_ARG and route(k=33, E=64) == B.QR_ERR_ARG
+    assert route(T=-1) == B.QR_ERR_ARG
+    assert route(off=NULL) == B.QR_ERR_ARG
+    assert route(lg=NULL) == B.QR_ERR_ARG
+    assert route(T=2 ** 28, k=8) == B.QR_ERR_UNSUPPORTED
+    assert route(lg=ctypes.c_void_p(0x7F0000000002)) == B.QR_ERR_ALIGN
+
+    def silu(rows=2048, inter=768, q=1, yg=P, codes=P, sc=P, h=NULL):
+        return L.qr_silu_mul_quantize(yg, rows, inter, NULL, q, codes, sc, h, S0)
+
+    assert silu(inter=760) == B.QR_ERR_UNSUPPORTED and "multiple of 16" in _err()
+    assert silu(q=3) == B.QR_ERR_ARG
+    assert silu(rows=-2) == B.QR_ERR_ARG
+    assert silu(rows=0, yg=NULL) == B.QR_OK  # nothing to do
+    assert silu(yg=NULL) == B.QR_ERR_ARG
+    assert silu(codes=MIS) == B.QR_ERR_ALIGN and silu(h=MIS) == B.QR_ERR_ALIGN
+
+    def combine(rows=2048, H=2048, T=256, k=8, yd=P, out=P):
+        return L.qr_moe_combine(yd, i64(rows), i64(H), P, P, i64(T), i64(k), out, S0)
+
+    assert combine(H=2044) == B.QR_ERR_UNSUPPORTED and "multiple of 8" in _err()
+    assert combine(H=0) == B.QR_ERR_ARG and combine(k=0) == B.QR_ERR_ARG and combine(k=33) == B.QR_ERR_ARG
+    assert combine(T=0, out=NULL) == B.QR_OK
+    assert combine(out=NULL) == B.QR_ERR_ARG
+    assert combine(out=MIS) == B.QR_ERR_ALIGN and combine(yd=MIS) == B.QR_ERR_ALIGN
