@@ -45,6 +45,7 @@ struct LinearPlan {
     int tiles;         // GEMV: 16-channel tiles per block
     int64_t n_tiles;   // GEMV: 16-channel tiles
     int splits;        // GEMV: K splits across blocks (> 1: partial sums in the workspace, then a reduction)
+    bool prefetch;     // GEMV: two register stages (the next K slice's loads in flight during the current MFMAs)
     GemmPlan gemm;     // GEMM (kind 1)
     size_t ws_bytes;   // workspace bytes
 };

@@ -67,8 +67,9 @@ __device__ __forceinline__ v8i as_v8i(const uint4 &a, const uint4 &b) {
 // the slice loop then reads its activation codes from LDS. For m <= kFuseRows only.
 constexpr int kXCodes = 0, kXBf16 = 1, kXBf16S = 2;
 constexpr int kFuseRows = 4;
+constexpr int kPrefetchWaves = 8;  // most waves per block of the two-stage (prefetching) form
 
-template <int QT, int MT, int U, int TB, int WMAX, int XM = kXCodes>
+template <int QT, int MT, int U, int TB, int WMAX, int XM = kXCodes, bool PF = false>
 __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq,
                                                          const float *__restrict__ xs, const uint8_t *__restrict__ wq,
                                                          const float *__restrict__ ws, void *__restrict__ y,
@@ -236,9 +237,8 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
     };
     const int64_t full = k / kSlice;
     const int64_t full_hi = hi < full ? hi : full;
-    for (int64_t sl = lo + wave; sl < full_hi; sl += waves) {
+    auto load_slice = [&](int64_t sl, uint4 (&xv)[MT][U], uint4 (&wv)[TB][U]) {
         const int64_t kb = sl * kSlice;
-        uint4 xv[MT][U], wv[TB][U];
 #pragma unroll
         for (int t = 0; t < U; ++t)
 #pragma unroll
@@ -247,9 +247,35 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
         for (int r = 0; r < TB; ++r)
 #pragma unroll
             for (int t = 0; t < U; ++t) wv[r][t] = load16(wrow[r] + kb + 64 * t);
+    };
+    auto compute_slice = [&](uint4 (&xv)[MT][U], const uint4 (&wv)[TB][U]) {
         transpose(xv);
 #pragma unroll
         for (int r = 0; r < TB; ++r) mma(acc[r], xv, wv[r]);
+    };
+    if constexpr (PF) {
+        // two register stages: the next slice's loads are in flight while the current slice's MFMAs run, so a
+        // wave with several slices waits for one memory round trip instead of one per slice (for blocks too
+        // few to hide each other's latency: a short grid on a deep K)
+        uint4 xa[MT][U], wa[TB][U], xb[MT][U], wb[TB][U];
+        int64_t sl = lo + wave;
+        if (sl < full_hi) load_slice(sl, xa, wa);
+        while (sl < full_hi) {
+            const int64_t s1 = sl + waves;
+            if (s1 < full_hi) load_slice(s1, xb, wb);
+            compute_slice(xa, wa);
+            if (s1 >= full_hi) break;
+            const int64_t s2 = s1 + waves;
+            if (s2 < full_hi) load_slice(s2, xa, wa);
+            compute_slice(xb, wb);
+            sl = s2;
+        }
+    } else {
+        for (int64_t sl = lo + wave; sl < full_hi; sl += waves) {
+            uint4 xv[MT][U], wv[TB][U];
+            load_slice(sl, xv, wv);
+            compute_slice(xv, wv);
+        }
     }
     if (full < slices && full >= lo && full < hi && wave == (full - lo) % waves) {  // the partial last slice
         const int64_t kb = full * kSlice;
@@ -355,8 +381,14 @@ void launch_gemv_t(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const u
     const int64_t m_blocks = (m + 16 * MT - 1) / (16 * MT);
     const dim3 grid((unsigned)((p.n_tiles + TB - 1) / TB), (unsigned)m_blocks, (unsigned)p.splits);
     const size_t lds = p.waves > 1 ? (size_t)p.waves * TB * MT * 256 * 4 : 0;
-    hipLaunchKernelGGL((gemv_kernel<QT, MT, U, TB, WMAX>), grid, dim3(p.waves * 64), lds, stream, m, n, k, xq, xs, wq,
-                       ws, y, y_bf16 ? 1 : 0, acc_out, p.splits, workspace);
+    // the two-stage form holds twice the registers: at most 8 waves per block (256 VGPRs each, no spills)
+    constexpr int kPfWaves = WMAX < kPrefetchWaves ? WMAX : kPrefetchWaves;
+    if (p.prefetch)
+        hipLaunchKernelGGL((gemv_kernel<QT, MT, U, TB, kPfWaves, kXCodes, true>), grid, dim3(p.waves * 64), lds, stream,
+                           m, n, k, xq, xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, p.splits, workspace);
+    else
+        hipLaunchKernelGGL((gemv_kernel<QT, MT, U, TB, WMAX>), grid, dim3(p.waves * 64), lds, stream, m, n, k, xq, xs,
+                           wq, ws, y, y_bf16 ? 1 : 0, acc_out, p.splits, workspace);
     if (p.splits > 1) launch_splitk_reduce(QT, m, n, p.splits, workspace, xs, ws, y, y_bf16, acc_out, stream);
 }
 
@@ -515,6 +547,12 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
     if (forced_w >= 1 && forced_w <= cap) waves = forced_w;
     p.waves = (int)(waves < 1 ? 1 : waves);
     p.splits = (int)splits;
+    // two register stages for four token tiles on few blocks (32 < m <= 64, fewer than 1024 blocks): measured on
+    // MI355X, 1.5B qkv / o at m = 64 from 7.2 to 6.4 us, down (two K splits) from 16.0 to 13.9 us; neutral or
+    // slower at m <= 16 and on many-block plans, where other resident waves already hide the latency
+    const int fpf = env_int("QR_GEMV_PREFETCH", -1);
+    p.prefetch = fpf >= 0 ? fpf > 0 : (p.m_tiles == 4 && blocks < 1024);
+    if (p.prefetch && p.waves > kPrefetchWaves) p.waves = kPrefetchWaves;
     p.ws_bytes = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * 4 : 0;
     return p;
 }
