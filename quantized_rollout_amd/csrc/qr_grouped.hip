@@ -234,9 +234,23 @@ __global__ void zero3_kernel(unsigned long long *out3) {
 
 // One streaming pass over both code sets: each lane keeps kCountUnroll pairs of 16-byte loads in flight (grid-
 // stride over 16-byte words), compares bytes four at a time, and the counts are summed over the wave and added
-// with one 64-bit atomic per wave and count.
-constexpr int kCountUnroll = 4;
+// with one 64-bit atomic per wave and count. The loads are non-temporal (each byte is read once, so it should
+// not displace cached data). Measured on MI355X over two 1.31 GB code sets: 4 pairs in flight on 2048
+// workgroups 550 us; 8 pairs, non-temporal, 768 workgroups (3 per CU) 415 us = 6.3 TB/s.
+constexpr int kCountUnroll = 8;
+constexpr int kCountBlocks = 768;
 
+template <bool NT>
+__device__ __forceinline__ uint4 count_load(const uint4 *p) {
+    if constexpr (NT) {
+        const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+        return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+    } else {
+        return *p;
+    }
+}
+
+template <int UNR, bool NT>
 __global__ __launch_bounds__(256) void count_kernel(const uint8_t *__restrict__ a, const uint8_t *__restrict__ b,
                                                     int64_t count, int fp8, const uint32_t *__restrict__ sa,
                                                     const uint32_t *__restrict__ sb, int64_t n_scales,
@@ -248,15 +262,15 @@ __global__ __launch_bounds__(256) void count_kernel(const uint8_t *__restrict__ 
     const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(a);
     const uint4 *__restrict__ b4 = reinterpret_cast<const uint4 *>(b);
     int64_t i = tid;
-    for (; i + (kCountUnroll - 1) * stride < n16; i += kCountUnroll * stride) {
-        uint4 x[kCountUnroll], z[kCountUnroll];
+    for (; i + (UNR - 1) * stride < n16; i += UNR * stride) {
+        uint4 x[UNR], z[UNR];
 #pragma unroll
-        for (int u = 0; u < kCountUnroll; ++u) {
-            x[u] = a4[i + u * stride];
-            z[u] = b4[i + u * stride];
+        for (int u = 0; u < UNR; ++u) {
+            x[u] = count_load<NT>(a4 + i + u * stride);
+            z[u] = count_load<NT>(b4 + i + u * stride);
         }
 #pragma unroll
-        for (int u = 0; u < kCountUnroll; ++u) {
+        for (int u = 0; u < UNR; ++u) {
             count_word(x[u].x, z[u].x, fp8 != 0, nb, nv);
             count_word(x[u].y, z[u].y, fp8 != 0, nb, nv);
             count_word(x[u].z, z[u].z, fp8 != 0, nb, nv);
@@ -337,13 +351,22 @@ hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t coun
     if (err != hipSuccess) return err;
     // enough 256-thread blocks for every CU to hold several (2048 = 256 CUs x 8), fewer for small inputs
     const int64_t work = count / 16 > n_scales ? count / 16 : n_scales;
-    int64_t blocks = (work + 256 * kCountUnroll - 1) / (256 * kCountUnroll);
-    const int64_t max_blocks = env_int("QR_COUNT_BLOCKS", 2048);
+    const int unr = env_int("QR_COUNT_UNROLL", kCountUnroll) == 4 ? 4 : kCountUnroll;
+    const bool nt = env_int("QR_COUNT_NT", 1) > 0;
+    int64_t blocks = (work + 256 * unr - 1) / (256 * unr);
+    const int64_t max_blocks = env_int("QR_COUNT_BLOCKS", kCountBlocks);
     if (blocks > max_blocks) blocks = max_blocks;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(count_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, b, count,
-                       qtype == kFp8 ? 1 : 0, reinterpret_cast<const uint32_t *>(sa),
-                       reinterpret_cast<const uint32_t *>(sb), n_scales, o);
+#define QR_COUNT(U_, NT_)                                                                                    \
+    hipLaunchKernelGGL((count_kernel<U_, NT_>), dim3((unsigned)blocks), dim3(256), 0, stream, a, b, count, \
+                       qtype == kFp8 ? 1 : 0, reinterpret_cast<const uint32_t *>(sa),                      \
+                       reinterpret_cast<const uint32_t *>(sb), n_scales, o)
+    if (unr == 8) {
+        if (nt) QR_COUNT(8, true); else QR_COUNT(8, false);
+    } else {
+        if (nt) QR_COUNT(4, true); else QR_COUNT(4, false);
+    }
+#undef QR_COUNT
     return hipGetLastError();
 }
 
