@@ -75,7 +75,8 @@ qr_status quantize_common(const void *in, qr_dtype in_type, int64_t rows, int64_
         return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
     const hipError_t e =
         qr::launch_quantize_rows(in, in_type == QR_BF16, rows, k, s, s == nullptr ? qr::kSNone : s_mode, (int)q,
-                                 static_cast<uint8_t *>(codes), scales, static_cast<hipStream_t>(stream));
+                                 static_cast<uint8_t *>(codes), scales, static_cast<hipStream_t>(stream),
+                                 s_mode == qr::kSMul);
     return hip_status(e, "quantize launch");
 }
 

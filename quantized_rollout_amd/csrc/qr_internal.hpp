@@ -10,9 +10,10 @@ namespace qr {
 // invariant-scale modes of the row quantizer
 enum SMode { kSNone = 0, kSMul = 1, kSMulRecip = 2 };
 
-// Row quantizer: one absmax scale per row of in[rows, k] (k % 16 == 0).
+// Row quantizer: one absmax scale per row of in[rows, k] (k % 16 == 0). streaming: non-temporal loads of the input
+// and stores of the codes (weights, read and written once); activations keep their codes cached for the linear.
 hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode,
-                                int qtype, uint8_t *codes, float *scales, hipStream_t stream);
+                                int qtype, uint8_t *codes, float *scales, hipStream_t stream, bool streaming = false);
 // the weight quantizer with the changed-code triple of every row against the previous publish (which may be
 // the output itself), then out3 = the triples' sums
 hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int qtype,

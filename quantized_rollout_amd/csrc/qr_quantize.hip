@@ -56,7 +56,39 @@ __device__ __forceinline__ void expand_chunk(const uint4 &c, const float *__rest
 // compares every new code and the row's scale with the previous publish (prev_codes / prev_scales, which may be
 // codes / scales themselves: each lane reads the previous bytes it then overwrites) and writes the row's
 // changed-code triple {bytes, values, scale} to row_counts[row].
-template <bool BF16, int QT, int SMODE, int THREADS, int RPB, bool DIFF>
+// Non-temporal 16-byte load and code stores for the weight quantizer: the masters, the previous codes and the new
+// codes each pass through once, so they should not displace cached data (measured on MI355X over the 28-layer
+// 1.5B-shaped publish: 740 -> 707 us). Activation codes are read right away by the linear and keep the default.
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint4 *p) {
+    if constexpr (NT) {
+        const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+        return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+    } else {
+        return *p;
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st_codes(uint8_t *p, const uint2 &o) {
+    if constexpr (NT) {
+        typedef int v2i_t __attribute__((ext_vector_type(2)));
+        const v2i_t v = {(int)o.x, (int)o.y};
+        __builtin_nontemporal_store(v, reinterpret_cast<v2i_t *>(p));
+    } else {
+        *reinterpret_cast<uint2 *>(p) = o;
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st_codes(uint8_t *p, uint32_t o) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(p));
+    else
+        *reinterpret_cast<uint32_t *>(p) = o;
+}
+
+template <bool BF16, int QT, int SMODE, int THREADS, int RPB, bool DIFF, bool NT>
 __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void *__restrict__ in, int64_t rows,
                                                                        int64_t k, const float *__restrict__ s,
                                                                        uint8_t *codes, float *scales,
@@ -93,7 +125,7 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
     for (int i = 0; i < kC; ++i) {
         const int64_t c = t + (int64_t)i * THREADS;
         if (c < nch) {
-            keep[i] = src[c];
+            keep[i] = ld16<NT>(src + c);
             float w[E];
             expand_chunk<BF16, SMODE>(keep[i], s, c * E, w);
 #pragma unroll
@@ -153,11 +185,11 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
                 count_word(old.x, o.x, QT == kFp8, nb, nv);
                 count_word(old.y, o.y, QT == kFp8, nb, nv);
             }
-            *reinterpret_cast<uint2 *>(dst + c * 8) = o;
+            st_codes<NT>(dst + c * 8, o);
         } else {
             const uint32_t o = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
             if constexpr (DIFF) count_word(old, o, QT == kFp8, nb, nv);
-            *reinterpret_cast<uint32_t *>(dst + c * 4) = o;
+            st_codes<NT>(dst + c * 4, o);
         }
     };
 #pragma unroll
@@ -222,7 +254,7 @@ struct DiffArgs {
     int32_t *row_counts;
 };
 
-template <bool BF16, int QT, int SMODE, bool DIFF>
+template <bool BF16, int QT, int SMODE, bool DIFF, bool NT>
 hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uint8_t *codes, float *scales,
                     const DiffArgs &d, hipStream_t stream) {
     constexpr int E = BF16 ? 8 : 4;
@@ -230,7 +262,7 @@ hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uin
     const int64_t nch = k / E;
     const dim3 grid((unsigned)rows);
 #define QR_QROWS(T, R, G)                                                                                      \
-    hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, T, R, DIFF>), G, dim3(T * R), 0, stream, in, rows, \
+    hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, T, R, DIFF, NT>), G, dim3(T * R), 0, stream, in, rows, \
                        k, s, codes, scales, d.prev_codes, d.prev_scales, d.row_counts)
     if (nch <= 64 * kC) {
         constexpr int kRows = 4;
@@ -249,43 +281,45 @@ hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uin
 }
 
 template <bool BF16, int QT, bool DIFF>
-hipError_t launch_s(const void *in, int64_t rows, int64_t k, const float *s, int s_mode, uint8_t *codes,
+hipError_t launch_s(const void *in, int64_t rows, int64_t k, const float *s, int s_mode, bool nt, uint8_t *codes,
                     float *scales, const DiffArgs &d, hipStream_t stream) {
     switch (s_mode) {
         case kSMul:
-            return launch_t<BF16, QT, kSMul, DIFF>(in, rows, k, s, codes, scales, d, stream);
-        case kSMulRecip:
-            return launch_t<BF16, QT, kSMulRecip, DIFF>(in, rows, k, s, codes, scales, d, stream);
+            return nt ? launch_t<BF16, QT, kSMul, DIFF, true>(in, rows, k, s, codes, scales, d, stream)
+                      : launch_t<BF16, QT, kSMul, DIFF, false>(in, rows, k, s, codes, scales, d, stream);
+        case kSMulRecip:  // activations only
+            return launch_t<BF16, QT, kSMulRecip, DIFF, false>(in, rows, k, s, codes, scales, d, stream);
         default:
-            return launch_t<BF16, QT, kSNone, DIFF>(in, rows, k, s, codes, scales, d, stream);
+            return nt ? launch_t<BF16, QT, kSNone, DIFF, true>(in, rows, k, s, codes, scales, d, stream)
+                      : launch_t<BF16, QT, kSNone, DIFF, false>(in, rows, k, s, codes, scales, d, stream);
     }
 }
 
 template <bool DIFF>
-hipError_t launch_q(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode, int qtype,
-                    uint8_t *codes, float *scales, const DiffArgs &d, hipStream_t stream) {
+hipError_t launch_q(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode, bool nt,
+                    int qtype, uint8_t *codes, float *scales, const DiffArgs &d, hipStream_t stream) {
     if (in_bf16) {
-        return qtype == kInt8 ? launch_s<true, kInt8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream)
-                              : launch_s<true, kFp8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream);
+        return qtype == kInt8 ? launch_s<true, kInt8, DIFF>(in, rows, k, s, s_mode, nt, codes, scales, d, stream)
+                              : launch_s<true, kFp8, DIFF>(in, rows, k, s, s_mode, nt, codes, scales, d, stream);
     }
-    return qtype == kInt8 ? launch_s<false, kInt8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream)
-                          : launch_s<false, kFp8, DIFF>(in, rows, k, s, s_mode, codes, scales, d, stream);
+    return qtype == kInt8 ? launch_s<false, kInt8, DIFF>(in, rows, k, s, s_mode, nt, codes, scales, d, stream)
+                          : launch_s<false, kFp8, DIFF>(in, rows, k, s, s_mode, nt, codes, scales, d, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode,
-                                int qtype, uint8_t *codes, float *scales, hipStream_t stream) {
-    return launch_q<false>(in, in_bf16, rows, k, s, s_mode, qtype, codes, scales, DiffArgs{nullptr, nullptr, nullptr},
-                           stream);
+                                int qtype, uint8_t *codes, float *scales, hipStream_t stream, bool streaming) {
+    return launch_q<false>(in, in_bf16, rows, k, s, s_mode, streaming, qtype, codes, scales,
+                           DiffArgs{nullptr, nullptr, nullptr}, stream);
 }
 
 hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int qtype,
                              const uint8_t *prev_codes, const float *prev_scales, uint8_t *codes, float *scales,
                              int32_t *row_counts, int64_t *out3, hipStream_t stream) {
     if (rows > 0) {  // no rows: out3 is still written (zeros)
-        const hipError_t e = launch_q<true>(in, in_bf16, rows, k, s, s == nullptr ? kSNone : kSMul, qtype, codes,
-                                            scales, DiffArgs{prev_codes, prev_scales, row_counts}, stream);
+        const hipError_t e = launch_q<true>(in, in_bf16, rows, k, s, s == nullptr ? kSNone : kSMul, true, qtype,
+                                            codes, scales, DiffArgs{prev_codes, prev_scales, row_counts}, stream);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(sum_row_counts_kernel, dim3(1), dim3(1024), 0, stream, row_counts, rows, out3);
