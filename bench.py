@@ -10,7 +10,9 @@ than the 256 MB last-level cache and every read comes from HBM):
   2. decode, at every batch M in (1, 16, 64) ("QuRL" section 5: token-wise activation scales), for each
      layer and each of qkv 1536->2048, o 1536->1536, gate/up 1536->2x8960, down 8960->1536:
      a2  quantize the layer's bf16 activations per token;
-     a3  the W8A8 linear with its dequantization epilogue, bf16 out.
+     a3  the W8A8 linear with its dequantization epilogue, bf16 out;
+     at M = 1 both run in one launch (qr_w8a8_linear_bf16: each workgroup quantizes the token row into its LDS,
+     the same codes and outputs bit for bit), at M = 16 and 64 as two launches.
 The step is captured once in a HIP graph (about 680 launches, most of them a few microseconds long) and
 replayed; inputs are resident in HBM before the timed region starts.
 
@@ -43,6 +45,7 @@ MFMA_PEAK_TOPS = 5000.0       # MI355X dense INT8 POP/s and FP8 PFLOP/s, publish
 LAYERS = 28
 LINEARS = (("qkv", 2048, 1536), ("o", 1536, 1536), ("gate_up", 17920, 1536), ("down", 1536, 8960))
 BATCHES = (1, 16, 64)
+FUSED_BATCHES = (1,)          # decode batches whose activation quantization runs inside the linear
 M_MAX = max(BATCHES)
 WEIGHT_STD = 0.02
 W4_GROUP = 128                # input channels per INT4 scale group (W4A16)
@@ -168,7 +171,9 @@ class DecoderStack:
             self.xs[name] = torch.empty((LAYERS, M_MAX), dtype=torch.float32, device=dev)
             self.y[name] = torch.empty((M_MAX, n), dtype=torch.bfloat16, device=dev)
         self.wsp = qr.Workspace()
-        need = max(qr.qr_workspace_bytes(qr.QR_INT8, m, n, k) for m in BATCHES for _, n, k in LINEARS)
+        need = max(max(qr.qr_workspace_bytes(qr.QR_INT8, m, n, k),
+                       qr.qr_w8a8_linear_bf16_workspace_bytes(qr.QR_INT8, m, n, k))
+                   for m in BATCHES for _, n, k in LINEARS)
         self.wsp.get(need)
         torch.cuda.synchronize()
 
@@ -198,7 +203,8 @@ class DecoderStack:
                                   self.wc[name][l * n:(l + 1) * n], self.ws[name][l * n:(l + 1) * n],
                                   y=self.y[name][:m], workspace=self.wsp)
 
-    def decode(self, m):
+    def decode_separate(self, m):
+        """a2 then a3 for every linear: two launches each"""
         qr = self.qr
         for l in range(LAYERS):
             for name, n, k in LINEARS:
@@ -207,6 +213,22 @@ class DecoderStack:
                 qr.qr_w8a8_linear(qr.QR_INT8, self.xc[name][l, :m], self.xs[name][l, :m],
                                   self.wc[name][l * n:(l + 1) * n], self.ws[name][l * n:(l + 1) * n],
                                   y=self.y[name][:m], workspace=self.wsp)
+
+    def decode_fused(self, m):
+        """a2 inside a3 (qr_w8a8_linear_bf16 on the bfloat16 activations): one launch per linear"""
+        qr = self.qr
+        for l in range(LAYERS):
+            for name, n, k in LINEARS:
+                qr.qr_w8a8_linear_bf16(qr.QR_INT8, self.x[name][l, :m], self.wc[name][l * n:(l + 1) * n],
+                                       self.ws[name][l * n:(l + 1) * n], y=self.y[name][:m], workspace=self.wsp)
+
+    def decode(self, m):
+        # single-token decode runs the activation quantization inside the linear's kernel (the same codes and
+        # outputs, bit for bit, one launch instead of two); larger batches quantize first, then run the linear
+        if m in FUSED_BATCHES:
+            self.decode_fused(m)
+        else:
+            self.decode_separate(m)
 
     def step(self):
         self.publish_quantize()
@@ -350,7 +372,8 @@ def measure_decode_fused(stack, reps):
                 qr.qr_w8a8_linear_bf16(qr.QR_INT8, stack.x[name][l, :1], stack.wc[name][l * n:(l + 1) * n],
                                        stack.ws[name][l * n:(l + 1) * n], y=stack.y[name][:1], workspace=stack.wsp)
 
-    g2, gf = TimedGraph(lambda: stack.decode(1), 2 * LAYERS * len(LINEARS)), TimedGraph(fused, LAYERS * len(LINEARS))
+    g2, gf = (TimedGraph(lambda: stack.decode_separate(1), 2 * LAYERS * len(LINEARS)),
+              TimedGraph(fused, LAYERS * len(LINEARS)))
     ms2, msf = g2.time_ms(reps), gf.time_ms(reps)
     outs = []
     for g in (g2, gf):
@@ -833,7 +856,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "qwen2.5-1.5b-shaped INT8 W8A8 decoder linears x %d layers: publish (a1+a5) + "
-                               "decode at M=1,16,64 (a2+a3)" % LAYERS,
+                               "decode at M=1,16,64 (a2+a3; at M=1 in one launch)" % LAYERS,
                    "layers": LAYERS, "linears": {n: [nn, k] for n, nn, k in LINEARS}, "batches": list(BATCHES),
                    "weights": "bf16 N(0,0.02)", "acts": "bf16 N(0,1), 4 outlier channels x20"},
         "tops": round(step_ops * args.steps / (ms_total / 1e3) / 1e12, 3),
