@@ -609,18 +609,24 @@ def row_pieces(stack):
     return pieces
 
 
-def sources_digest():
-    """sha256 over the library's kernel sources: a traffic figure is only reported for the sources it was
-    measured on."""
+# the library sources each row's kernels are built from (plus the shared device and host headers and the ABI,
+# which holds the planners' inputs): a measured traffic figure stays valid while these files are unchanged
+ROW_SOURCES = {"a1": ["qr_quantize.hip"], "a2": ["qr_quantize.hip"], "a5": ["qr_grouped.hip"],
+               "a3": ["qr_linear.hip", "qr_gemm.hip"]}
+SHARED_SOURCES = ["qr_device.hpp", "qr_internal.hpp", "qr_abi.hip"]
+
+
+def sources_digest(row):
+    """sha256 over the library sources of `row`'s kernels: a traffic figure is only reported for the sources it
+    was measured on."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_rollout_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(ROW_SOURCES[row.split("_")[0]] + SHARED_SOURCES):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -710,7 +716,7 @@ def traffic_summary(fetch_dir, write_dir, name, reps, command):
         "",
         "traffic_row: %s" % name,
         "traffic_bytes_per_launch: %d" % int(per_launch),
-        "traffic_sources_sha256: %s" % sources_digest(),
+        "traffic_sources_sha256: %s" % sources_digest(name),
         "",
     ]
     return "\n".join(lines)
@@ -727,7 +733,7 @@ def read_traffic(name):
                 if line.startswith("traffic_") and ":" in line:
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        if fields.get("traffic_row") == name and fields.get("traffic_sources_sha256") == sources_digest():
+        if fields.get("traffic_row") == name and fields.get("traffic_sources_sha256") == sources_digest(name):
             return int(fields["traffic_bytes_per_launch"])
     return None
 

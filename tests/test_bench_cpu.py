@@ -39,19 +39,29 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     fields = dict(line.split(": ", 1) for line in md.splitlines() if line.startswith("traffic_"))
     assert fields["traffic_row"] == row
     assert int(fields["traffic_bytes_per_launch"]) == (100 * 2 + 10) * 1024
-    assert fields["traffic_sources_sha256"] == bench.sources_digest()
+    assert fields["traffic_sources_sha256"] == bench.sources_digest(row)
     assert "| algorithmic (what the method must move) | %d |" % (nbytes // launches) in md
 
 
 def test_traffic_is_only_reported_for_the_current_sources(tmp_path, monkeypatch):
+    """The figure is valid while the sources of the row's kernels (and the shared headers and ABI) are
+    unchanged; a change elsewhere in the library leaves it valid."""
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     (tmp_path / "profiles").mkdir()
-    (tmp_path / "quantized_rollout_amd" / "csrc").mkdir(parents=True)
-    (tmp_path / "quantized_rollout_amd" / "csrc" / "k.hip").write_text("kernel v1")
-    digest = bench.sources_digest()
+    csrc = tmp_path / "quantized_rollout_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in bench.SHARED_SOURCES + sum(bench.ROW_SOURCES.values(), []) + ["qr_moe.hip"]:
+        (csrc / name).write_text("v1 " + name)
+    digest = bench.sources_digest("a3_linear_m64")
     (tmp_path / "profiles" / "traffic_x.md").write_text(
         "traffic_row: a3_linear_m64\ntraffic_bytes_per_launch: 123\ntraffic_sources_sha256: %s\n" % digest)
     assert bench.read_traffic("a3_linear_m64") == 123
     assert bench.read_traffic("a1_quantize_weights") is None
-    (tmp_path / "quantized_rollout_amd" / "csrc" / "k.hip").write_text("kernel v2")
+    (csrc / "qr_moe.hip").write_text("v2")  # not a source of the row's kernels
+    assert bench.read_traffic("a3_linear_m64") == 123
+    (csrc / "qr_linear.hip").write_text("v2")
+    assert bench.read_traffic("a3_linear_m64") is None
+    (csrc / "qr_linear.hip").write_text("v1 qr_linear.hip")
+    assert bench.read_traffic("a3_linear_m64") == 123
+    (csrc / "qr_device.hpp").write_text("v2")
     assert bench.read_traffic("a3_linear_m64") is None
