@@ -41,6 +41,14 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert int(fields["traffic_bytes_per_launch"]) == (100 * 2 + 10) * 1024
     assert fields["traffic_sources_sha256"] == bench.sources_digest(row)
     assert "| algorithmic (what the method must move) | %d |" % (nbytes // launches) in md
+    # a call that runs two kernels (a split-K reduction after the linear): both count toward that call
+    fetch2 = fetch[:-1] + [("qr::splitk_reduce_kernel", 50.0)] * (2 * launches) + fetch[-1:]
+    write2 = write[:-1] + [("qr::splitk_reduce_kernel", 4.0)] * (2 * launches) + write[-1:]
+    _write_counters(str(tmp_path / "f2"), "FETCH_SIZE", fetch2)
+    _write_counters(str(tmp_path / "w2"), "WRITE_SIZE", write2)
+    md2 = bench.traffic_summary(str(tmp_path / "f2"), str(tmp_path / "w2"), row, 2, "cmd")
+    fields2 = dict(line.split(": ", 1) for line in md2.splitlines() if line.startswith("traffic_"))
+    assert int(fields2["traffic_bytes_per_launch"]) == (100 * 2 + 50 * 2 + 10 + 4) * 1024
 
 
 def test_traffic_is_only_reported_for_the_current_sources(tmp_path, monkeypatch):
