@@ -58,7 +58,8 @@ __device__ __forceinline__ void expand_chunk(const uint4 &c, const float *__rest
 // changed-code triple {bytes, values, scale} to row_counts[row].
 // Non-temporal 16-byte load and code stores for the weight quantizer: the masters, the previous codes and the new
 // codes each pass through once, so they should not displace cached data (measured on MI355X over the 28-layer
-// 1.5B-shaped publish: 740 -> 707 us). Activation codes are read right away by the linear and keep the default.
+// 1.5B-shaped publish: 740 -> 707 us; the requantize + diff form with the previous codes' loads non-temporal
+// too: 1139 -> 1086 us). Activation codes are read right away by the linear and keep the default.
 template <bool NT>
 __device__ __forceinline__ uint4 ld16(const uint4 *p) {
     if constexpr (NT) {
@@ -88,6 +89,14 @@ __device__ __forceinline__ void st_codes(uint8_t *p, uint32_t o) {
         *reinterpret_cast<uint32_t *>(p) = o;
 }
 
+// non-temporal loads of the previous publish's code words (4 or 8 bytes), read once by the DIFF form
+__device__ __forceinline__ uint32_t ld_nt(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint2 ld_nt(const uint2 *p) {
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    const v2i_t v = __builtin_nontemporal_load(reinterpret_cast<const v2i_t *>(p));
+    return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
+
 template <bool BF16, int QT, int SMODE, int THREADS, int RPB, bool DIFF, bool NT>
 __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void *__restrict__ in, int64_t rows,
                                                                        int64_t k, const float *__restrict__ s,
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
 #pragma unroll
         for (int i = 0; i < kC; ++i) {
             const int64_t c = t + (int64_t)i * THREADS;
-            if (c < nch) old_keep[i] = *reinterpret_cast<const cword_t *>(prev + c * E);
+            if (c < nch) old_keep[i] = ld_nt(reinterpret_cast<const cword_t *>(prev + c * E));
         }
     }
 
