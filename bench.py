@@ -649,6 +649,37 @@ def profile_row(stack, name, reps):
     torch.cuda.synchronize()
 
 
+def profile_linear(dev, spec, reps):
+    """One W8A8 linear shape for counter runs: `spec` = "int8|fp8:M:N:K"; distinct weight-code copies (together
+    past the caches) are used in turn for `reps` calls between two elementwise copies (the markers)."""
+    import torch
+
+    import quantized_rollout_amd as qr
+
+    qname, m, n, k = spec.split(":")
+    q = {"int8": qr.QR_INT8, "fp8": qr.QR_FP8_E4M3}[qname]
+    m, n, k = int(m), int(n), int(k)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    copies = max(2, min(reps, int(1.2e9 // (n * k)) + 1))
+    # codes of N(0, 0.02) weights and N(0, 1) activations quantized by the library (every byte a valid code)
+    w = [qr.qr_quantize_weights(normal_bf16(gen, (n, k), WEIGHT_STD, dev), q) for _ in range(copies)]
+    xc, xs = qr.qr_quantize_acts(activations_bf16(gen, 1, m, k, dev)[0], q)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    wsp = qr.Workspace()
+    src = torch.ones(TRAFFIC_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        qr.qr_w8a8_linear(q, xc, xs, w[i % copies][0], w[i % copies][1], y=y, workspace=wsp)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("profiled %d calls of %s" % (reps, spec))
+
+
 def _counter_dispatches(directory, counter):
     """[(dispatch id, kernel name, value)] of one counter from a rocprofv3 csv output directory."""
     import csv
@@ -754,6 +785,8 @@ def main():
     ap.add_argument("--profile-row", metavar="ROW", help="only run ROW between two device copies (for the "
                     "rocprofv3 counter runs) and exit")
     ap.add_argument("--profile-reps", type=int, default=3)
+    ap.add_argument("--profile-linear", metavar="Q:M:N:K", help="only run one W8A8 linear shape (int8 or fp8) "
+                    "--profile-reps times between two device copies (for the rocprofv3 counter runs) and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the markdown summary of the two counter runs of --profile-row ROW and exit")
     ap.add_argument("--traffic-command", default="", help="the command lines recorded in that summary")
@@ -781,6 +814,9 @@ def main():
     torch.cuda.set_device(dev)
     log("device %s, libqr %s" % (torch.cuda.get_device_name(dev), qr.qr_version()))
 
+    if args.profile_linear:
+        profile_linear(dev, args.profile_linear, args.profile_reps)
+        return 0
     stack = DecoderStack(dev)
     if args.profile_row:
         profile_row(stack, args.profile_row, args.profile_reps)
