@@ -47,11 +47,13 @@ struct LinearPlan {
     int64_t n_tiles;   // GEMV: 16-channel tiles
     int splits;        // GEMV: K splits across blocks (> 1: partial sums in the workspace, then a reduction)
     bool prefetch;     // GEMV: two register stages (the next K slice's loads in flight during the current MFMAs)
+    int ksub;          // GEMV: K parts inside each MFMA (1, 2, 4, 8): tiles of 16 / ksub channels, m <= 16 / ksub
     GemmPlan gemm;     // GEMM (kind 1)
     size_t ws_bytes;   // workspace bytes
 };
 
-LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll = 8);
+// fused_quant: the plan is for the in-kernel activation quantization (qr_w8a8_linear_bf16)
+LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll = 8, bool fused_quant = false);
 
 hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,

@@ -20,6 +20,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace qr {
 namespace {
@@ -69,7 +70,7 @@ constexpr int kXCodes = 0, kXBf16 = 1, kXBf16S = 2;
 constexpr int kFuseRows = 4;
 constexpr int kPrefetchWaves = 8;  // most waves per block of the two-stage (prefetching) form
 
-template <int QT, int MT, int U, int TB, int WMAX, int XM = kXCodes, bool PF = false>
+template <int QT, int MT, int U, int TB, int WMAX, int XM = kXCodes, bool PF = false, int KS = 1>
 __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq,
                                                          const float *__restrict__ xs, const uint8_t *__restrict__ wq,
                                                          const float *__restrict__ ws, void *__restrict__ y,
@@ -80,6 +81,13 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
     typedef typename Acc<QT>::type acc_t;
     static_assert(QT == kInt8 || U % 2 == 0, "FP8 pairs load instructions");
     static_assert(XM == kXCodes || MT == 1, "in-kernel activation quantization for one token tile only");
+    static_assert(KS == 1 || (MT == 1 && TB == 1 && !PF), "K parts inside the MFMA: one token tile, one weight tile");
+    // KS > 1: K is cut into KS parts inside each MFMA. Lane row j of the weight operand is channel j / KS of a tile of
+    // 16 / KS channels, over K part j % KS; row i of the activation operand is token i / KS over K part i % KS.
+    // The products wanted are the blocks with equal parts, y[t][c] = sum_q C[t KS + q][c KS + q]: a tile covers
+    // 16 / KS channels (KS times the workgroups on a few-channel linear) for at most 16 / KS tokens.
+    constexpr int kCpt = 16 / KS;  // channels (and tokens) per tile
+    const int64_t kq = k / KS;     // bytes of one K part (the host keeps k a multiple of 16 KS)
     extern __shared__ int32_t red[];  // [waves][TB][MT][4][64]
     const int waves = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
     const int64_t tile0 = (int64_t)blockIdx.x * TB;
     const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
     constexpr int64_t kSlice = 64 * U;
-    const int64_t slices = (k + kSlice - 1) / kSlice;
+    const int64_t slices = (kq + kSlice - 1) / kSlice;
     // split-K across blocks (blockIdx.z): this block's slices [lo, hi); with splits > 1 the raw sums go to
     // partial[split][m][n] and a separate reduction adds the splits in order and applies the epilogue
     const int64_t per_split = (slices + splits - 1) / splits;
@@ -100,18 +108,20 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
     const uint8_t *__restrict__ wrow[TB];
 #pragma unroll
     for (int r = 0; r < TB; ++r) {
-        const int64_t col = (tile0 + r) * 16 + j;
-        wrow[r] = wq + (col < n ? col : n - 1) * k + 16 * g;
+        const int64_t col = (tile0 + r) * kCpt + j / KS;
+        wrow[r] = wq + (col < n ? col : n - 1) * k + (int64_t)(j % KS) * kq + 16 * g;
     }
     // coalesced activation loads: lane l reads token row (l >> 2) of each token tile, piece (l & 3)
     const int xr = lane >> 2, xp = lane & 3;
+    const int xtok = xr / KS;                      // token of this lane's activation row (KS = 1: the row)
+    const int64_t xkoff = (int64_t)(xr % KS) * kq;  // and its K part
     const int src_lane = 4 * j + g;  // the lane that loads what lane (j, g) needs
     // token rows past m re-read row m-1: they only feed output rows that are never stored
     const uint8_t *__restrict__ xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int64_t r = m0 + mt * 16 + xr;
-        xrow[mt] = xq + (r < m ? r : m - 1) * k + 16 * xp;
+        const int64_t r = m0 + mt * 16 + xtok;
+        xrow[mt] = xq + (r < m ? r : m - 1) * k + xkoff + 16 * xp;
     }
 
     acc_t acc[TB][MT];
@@ -199,8 +209,8 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
         if constexpr (XM == kXCodes) {
             return load16(codes_at);
         } else {
-            const int row = xr < xrows ? xr : xrows - 1;
-            return *reinterpret_cast<const uint4 *>(xlds + row * k + j0);
+            const int row = xtok < xrows ? xtok : xrows - 1;
+            return *reinterpret_cast<const uint4 *>(xlds + row * k + xkoff + j0);
         }
     };
 
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
             }
         }
     };
-    const int64_t full = k / kSlice;
+    const int64_t full = kq / kSlice;
     const int64_t full_hi = hi < full ? hi : full;
     auto load_slice = [&](int64_t sl, uint4 (&xv)[MT][U], uint4 (&wv)[TB][U]) {
         const int64_t kb = sl * kSlice;
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
         uint4 xv[MT][U], wv[TB][U];
 #pragma unroll
         for (int t = 0; t < U; ++t) {
-            const bool in = kb + 64 * t + 16 * xp < k;
+            const bool in = kb + 64 * t + 16 * xp < kq;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 xv[mt][t] = in ? x_codes16(xrow[mt] + kb + 64 * t, kb + 64 * t + 16 * xp) : make_uint4(0, 0, 0, 0);
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
         for (int r = 0; r < TB; ++r)
 #pragma unroll
             for (int t = 0; t < U; ++t) {
-                const bool in = kb + 64 * t + 16 * g < k;
+                const bool in = kb + 64 * t + 16 * g < kq;
                 wv[r][t] = in ? load16(wrow[r] + kb + 64 * t) : make_uint4(0, 0, 0, 0);
             }
         transpose(xv);
@@ -337,6 +347,42 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
                         acc[r][mt][i] = sum;
                     }
                 }
+            }
+            if constexpr (KS > 1) {
+                // the complete 16 x 16 fragment goes through this wave's own LDS area (after the reduction has
+                // read it), then lane t kCpt + c adds the equal-part blocks C[t KS + q][c KS + q] over q in order
+                // and applies the epilogue to token t, channel c of the tile
+                int32_t *frag = red + (int64_t)wave * (kFrags * 256);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = (4 * g + i) * 16 + j;  // C[4 g + i][j]
+                    if constexpr (QT == kInt8)
+                        frag[idx] = acc[r][mt][i];
+                    else
+                        frag[idx] = __float_as_int(acc[r][mt][i]);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's stores land before its reads
+                const int tt = lane / kCpt, c = lane % kCpt;
+                const int64_t row = m0 + tt, col = tile0 * kCpt + c;
+                if (lane < kCpt * kCpt && row < m && col < n) {
+                    typename std::remove_reference<decltype(acc[0][0][0])>::type a = 0;
+                    for (int q = 0; q < KS; ++q) {
+                        const int32_t v = frag[(tt * KS + q) * 16 + c * KS + q];
+                        if constexpr (QT == kInt8)
+                            a += v;
+                        else
+                            a += __int_as_float(v);
+                    }
+                    float sxv;
+                    if constexpr (XM == kXCodes)
+                        sxv = xs[row];
+                    else
+                        sxv = xq_scale[row - m0];
+                    const float v = acc_to_f32(a) * sxv * ws[col];
+                    store_y(y, row * n + col, v, y_bf16 != 0);
+                    if (acc_out != nullptr) store_acc(acc_out, row * n + col, a);
+                }
+                continue;
             }
             const int64_t col = (tile0 + r) * 16 + j;
             if (splits > 1) {
@@ -407,10 +453,44 @@ int gemv_variant_waves(int mt, int u, int tb) {
     return 0;
 }
 
+// the GEMV with K cut into S parts inside the MFMA (one token tile of at most 16 / S tokens, one weight tile of
+// 16 / S channels per workgroup, no K split across workgroups)
+template <int QT, int U, int S, int XM>
+void launch_gemv_ksub_t(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                        const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, size_t lds,
+                        const uint16_t *xb, const float *s, hipStream_t stream) {
+    const dim3 grid((unsigned)p.n_tiles, 1u, 1u);
+    hipLaunchKernelGGL((gemv_kernel<QT, 1, U, 1, 16, XM, false, S>), grid, dim3(p.waves * 64), lds, stream, m, n, k, xq,
+                       xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, 1, nullptr, xb, s);
+}
+
+template <int QT, int XM>
+bool launch_gemv_ksub(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                      const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, size_t lds,
+                      const uint16_t *xb, const float *s, hipStream_t stream) {
+#define QR_KSUB(U_, S_)                                                                                          \
+    if (p.unroll == U_ && p.ksub == S_) {                                                                        \
+        launch_gemv_ksub_t<QT, U_, S_, XM>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, lds, xb, s, stream); \
+        return true;                                                                                             \
+    }
+    QR_KSUB(4, 2) QR_KSUB(4, 4) QR_KSUB(4, 8)
+    if constexpr (XM == kXCodes) {
+        QR_KSUB(8, 2) QR_KSUB(8, 4) QR_KSUB(8, 8)
+    }
+#undef QR_KSUB
+    return false;
+}
+
 template <int QT>
 void launch_gemv_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
                    const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
                    hipStream_t stream) {
+    if (p.ksub > 1) {
+        if (launch_gemv_ksub<QT, kXCodes>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, (size_t)p.waves * 1024,
+                                          nullptr, nullptr, stream))
+            return;
+        abort();  // plan_linear only produces the cases above
+    }
 #define QR_GEMV_CASE(MT_, U_, TB_, W_)                                                                          \
     if (p.m_tiles == MT_ && p.unroll == U_ && p.tiles == TB_) {                                                 \
         launch_gemv_t<QT, MT_, U_, TB_, W_>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream); \
@@ -447,6 +527,13 @@ template <int QT>
 bool launch_gemv_fused_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint16_t *xb, const float *s,
                          const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          hipStream_t stream) {
+    if (p.ksub > 1) {
+        const size_t lds = gemv_fused_lds_bytes(p, m, k);
+        return s != nullptr ? launch_gemv_ksub<QT, kXBf16S>(p, m, n, k, nullptr, nullptr, wq, ws, y, y_bf16, acc_out,
+                                                            lds, xb, s, stream)
+                            : launch_gemv_ksub<QT, kXBf16>(p, m, n, k, nullptr, nullptr, wq, ws, y, y_bf16, acc_out,
+                                                           lds, xb, s, stream);
+    }
 #define QR_GEMV_FUSED_CASE(MT_, U_, TB_, W_)                                                                    \
     if constexpr (MT_ == 1 && U_ == 4) {                                                                        \
         if (p.m_tiles == MT_ && p.unroll == U_ && p.tiles == TB_) {                                             \
@@ -467,7 +554,7 @@ int env_int(const char *name, int dflt) {
     return atoi(v);
 }
 
-LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll) {
+LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll, bool fused_quant) {
     (void)qtype;
     LinearPlan p{};
     const int force = env_int("QR_FORCE_VARIANT", -1);  // 0 = GEMV, 1 = tiled GEMM
@@ -523,9 +610,40 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
         tb = ft > 0 ? ft : tb;
     }
     if (u > max_unroll && gemv_variant_waves(p.m_tiles, max_unroll, tb) > 0) u = max_unroll;
+    // K cut into S parts inside the MFMA for one token tile of m <= 16 / S tokens: tiles of 16 / S channels, S
+    // times the workgroups. A linear with fewer 16-channel tiles than about two per CU cannot stream at full rate
+    // (one CU streams at most ~25 GB/s), and at m = 1 the MFMA's token rows are free to carry K parts instead.
+    // Chosen at m = 1 from measurements on MI355X (graph replay, weights past the caches):
+    //  - codes in: 8 parts below 512 tiles with k <= 8960 (1.5B down 8.8 -> 5.8 us, o 4.3 -> 3.4, 7B qkv
+    //    7.6 -> 5.8, o 6.0 -> 5.2), 2 or 4 on many tiles (1.5B gate/up 8.2 -> 7.9 with k < 2048, 7B gate/up
+    //    26.8 -> 24.5), none for the 7B down (k = 18944: slower with any split);
+    //  - activation quantization inside the kernel (every workgroup repeats it): 2 parts below 256 tiles (1.5B
+    //    qkv 6.4 -> 5.6 us, o 6.3 -> 5.5, down 11.4 -> 9.3; 7B o 9.2 -> 8.2), none otherwise.
+    // QR_GEMV_KSUB forces S; other GEMV overrides turn the automatic choice off.
+    p.ksub = 1;
+    if (p.m_tiles == 1) {
+        const int fk = env_int("QR_GEMV_KSUB", 0);
+        const bool overrides = fu > 0 || ft > 0 || env_int("QR_GEMV_WAVES", 0) > 0 || env_int("QR_GEMV_SPLITS", 0) > 0;
+        int ks = 1;
+        if (fk == 2 || fk == 4 || fk == 8) {
+            ks = fk;
+        } else if (fk == 0 && !overrides && m == 1) {
+            if (fused_quant)
+                ks = p.n_tiles < 256 ? 2 : 1;
+            else if (k <= 8960)
+                ks = p.n_tiles < 512 ? 8 : (k >= 2048 ? 4 : 2);
+        }
+        while (ks > 1 && k % (16 * ks) != 0) ks /= 2;
+        if (ks > 1 && m <= 16 / ks && (u == 4 || u == 8)) {
+            p.ksub = ks;
+            tb = 1;
+            p.n_tiles = (n + 16 / ks - 1) / (16 / ks);
+        }
+    }
     p.unroll = u;
     p.tiles = tb;
-    const int64_t slices = (k + 64 * u - 1) / (64 * u);
+    const int64_t kpart = k / p.ksub;
+    const int64_t slices = (kpart + 64 * u - 1) / (64 * u);
     // the reduction's LDS (waves x tb x m_tiles KiB) stays within 64 KiB
     int cap = gemv_variant_waves(p.m_tiles, u, tb);
     if (cap > 64 / (tb * p.m_tiles)) cap = 64 / (tb * p.m_tiles);
@@ -540,6 +658,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
     if (p.m_tiles == 4 && blocks < 128 && slices >= 16) splits = 2;
     const int fs = env_int("QR_GEMV_SPLITS", 0);
     if (fs >= 1) splits = std::min<int64_t>(fs, slices);
+    if (p.ksub > 1) splits = 1;
     const int64_t per_split = (slices + splits - 1) / splits;
     splits = (slices + per_split - 1) / per_split;  // no split without a slice
     int64_t waves = per_split < waves_cap ? per_split : waves_cap;
@@ -559,7 +678,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
 
 LinearPlan plan_linear_bf16(int qtype, int64_t m, int64_t n, int64_t k) {
     // the in-kernel activation quantization holds a slice's activations as floats: at most 256-byte slices
-    const LinearPlan p = plan_linear(qtype, m, n, k, 4);
+    const LinearPlan p = plan_linear(qtype, m, n, k, 4, true);
     if (linear_bf16_fused(p, qtype, m, k)) return p;
     return plan_linear(qtype, m, n, k);
 }

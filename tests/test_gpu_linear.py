@@ -156,6 +156,42 @@ def test_gemv_split_k(splits, monkeypatch, capfd):
                 assert ("splits=2 " if m > 32 else "splits=1 ") in err, err
 
 
+@pytest.mark.parametrize("ks", [2, 4, 8])
+def test_gemv_k_parts(ks, monkeypatch, capfd):
+    """K cut into ks parts inside each MFMA (tiles of 16 / ks channels): INT8 accumulators bit-exact, FP8 within
+    the tolerance, at m = 1 up to 16 / ks tokens, with channels not a multiple of the tile, K parts with a partial
+    last slice, and the bfloat16-activation entry point (the activation quantization inside the kernel)."""
+    monkeypatch.setenv("QR_GEMV_KSUB", str(ks))
+    monkeypatch.setenv("QR_TRACE", "1")
+    shapes = [(1, 1536, 8960), (1, 70, 1664), (min(4, 16 // ks), 100, 2048), (16 // ks, 37, 3584), (1, 3, 128 * ks)]
+    for i, (m, n, k) in enumerate(shapes):
+        for oq in (O.INT8, O.FP8):
+            xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1700 + 10 * i + oq + ks)
+            what = "gemv ksub=%d %s m=%d n=%d k=%d" % (ks, oq, m, n, k)
+            log(what)
+            _check(oq, xc, xs, wc, ws, what)
+            err = capfd.readouterr().err
+            assert "ksub=%d " % ks in err, err
+    # the entry point on bfloat16 activations at m = 1 (quantization inside the kernel)
+    rng = np.random.default_rng(1790 + ks)
+    for oq in (O.INT8, O.FP8):
+        for n, k in ((1536, 8960), (70, 1664)):
+            x = synth.f32_to_bf16_bits(rng.standard_normal((1, k)).astype(np.float32))
+            w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+            wc, ws = O.quantize_rows(w, oq)
+            xc, xs = O.quantize_rows(x, oq, s_mode=O.S_MUL_RECIP)
+            y_ref, acc_i, _ = O.linear(oq, xc, xs, wc, ws, O.BF16)
+            y, acc = qr.qr_w8a8_linear_bf16(GQ[oq], dev(x), dev(wc), dev(ws), acc_out=True)
+            torch.cuda.synchronize()
+            err = capfd.readouterr().err
+            fused = not (oq == O.FP8 and k > 8192)  # the FP8 in-kernel quantization stops at k = 8192
+            assert ("fused=1" in err) == fused, err
+            assert "ksub=%d " % ks in err, err
+            if oq == O.INT8:
+                assert np.array_equal(host(acc), acc_i), (ks, n, k)
+            assert_y_close(host(y), y_ref, "bf16 ksub=%d n=%d k=%d" % (ks, n, k))
+
+
 # every compiled GEMV variant: (token tiles, 64-byte loads per slice, weight tiles per block)
 GEMV_VARIANTS = [(1, 4, 1), (1, 4, 2), (1, 4, 4), (1, 8, 1), (1, 8, 2), (2, 4, 1), (2, 4, 2), (2, 8, 1),
                  (4, 2, 1), (4, 2, 2), (4, 4, 1)]
