@@ -95,7 +95,7 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
     const int j = lane & 15;
     const int g = lane >> 4;
     const int64_t tile0 = (int64_t)blockIdx.x * TB;
-    const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+    const int64_t m0 = (int64_t)blockIdx.y * (KS > 1 ? 16 / KS : 16 * MT);  // first token of this block
     constexpr int64_t kSlice = 64 * U;
     const int64_t slices = (kq + kSlice - 1) / kSlice;
     // split-K across blocks (blockIdx.z): this block's slices [lo, hi); with splits > 1 the raw sums go to
@@ -453,13 +453,13 @@ int gemv_variant_waves(int mt, int u, int tb) {
     return 0;
 }
 
-// the GEMV with K cut into S parts inside the MFMA (one token tile of at most 16 / S tokens, one weight tile of
-// 16 / S channels per workgroup, no K split across workgroups)
+// the GEMV with K cut into S parts inside the MFMA (token blocks of 16 / S tokens, one weight tile of 16 / S
+// channels per workgroup, no K split across workgroups)
 template <int QT, int U, int S, int XM>
 void launch_gemv_ksub_t(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
                         const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, size_t lds,
                         const uint16_t *xb, const float *s, hipStream_t stream) {
-    const dim3 grid((unsigned)p.n_tiles, 1u, 1u);
+    const dim3 grid((unsigned)p.n_tiles, (unsigned)((m + 16 / S - 1) / (16 / S)), 1u);
     hipLaunchKernelGGL((gemv_kernel<QT, 1, U, 1, 16, XM, false, S>), grid, dim3(p.waves * 64), lds, stream, m, n, k, xq,
                        xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, 1, nullptr, xb, s);
 }
@@ -625,6 +625,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
         const int fk = env_int("QR_GEMV_KSUB", 0);
         const bool overrides = fu > 0 || ft > 0 || env_int("QR_GEMV_WAVES", 0) > 0 || env_int("QR_GEMV_SPLITS", 0) > 0;
         int ks = 1;
+        bool blocks_ok = env_int("QR_GEMV_KSUB_BLOCKS", 0) > 0;  // several token blocks of 16 / S tokens
         if (fk == 2 || fk == 4 || fk == 8) {
             ks = fk;
         } else if (fk == 0 && !overrides && m == 1) {
@@ -632,9 +633,15 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
                 ks = p.n_tiles < 256 ? 2 : 1;
             else if (k <= 8960)
                 ks = p.n_tiles < 512 ? 8 : (k >= 2048 ? 4 : 2);
+        } else if (fk == 0 && !overrides && !fused_quant && m > 8 && p.n_tiles < 160 && k <= 8960) {
+            // two token blocks of 8 tokens, K in 2 parts: the weights are read twice (the second time mostly
+            // from cache), which pays only on the fewest tiles (1.5B o at m = 16: 4.8 -> 4.1 us, down 10.2 ->
+            // 9.7, qkv 4.4 -> 4.3; the 7B o and any many-tile linear are slower)
+            ks = 2;
+            blocks_ok = true;
         }
         while (ks > 1 && k % (16 * ks) != 0) ks /= 2;
-        if (ks > 1 && m <= 16 / ks && (u == 4 || u == 8)) {
+        if (ks > 1 && (u == 4 || u == 8) && (m <= 16 / ks || blocks_ok)) {
             p.ksub = ks;
             tb = 1;
             p.n_tiles = (n + 16 / ks - 1) / (16 / ks);

@@ -192,6 +192,23 @@ def test_gemv_k_parts(ks, monkeypatch, capfd):
             assert_y_close(host(y), y_ref, "bf16 ksub=%d n=%d k=%d" % (ks, n, k))
 
 
+@pytest.mark.parametrize("ks", [2, 4, 8])
+def test_gemv_k_parts_token_blocks(ks, monkeypatch, capfd):
+    """K parts with more tokens than one tile holds (16 / ks): token blocks of 16 / ks tokens, each its own row of
+    workgroups; INT8 accumulators bit-exact, FP8 within the tolerance, ragged batches and channels."""
+    monkeypatch.setenv("QR_GEMV_KSUB", str(ks))
+    monkeypatch.setenv("QR_GEMV_KSUB_BLOCKS", "1")
+    monkeypatch.setenv("QR_TRACE", "1")
+    for i, (m, n, k) in enumerate([(16, 1536, 8960), (13, 70, 1664), (5, 37, 3584)]):
+        for oq in (O.INT8, O.FP8):
+            xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1800 + 10 * i + oq + ks)
+            what = "gemv ksub=%d token blocks %s m=%d n=%d k=%d" % (ks, oq, m, n, k)
+            log(what)
+            _check(oq, xc, xs, wc, ws, what)
+            err = capfd.readouterr().err
+            assert "ksub=%d " % ks in err, err
+
+
 # every compiled GEMV variant: (token tiles, 64-byte loads per slice, weight tiles per block)
 GEMV_VARIANTS = [(1, 4, 1), (1, 4, 2), (1, 4, 4), (1, 8, 1), (1, 8, 2), (2, 4, 1), (2, 4, 2), (2, 8, 1),
                  (4, 2, 1), (4, 2, 2), (4, 4, 1)]
