@@ -569,6 +569,16 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
     p.kind = 0;
     p.m_tiles = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
     p.n_tiles = (n + 15) / 16;
+    // token tiles per workgroup: QR_GEMV_MT forces 1, 2 or 4 (fewer tiles: more token blocks, each reading the
+    // weights). Two instead of four pay for 32 < m <= 64 on few tiles with a short K (measured on MI355X: 1.5B
+    // qkv at m = 64 6.4 -> 5.6 us, o 6.4 -> 5.4; the gate/up is slower, the down unchanged)
+    const int fmt = env_int("QR_GEMV_MT", 0);
+    const bool gemv_overrides = env_int("QR_GEMV_UNROLL", 0) > 0 || env_int("QR_GEMV_TILES", 0) > 0 ||
+                                env_int("QR_GEMV_WAVES", 0) > 0 || env_int("QR_GEMV_SPLITS", 0) > 0;
+    if (fmt == 1 || fmt == 2 || fmt == 4)
+        p.m_tiles = fmt;
+    else if (fmt == 0 && !gemv_overrides && p.m_tiles == 4 && p.n_tiles < 160 && k <= 2048)
+        p.m_tiles = 2;
     const int64_t m_blocks = (m + 16 * p.m_tiles - 1) / (16 * p.m_tiles);
     // slices of 256 bytes (128 for four token tiles) unless overridden
     int u = p.m_tiles == 4 ? 2 : 4;
