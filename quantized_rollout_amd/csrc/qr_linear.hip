@@ -593,6 +593,10 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
         const bool few = p.n_tiles < 128;
         if (k >= 1536 && !few) u = 8;
         wave_cap = few ? 8 : 4;
+        // past half a token tile, on very many tiles, two weight tiles per block share each activation slice
+        // (measured on MI355X: 7B gate/up at m = 16 from 34.4 to 32.3 us; the 1.5B gate/up, 1120 tiles, is
+        // slower with two)
+        if (m > 8 && p.n_tiles >= 2048 && gemv_variant_waves(1, u, 2) > 0) tb = 2;
     } else {
         // more tiles per block share each activation load (at m = 64 the activation slices a block reads
         // outweigh its weights); keep at least ~1000 blocks in flight
