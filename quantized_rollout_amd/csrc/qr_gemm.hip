@@ -268,7 +268,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq, const float *__restrict__ xs,
     const uint8_t *__restrict__ wq, const float *__restrict__ ws, void *__restrict__ y, int y_bf16,
     void *__restrict__ acc_out, int tiles_m, int tiles_n, int splits, int stages_per_split,
-    void *__restrict__ partial) {
+    void *__restrict__ partial, int dp_tiles) {
     typedef Ring<BM> R;
     typedef typename Acc32<QT>::type acc_t;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * R::kBuf];  // local stage s in buffer s mod 4
@@ -276,16 +276,40 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     // work item order: each XCD (workgroup id mod 8) takes a contiguous run, split-major then token tiles
     // fastest, so the workgroups that share an operand slice run on one XCD and share its L2
     const int tiles = tiles_m * tiles_n;
-    const int total = tiles * splits;
-    const int per_xcd = (total + 7) / 8;
-    const int order = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (order >= total) return;
-    const int split = order / tiles, tile = order % tiles;
+    const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
+    int split = 0, tile;
+    bool to_partial;
+    if (dp_tiles == 0) {
+        const int total = tiles * splits;
+        const int per_xcd = (total + 7) / 8;
+        const int order = xcd * per_xcd + slot;
+        if (order >= total) return;
+        split = order / tiles;
+        tile = order % tiles;
+        to_partial = splits > 1;
+    } else {
+        // whole-K tiles first: each XCD's first dp_tiles / 8 workgroups, a contiguous run of tiles (whole CU
+        // rounds, dp_tiles being a multiple of the CU count); then the K pieces of the remaining tiles, spread
+        // evenly over the XCDs and dispatched as CUs free up
+        const int dpx = dp_tiles / 8;
+        if (slot < dpx) {
+            tile = xcd * dpx + slot;
+            to_partial = false;
+        } else {
+            const int rem = tiles - dp_tiles, pieces = rem * splits;
+            const int p = xcd * ((pieces + 7) / 8) + (slot - dpx);
+            if (p >= pieces) return;
+            split = p / rem;
+            tile = dp_tiles + p % rem;
+            to_partial = true;
+        }
+    }
     const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
     const int64_t n0 = (int64_t)(tile / tiles_m) * kRingN;
     const int64_t all_stages = (k + kRingK - 1) / kRingK;
-    const int64_t st0 = (int64_t)split * stages_per_split;
-    const int64_t stages = std::min<int64_t>(stages_per_split, all_stages - st0);  // >= 1 by construction
+    const int64_t st0 = to_partial ? (int64_t)split * stages_per_split : 0;
+    const int64_t stages = to_partial ? std::min<int64_t>(stages_per_split, all_stages - st0)  // >= 1 by construction
+                                      : all_stages;
     const int64_t full = k / kRingK;  // stages with every piece inside k
 
     const int t = threadIdx.x;
@@ -399,10 +423,12 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     wait_vmcnt<0>();  // no load may still be writing LDS when the wave ends
 
     const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 64;
-    if (splits > 1) {
-        // split-K: this split's raw accumulators into its slice of the partial sums, [split][m][n]
+    if (to_partial) {
+        // split-K: this split's raw accumulators into its slice of the partial sums, [split][m][nb] over the
+        // split columns n_lo .. n - 1 (all of n unless whole-K tiles come first)
         typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
-        part_t *P = static_cast<part_t *>(partial) + (int64_t)split * m * n;
+        const int64_t n_lo = dp_tiles == 0 ? 0 : (int64_t)(dp_tiles / tiles_m) * kRingN, nb = n - n_lo;
+        part_t *P = static_cast<part_t *>(partial) + (int64_t)split * m * nb;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -411,7 +437,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
-                    if (row < m && col < n) P[row * n + col] = acc[i][j][e];
+                    if (row < m && col < n) P[row * nb + (col - n_lo)] = acc[i][j][e];
                 }
             }
         return;
@@ -497,16 +523,18 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
 }
 
 // Split-K: acc = the partial sums of the splits added in split order (exact for INT32; a fixed order for FP32,
-// so repeated calls agree bit for bit), then the epilogue y = acc * x_scale[row] * w_scale[col]. Four
-// consecutive outputs per thread when n is a multiple of 4, one otherwise.
+// so repeated calls agree bit for bit), then the epilogue y = acc * x_scale[row] * w_scale[col]. The partial
+// sums cover the columns n_lo .. n - 1 ([split][m][nb], nb = n - n_lo). Four consecutive outputs per thread
+// when nb is a multiple of 4, one otherwise.
 template <int QT, int VEC>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n, int splits,
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n, int64_t n_lo, int splits,
                                                             const void *__restrict__ partial,
                                                             const float *__restrict__ xs,
                                                             const float *__restrict__ ws, void *__restrict__ y,
                                                             int y_bf16, void *__restrict__ acc_out) {
     typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
-    const int64_t total = m * n;
+    const int64_t nb = n - n_lo;
+    const int64_t total = m * nb;
     const part_t *P = static_cast<const part_t *>(partial);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x * VEC;
     for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC; base < total; base += stride) {
@@ -523,12 +551,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n
             a[0] = P[base];
             for (int sp = 1; sp < splits; ++sp) a[0] += P[(int64_t)sp * total + base];
         }
-        const int64_t row = base / n;
+        const int64_t row = base / nb, col = n_lo + (base - row * nb);
         const float sx = xs[row];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const int64_t idx = base + e;
-            const float v = acc_to_f32(a[e]) * sx * ws[idx - row * n];
+            const int64_t idx = row * n + col + e;
+            const float v = acc_to_f32(a[e]) * sx * ws[col + e];
             if (y_bf16)
                 static_cast<uint16_t *>(y)[idx] = f32_to_bf16(v);
             else
@@ -543,12 +571,18 @@ hipError_t launch_ring(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const
                        const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
                        hipStream_t stream) {
     const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + kRingN - 1) / kRingN);
-    const int total = tiles_m * tiles_n * g.splits;
-    const int grid = ((total + 7) / 8) * 8;
+    int grid;
+    if (g.dp_tiles == 0) {
+        grid = ((tiles_m * tiles_n * g.splits + 7) / 8) * 8;
+    } else {
+        const int pieces = (tiles_m * tiles_n - g.dp_tiles) * g.splits;
+        grid = 8 * (g.dp_tiles / 8 + (pieces + 7) / 8);
+    }
     hipLaunchKernelGGL((gemm_ring_kernel<QT, BM>), dim3(grid), dim3(Ring<BM>::kThreads), 0, stream, m, n, k, xq, xs,
                        wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits, g.stages_per_split,
-                       workspace);
-    if (g.splits > 1) launch_splitk_reduce(QT, m, n, g.splits, workspace, xs, ws, y, y_bf16, acc_out, stream);
+                       workspace, g.dp_tiles);
+    if (g.splits > 1)
+        launch_splitk_reduce(QT, m, n, g.splits, workspace, xs, ws, y, y_bf16, acc_out, stream, g.n_lo);
     return hipGetLastError();
 }
 
@@ -629,18 +663,50 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
             }
         }
     }
-    g.ws_bytes = g.splits > 1 ? (size_t)g.splits * (size_t)m * (size_t)n * 4 : 0;
+    // Whole rounds of tiles over all of K, then the remaining tiles (a band of output columns) split over K
+    // so that their pieces fill one more round: for tile counts just past a multiple of the CU count (the 7B
+    // gate/up at m = 512: 296 tiles of 256 x 256), where the last round would otherwise run few tiles over all
+    // of K. Needs the round to hold whole columns of tiles (round mod token tiles = 0).
+    const int round = std::max(8, env_int("QR_GEMM_ROUND", 256) / 8 * 8);
+    const int fh = env_int("QR_GEMM_HYB", -1);  // -1 automatic, 0 never, >= 2 that many splits where possible
+    if (fh != 0 && !(fs >= 1)) {
+        for (int bm : {128, 256}) {
+            if ((fbm == 128 || fbm == 256) && fbm != bm) continue;
+            const int64_t tm = (m + bm - 1) / bm, tiles = count(bm, kRingN);
+            if (tiles <= round || round % tm != 0 || tiles % round == 0) continue;
+            const int64_t dp = tiles / round * round, rem = tiles - dp;
+            const int64_t n_lo = dp / tm * kRingN;
+            for (int64_t sp = fh >= 2 ? fh : 2; sp <= (fh >= 2 ? fh : 16); ++sp) {
+                const int64_t sps = (stages + sp - 1) / sp;
+                const int64_t used = (stages + sps - 1) / sps;
+                if (used < 2) break;
+                if (fh < 2 && (sps < 4 || rem * used > round)) continue;
+                const double c = bm == 128 ? 0.65 : 0.83;
+                const double t = (double)(dp / round) * (double)stages * c + (double)((rem * used + round - 1) / round) *
+                                 (double)sps * c + 5.0 + (double)used * (double)m * (double)(n - n_lo) * 8.0 / 5.0e6;
+                if (fh >= 2 || t < best) {
+                    best = fh >= 2 ? -1.0 : t;
+                    g.bm = bm;
+                    g.stages_per_split = (int)sps;
+                    g.splits = (int)used;
+                    g.dp_tiles = (int)dp;
+                    g.n_lo = n_lo;
+                }
+            }
+        }
+    }
+    g.ws_bytes = g.splits > 1 ? (size_t)g.splits * (size_t)m * (size_t)(n - g.n_lo) * 4 : 0;
     return g;
 }
 
 void launch_splitk_reduce(int qtype, int64_t m, int64_t n, int splits, const void *partial, const float *xs,
-                          const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
-    const int64_t total_out = m * n;
-    const bool vec = (n % 4) == 0;
+                          const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream, int64_t n_lo) {
+    const int64_t total_out = m * (n - n_lo);
+    const bool vec = ((n - n_lo) % 4) == 0;
     const int64_t items = vec ? total_out / 4 : total_out;
     const int blocks = (int)std::min<int64_t>((items + 255) / 256, 4096);
 #define QR_REDUCE(QT, V)                                                                                       \
-    hipLaunchKernelGGL((splitk_reduce_kernel<QT, V>), dim3(blocks), dim3(256), 0, stream, m, n, splits, partial, \
+    hipLaunchKernelGGL((splitk_reduce_kernel<QT, V>), dim3(blocks), dim3(256), 0, stream, m, n, n_lo, splits, partial, \
                        xs, ws, y, y_bf16 ? 1 : 0, acc_out)
     if (qtype == kInt8) {
         if (vec) QR_REDUCE(kInt8, 4); else QR_REDUCE(kInt8, 1);

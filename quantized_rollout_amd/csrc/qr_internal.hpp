@@ -28,12 +28,17 @@ struct GemmPlan {
     int bm;                // ring: activation rows per tile (128 or 256)
     int splits;            // ring: K splits (1 = none; else partial sums in the workspace + a reduction)
     int stages_per_split;  // ring: 64-byte K stages per split
-    size_t ws_bytes;       // splits x m x n x 4 when split, else 0
+    int dp_tiles;          // ring: > 0: the first dp_tiles tiles (whole CU rounds) run over all of K and only the
+                           // remaining tiles, a band of output columns from n_lo, are split; 0: every tile alike
+    int64_t n_lo;          // ring: first column of the split band (0 unless dp_tiles > 0)
+    size_t ws_bytes;       // splits x m x (n - n_lo) x 4 when split, else 0
 };
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k);
-// adds splits x [m, n] partial sums (int32 for INT8, fp32 for FP8) in split order, then the epilogue
+// adds splits x [m, n - n_lo] partial sums (int32 for INT8, fp32 for FP8) in split order, then the epilogue
+// into columns n_lo .. n - 1 of y [m, n]
 void launch_splitk_reduce(int qtype, int64_t m, int64_t n, int splits, const void *partial, const float *xs,
-                          const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream);
+                          const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream,
+                          int64_t n_lo = 0);
 hipError_t launch_gemm(const GemmPlan &g, int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *xq,
                        const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                        void *workspace, hipStream_t stream);

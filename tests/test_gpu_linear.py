@@ -276,6 +276,38 @@ def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
             assert np.array_equal(y, y_acc), what
 
 
+# Whole rounds of tiles over all of K first, then the remaining band of output columns split over K: the planner's
+# choice for tile counts just past a whole number of CU rounds, forced here with a round of 8 tiles.
+# (m, n, k, rows per tile, splits, whole-K tiles): 2 x 11 tiles with a ragged 3-tile band and a partial last
+# stage; 2 x 9 tiles with a one-tile band of 253 columns (element-wise reduction) and a one-stage last split;
+# 1 x 9 tiles with 13 splits of 5 stages
+HYB_CASES = [(300, 2600, 1040, 256, 3, 16), (512, 2301, 1040, 256, 5, 16), (100, 2304, 4160, 128, 16, 8)]
+
+
+@pytest.mark.parametrize("m,n,k,bm,splits,dp", HYB_CASES)
+def test_gemm_whole_tiles_then_split_band(m, n, k, bm, splits, dp, monkeypatch, capfd):
+    monkeypatch.setenv("QR_GEMM_ROUND", "8")
+    monkeypatch.setenv("QR_GEMM_HYB", str(splits))
+    monkeypatch.setenv("QR_GEMM_BM", str(bm))
+    monkeypatch.setenv("QR_TRACE", "1")
+    stages = -(-k // 64)
+    sps = -(-stages // splits)
+    used = -(-stages // sps)
+    wsp = qr.Workspace()
+    for oq in (O.INT8, O.FP8):
+        xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1700 + m + oq)
+        what = "gemm band split %s m=%d n=%d k=%d bm=%d splits=%d" % (oq, m, n, k, bm, splits)
+        log(what)
+        _check(oq, xc, xs, wc, ws, what)
+        err = capfd.readouterr().err
+        assert "kind=1" in err and "bm=%d splits=%d dp=%d " % (bm, used, dp) in err, err
+        y_acc, _ = _run(oq, xc, xs, wc, ws)
+        for rep in range(2):  # one workspace object, called again: the same bytes
+            y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(y), y_acc), (what, rep)
+
+
 def test_workspace_reuse_across_plans():
     """One workspace object serves a sequence of differently planned shapes: every call stays bit-exact (INT8)
     or within tolerance (FP8)."""
