@@ -798,7 +798,7 @@ def main():
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no collectives or sharding); --gpus %d is not "
+        print("bench.py: the library runs on one GPU only (no collectives or sharding); --gpus %d is not "
               "supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
