@@ -44,6 +44,10 @@ def lib():
         L.or_e4m3_encode_array.restype = None
         L.or_e4m3_encode_search_array.argtypes = [vp, i64, vp]
         L.or_e4m3_encode_search_array.restype = None
+        L.or_e4m3_encoders_disagree.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp]
+        L.or_e4m3_encoders_disagree.restype = ctypes.c_int64
+        L.or_linear_abs_sum.argtypes = [i32, i64, i64, i64, vp, vp, vp]
+        L.or_linear_abs_sum.restype = ctypes.c_int
         L.or_quantize_rows.argtypes = [vp, i32, i64, i64, vp, i32, i32, vp, vp]
         L.or_quantize_rows.restype = None
         L.or_linear.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -58,7 +62,7 @@ def lib():
         L.or_moe_route.restype = None
         L.or_silu_mul.argtypes = [vp, i64, i64, vp]
         L.or_silu_mul.restype = None
-        L.or_moe_combine.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.or_moe_combine.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp]
         L.or_moe_combine.restype = None
         L.or_quantize_w4.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp]
         L.or_quantize_w4.restype = None
@@ -135,6 +139,45 @@ def quantize_rows(x, qtype, s=None, s_mode=None, in_type=None):
     return codes, scales
 
 
+def host_threads():
+    """Threads for the row-parallel drivers below: the host cores this process may run on."""
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _row_chunks(rows, threads, min_rows=64):
+    n = max(1, min(threads, -(-rows // min_rows)))
+    step = -(-rows // n) if rows else 1
+    return [(r, min(rows, r + step)) for r in range(0, rows, step)]
+
+
+def quantize_rows_threaded(x, qtype, s=None, s_mode=None, in_type=None, threads=None):
+    """quantize_rows on row chunks in parallel threads (rows are quantized independently, so the result is the
+    same bytes; ctypes releases the GIL during the C call). Returns (codes, scales)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    if in_type is None:
+        in_type = BF16 if np.asarray(x).dtype == np.uint16 else F32
+    x = _c(x, np.uint16 if in_type == BF16 else np.float32)
+    rows, k = x.shape
+    if s is None:
+        s_mode = S_NONE
+    else:
+        s = _c(s, np.float32)
+        if s_mode is None:
+            s_mode = S_MUL
+    codes = np.empty((rows, k), np.uint8)
+    scales = np.empty((rows,), np.float32)
+    L = lib()
+
+    def run(r):
+        a, b = r
+        L.or_quantize_rows(_p(x[a:b]), in_type, b - a, k, _p(s), s_mode, qtype, _p(codes[a:b]), _p(scales[a:b]))
+
+    with ThreadPoolExecutor(max_workers=threads or host_threads()) as pool:
+        list(pool.map(run, _row_chunks(rows, threads or host_threads())))
+    return codes, scales
+
+
 def linear(qtype, x_codes, x_scales, w_codes, w_scales, y_type=BF16):
     """Returns (y, acc_i32 or None, acc_f64). y is uint16 bfloat16 bits or float32."""
     x_codes, w_codes = _c(x_codes, np.uint8), _c(w_codes, np.uint8)
@@ -152,6 +195,27 @@ def linear(qtype, x_codes, x_scales, w_codes, w_scales, y_type=BF16):
     return y, acc_i32, acc_f64
 
 
+def linear_abs_sum(qtype, x_codes, w_codes):
+    """[m, n] exact sums of |x_j w_j| over the decoded codes: the scale of the fp32 summation bound of an FP8
+    accumulator, |acc_fp32 - acc_exact| <= gamma_k * abs_sum (gamma_k = k u / (1 - k u), u = 2^-24)."""
+    x_codes, w_codes = _c(x_codes, np.uint8), _c(w_codes, np.uint8)
+    m, k = x_codes.shape
+    n, k2 = w_codes.shape
+    assert k == k2
+    out = np.empty((m, n), np.float64)
+    if lib().or_linear_abs_sum(qtype, m, n, k, _p(x_codes), _p(w_codes), _p(out)) != 0:
+        raise ValueError("oracle abs sum: k too large for exact accumulation")
+    return out
+
+
+def e4m3_encoders_disagree(lo, hi):
+    """(count, first) of the fp32 bit patterns in [lo, hi) (clamped to +-448, NaN skipped) on which the two
+    oracle encoders differ."""
+    first = ctypes.c_uint32(0)
+    n = lib().or_e4m3_encoders_disagree(lo, hi, ctypes.byref(first))
+    return int(n), int(first.value)
+
+
 def grouped_linear(qtype, expert_offsets, row_ids, x_codes, x_scales, w_codes, w_scales, y_type=BF16):
     x_codes, w_codes = _c(x_codes, np.uint8), _c(w_codes, np.uint8)
     x_scales, w_scales = _c(x_scales, np.float32), _c(w_scales, np.float32)
@@ -167,6 +231,24 @@ def grouped_linear(qtype, expert_offsets, row_ids, x_codes, x_scales, w_codes, w
     if rc != 0:
         raise ValueError("oracle grouped linear: inconsistent token lists")
     return y
+
+
+def linear_threaded(qtype, x_codes, x_scales, w_codes, w_scales, y_type=BF16, threads=None):
+    """linear on chunks of output channels (weight rows) in parallel threads: every output is the same plain
+    dot product, so the result is the same. Returns (y, acc_i32 or None, acc_f64)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    x_codes, w_codes = _c(x_codes, np.uint8), _c(w_codes, np.uint8)
+    x_scales, w_scales = _c(x_scales, np.float32), _c(w_scales, np.float32)
+    n = w_codes.shape[0]
+    parts = _row_chunks(n, threads or host_threads(), min_rows=16)
+    with ThreadPoolExecutor(max_workers=threads or host_threads()) as pool:
+        res = list(pool.map(lambda r: linear(qtype, x_codes, x_scales, w_codes[r[0]:r[1]], w_scales[r[0]:r[1]],
+                                             y_type), parts))
+    y = np.concatenate([r[0] for r in res], axis=1)
+    acc_i = None if qtype != INT8 else np.concatenate([r[1] for r in res], axis=1)
+    acc_f = np.concatenate([r[2] for r in res], axis=1)
+    return y, acc_i, acc_f
 
 
 def count_code_changes(a, b, qtype, sa=None, sb=None):
@@ -205,13 +287,14 @@ def silu_mul(y_gu):
 
 
 def moe_combine(y_down, topk_weight, pair_rows):
-    """out [T, H] = bf16(sum_j topk_weight[t,j] y_down[pair_rows[t,j]]) (y_down bfloat16 bits [R, H])."""
+    """out [T, H] = bf16(sum_j topk_weight[t,j] y_down[pair_rows[t,j]]) (y_down bfloat16 bits [R, H]); a pair
+    row outside [0, R) adds nothing."""
     y_down = _c(y_down, np.uint16)
     topk_weight, pair_rows = _c(topk_weight, np.float32), _c(pair_rows, np.int32)
     T, k = pair_rows.shape
-    H = y_down.shape[1]
+    R, H = y_down.shape
     out = np.empty((T, H), np.uint16)
-    lib().or_moe_combine(_p(y_down), _p(topk_weight), _p(pair_rows), T, k, H, _p(out))
+    lib().or_moe_combine(_p(y_down), R, _p(topk_weight), _p(pair_rows), T, k, H, _p(out))
     return out
 
 

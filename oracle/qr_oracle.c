@@ -126,6 +126,26 @@ uint8_t or_e4m3_encode_search(float v) {
     return (uint8_t)(sign | ((lo % 2 == 0) ? lo : hi));
 }
 
+/* Agreement of the two encoders over the fp32 bit patterns u in [lo, hi): each finite pattern is clamped to
+ * [-448, 448] as the quantizers do, then encoded both ways; NaN patterns are skipped (they never reach an
+ * encoder). Returns the number of patterns on which they differ and stores the first in *first_bad. */
+int64_t or_e4m3_encoders_disagree(uint32_t lo, uint32_t hi, uint32_t *first_bad) {
+    int64_t bad = 0;
+    uint32_t u;
+    for (u = lo; u < hi; ++u) {
+        float v;
+        memcpy(&v, &u, sizeof v);
+        if (isnan(v)) continue;
+        if (v > 448.0f) v = 448.0f;
+        if (v < -448.0f) v = -448.0f;
+        if (or_e4m3_encode(v) != or_e4m3_encode_search(v)) {
+            if (bad == 0 && first_bad) *first_bad = u;
+            bad++;
+        }
+    }
+    return bad;
+}
+
 void or_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
     int64_t i;
     for (i = 0; i < n; ++i) out[i] = or_e4m3_encode(v[i]);
@@ -262,6 +282,36 @@ int or_linear(int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *x_codes
     return 0;
 }
 
+/* abs_f64[i,c] = sum_j |xq[i,j] * wq[c,j]| with the codes decoded (INT8: integers; FP8: multiples of 2^-9),
+ * exact: the sum of the magnitudes of the products whose sum is the accumulator. An fp32 sum of those products
+ * in any order is within gamma_k * abs_f64 of the exact accumulator (gamma_k = k u / (1 - k u), u = 2^-24;
+ * Higham, Accuracy and Stability of Numerical Algorithms, ch. 3), the bound that gates FP8 accumulators.
+ * Returns 0, or -1 when the sizes could overflow the exact sums. */
+int or_linear_abs_sum(int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *x_codes, const uint8_t *w_codes,
+                      double *abs_f64) {
+    int64_t i, c, j;
+    if (qtype == OR_INT8 && k > 133143) return -1;
+    if (qtype == OR_FP8 && k > 171196) return -1;
+    for (i = 0; i < m; ++i)
+        for (c = 0; c < n; ++c) {
+            int64_t units = 0;
+            const uint8_t *xr = x_codes + i * k, *wr = w_codes + c * k;
+            for (j = 0; j < k; ++j) {
+                int64_t a, b;
+                if (qtype == OR_INT8) {
+                    a = (int64_t)(int8_t)xr[j];
+                    b = (int64_t)(int8_t)wr[j];
+                } else {
+                    a = (int64_t)or_e4m3_decode_units(xr[j]);
+                    b = (int64_t)or_e4m3_decode_units(wr[j]);
+                }
+                units += (a < 0 ? -a : a) * (b < 0 ? -b : b);
+            }
+            abs_f64[i * n + c] = (qtype == OR_INT8) ? (double)units : ldexp((double)units, -18);
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------------------------
  * a4: grouped (MoE) linear
  * ---------------------------------------------------------------------------------------------------- */
@@ -388,15 +438,19 @@ void or_silu_mul(const uint16_t *y_gu, int64_t R, int64_t I, uint16_t *h) {
 }
 
 /* out[t][c] = bf16(sum_j topk_weight[t][j] * y_down[pair_rows[t][j]][c]) in double, the routing-weighted
- * combine of token t's k expert outputs. */
-void or_moe_combine(const uint16_t *y_down, const float *topk_weight, const int32_t *pair_rows, int64_t T,
-                    int64_t k, int64_t H, uint16_t *out) {
+ * combine of token t's k expert outputs (j = 0 .. k-1 in order). y_down holds R rows; a pair row outside
+ * [0, R) adds nothing (the pages give no combine: the library's contract for an inconsistent pair list). */
+void or_moe_combine(const uint16_t *y_down, int64_t R, const float *topk_weight, const int32_t *pair_rows,
+                    int64_t T, int64_t k, int64_t H, uint16_t *out) {
     int64_t t, j, c;
     for (t = 0; t < T; ++t)
         for (c = 0; c < H; ++c) {
             double acc = 0.0;
-            for (j = 0; j < k; ++j)
-                acc += (double)topk_weight[t * k + j] * (double)or_bf16_to_f32(y_down[pair_rows[t * k + j] * H + c]);
+            for (j = 0; j < k; ++j) {
+                const int64_t row = pair_rows[t * k + j];
+                if (row < 0 || row >= R) continue;
+                acc += (double)topk_weight[t * k + j] * (double)or_bf16_to_f32(y_down[row * H + c]);
+            }
             out[t * H + c] = or_round_to_bf16(acc);
         }
 }

@@ -49,6 +49,8 @@ int32_t  or_e4m3_decode_units(uint8_t c); /* value / 2^-9 as an exact integer (f
 uint16_t or_round_to_bf16(double v);      /* one rounding, to nearest even, to bfloat16 bits    */
 void     or_e4m3_encode_array(const float *v, int64_t n, uint8_t *out);
 void     or_e4m3_encode_search_array(const float *v, int64_t n, uint8_t *out);
+/* patterns in [lo, hi) (clamped to +-448, NaN skipped) on which the two encoders differ; the first in *first_bad */
+int64_t  or_e4m3_encoders_disagree(uint32_t lo, uint32_t hi, uint32_t *first_bad);
 
 /* ---- the four steps of the path -------------------------------------------------------------------- */
 /* One absmax scale per row (a weight row = output channel, an activation row = token). */
@@ -61,6 +63,10 @@ void or_quantize_rows(const void *in, int in_type, int64_t rows, int64_t k, cons
 int or_linear(int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *x_codes, const float *x_scales,
               const uint8_t *w_codes, const float *w_scales, int y_type, void *y, int32_t *acc_i32,
               double *acc_f64);
+
+/* abs_f64: [m,n] exact sums of |x_j w_j| over the decoded codes (the scale of the fp32 summation bound). */
+int or_linear_abs_sum(int qtype, int64_t m, int64_t n, int64_t k, const uint8_t *x_codes, const uint8_t *w_codes,
+                      double *abs_f64);
 
 /* Grouped (MoE) linear over CSR token lists: for expert e and j in [off[e], off[e+1]), output row j uses
  * activation row row_ids[j] (or j when row_ids is NULL) and expert e's weights w_codes[e] / w_scales[e]. */
@@ -75,12 +81,12 @@ void or_count_code_changes(const uint8_t *a, const uint8_t *b, int64_t count, in
 
 /* next row: MoE glue. Routing (top-k by logit, ties to the lower expert; softmax weights over the k logits;
  * CSR rows by expert then token), h = bf16(silu(g) u) over gate/up rows [g | u], and the routing-weighted
- * combine out[t] = bf16(sum_j w[t][j] y_down[pair_rows[t][j]]). */
+ * combine out[t] = bf16(sum_j w[t][j] y_down[pair_rows[t][j]]) over the pair rows inside [0, R). */
 void or_moe_route(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_expert, float *topk_weight,
                   int32_t *offsets, int32_t *row_ids, float *row_weights, int32_t *pair_rows);
 void or_silu_mul(const uint16_t *y_gu, int64_t R, int64_t I, uint16_t *h);
-void or_moe_combine(const uint16_t *y_down, const float *topk_weight, const int32_t *pair_rows, int64_t T,
-                    int64_t k, int64_t H, uint16_t *out);
+void or_moe_combine(const uint16_t *y_down, int64_t R, const float *topk_weight, const int32_t *pair_rows,
+                    int64_t T, int64_t k, int64_t H, uint16_t *out);
 
 /* next row: one publish of W + dW: the a1 quantizer, then per row the a5 triple against the previous
  * publish (row_counts [rows][3]: bytes, values, scale changed) and its sums in out3 */

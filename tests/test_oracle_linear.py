@@ -173,3 +173,40 @@ def test_count_code_changes(qtype):
     z = np.array([0x00, 0x80, 0x38, 0x38], np.uint8)
     z2 = np.array([0x80, 0x00, 0x38, 0xB8], np.uint8)
     assert list(O.count_code_changes(z, z2, O.FP8)) == [3, 1, 0]
+
+
+@pytest.mark.parametrize("qtype", QT)
+def test_abs_sum_matches_brute_force(qtype):
+    """The sum of |x_j w_j| (the scale of the fp32 summation bound that gates FP8 accumulators) against exact
+    rational arithmetic over every code byte, on tiny random inputs."""
+    rng = np.random.default_rng(90 + qtype)
+    for m, n, k in ((1, 1, 16), (3, 4, 32), (2, 5, 48)):
+        if qtype == O.INT8:
+            x = _codes_int8(rng.integers(-127, 128, (m, k)))
+            w = _codes_int8(rng.integers(-127, 128, (n, k)))
+        else:
+            x = rng.integers(0, 256, (m, k)).astype(np.uint8)
+            w = rng.integers(0, 256, (n, k)).astype(np.uint8)
+            x[(x & 0x7F) == 0x7F] = 0x01  # no NaN codes
+            w[(w & 0x7F) == 0x7F] = 0x81
+        got = O.linear_abs_sum(qtype, x, w)
+        for i in range(m):
+            for c in range(n):
+                want = sum(abs(brute.code_value(int(x[i, j]), qtype) * brute.code_value(int(w[c, j]), qtype))
+                           for j in range(k))
+                assert Fraction(float(got[i, c])) == want, (m, n, k, i, c)
+
+
+@pytest.mark.parametrize("qtype", QT)
+def test_abs_sum_closed_forms(qtype):
+    """Equal to |acc| when every product has one sign (all-max rows: 127^2 k or 448^2 k); at least |acc| and
+    strictly more when signs mix (alternating signs: acc = 0, abs sum = qmax^2 k)."""
+    k = 256
+    hi, lo = (0x7F, 0x81) if qtype == O.INT8 else (0x7E, 0xFE)  # +qmax, -qmax
+    q2 = 127 * 127 if qtype == O.INT8 else 448 * 448
+    x = np.stack([np.full(k, hi, np.uint8), np.array([hi if j % 2 == 0 else lo for j in range(k)], np.uint8)])
+    w = np.full((1, k), lo, np.uint8)
+    a = O.linear_abs_sum(qtype, x, w)
+    _, _, acc = O.linear(qtype, x, np.ones(2, np.float32), w, np.ones(1, np.float32), O.F32)
+    assert a[0, 0] == q2 * k and acc[0, 0] == -q2 * k
+    assert a[1, 0] == q2 * k and acc[1, 0] == 0

@@ -81,3 +81,58 @@ def test_combine_single_routes_and_equal_rows():
     y2 = np.concatenate([y[:1], y[:1]])
     out2 = O.moe_combine(y2, np.array([[0.25, 0.75]], np.float32), np.array([[0, 1]], np.int32))
     assert np.array_equal(out2[0], y[0])
+
+
+# A hand-worked combine: T = 2 tokens, k = 3 choices, H = 4 channels, six distinct expert-output rows and
+# distinct weights. Every value and weight is dyadic, so each sum is exact and its bfloat16 bits are written
+# out by hand below.
+_Y_ROWS = np.array([[1, 2, -4, 8],          # row 0
+                    [16, -1, 0.5, 3],       # row 1
+                    [-2, 6, 10, 0.25],      # row 2
+                    [4, -8, 2, 1],          # row 3
+                    [0, 1, -3, 12],         # row 4
+                    [-6, 0.5, 7, -1]],      # row 5
+                   np.float32)
+_PAIR_ROWS = np.array([[3, 0, 5], [1, 4, 2]], np.int32)          # [t][j]
+_WEIGHTS = np.array([[0.5, 0.25, 0.25], [0.125, 0.375, 0.5]], np.float32)
+# token 0: 0.5 row3 + 0.25 row0 + 0.25 row5 = [0.75, -3.375, 1.75, 2.25]
+# token 1: 0.125 row1 + 0.375 row4 + 0.5 row2 = [1, 3.25, 3.9375, 5]
+_EXPECTED_BITS = np.array([[0x3F40, 0xC058, 0x3FE0, 0x4010],
+                           [0x3F80, 0x4050, 0x407C, 0x40A0]], np.uint16)
+
+
+def test_combine_hand_worked_two_tokens_three_choices():
+    out = O.moe_combine(_bf16_bits(_Y_ROWS), _WEIGHTS, _PAIR_ROWS)
+    assert np.array_equal(out, _EXPECTED_BITS), [[hex(v) for v in r] for r in out]
+
+
+def test_combine_pairs_each_weight_with_its_own_row():
+    """Swapping two pair rows of token 0 (weights unchanged) changes its output to the hand value
+    0.5 row0 + 0.25 row3 + 0.25 row5 = [0, -0.875, 0.25, 4]; token 1 is untouched. A layout slip ([j][t]
+    instead of [t][j]) or a weight paired with another choice's row would give neither expected output."""
+    pr = _PAIR_ROWS.copy()
+    pr[0, 0], pr[0, 1] = pr[0, 1], pr[0, 0]
+    out = O.moe_combine(_bf16_bits(_Y_ROWS), _WEIGHTS, pr)
+    assert np.array_equal(out[0], np.array([0x0000, 0xBF60, 0x3E80, 0x4080], np.uint16)), [hex(v) for v in out[0]]
+    assert np.array_equal(out[1], _EXPECTED_BITS[1])
+    # the [j][t] reading of the same buffer pairs token 0's weights with rows 3, 0, 5 of another shape
+    wrong = O.moe_combine(_bf16_bits(_Y_ROWS), _WEIGHTS, _PAIR_ROWS.T.copy().reshape(2, 3))
+    assert not np.array_equal(wrong, _EXPECTED_BITS)
+
+
+def test_combine_rounds_once():
+    """1 + 2^-8 + 2^-20 rounds once to bfloat16 1 + 2^-7 (0x3F81); rounding the partial sum 1 + 2^-8 first
+    (a tie, to even: 1.0) would give 0x3F80."""
+    y = _bf16_bits(np.array([[2.0], [2.0 ** -6], [2.0 ** -18]], np.float32))
+    out = O.moe_combine(y, np.array([[0.5, 0.25, 0.25]], np.float32), np.array([[0, 1, 2]], np.int32))
+    assert out[0, 0] == 0x3F81
+
+
+def test_combine_skips_pair_rows_outside_the_rows():
+    """A pair row outside [0, R) adds nothing (the library's contract for an inconsistent pair list)."""
+    pr = _PAIR_ROWS.copy()
+    pr[1, 1] = 6      # past the last row: token 1 loses 0.375 row4 -> [1, 2.875, 5.0625, 0.5]
+    pr[0, 2] = -1     # token 0 loses 0.25 row5 -> [2.25, -3.5, 0, 2.5]
+    out = O.moe_combine(_bf16_bits(_Y_ROWS), _WEIGHTS, pr)
+    assert np.array_equal(out, np.array([[0x4010, 0xC060, 0x0000, 0x4020],
+                                         [0x3F80, 0x4038, 0x40A2, 0x3F00]], np.uint16)), out

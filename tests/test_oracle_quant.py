@@ -195,18 +195,52 @@ def test_power_of_two_invariant_scale_is_exact(qtype):
         assert np.array_equal(cx, c0) and np.array_equal(sx, (s0 * np.float32(2.0 ** -j)))
 
 
-def test_unquantized_product_invariant_under_transform():
-    """X W^T = (X diag(1/s)) (W diag(s))^T exactly (QuRL section 4.3), in rational arithmetic."""
+def _transform_bound_check(qtype, X, W, s_w, s_x):
+    """The oracle's quantized product of X diag(1/s_x) and W diag(s_w) against the exact X W^T: returns the
+    largest |y - (X W^T)[i,c]| / bound over all outputs, where bound is the closed-form quantization error of
+    the transformed operands (P3 per element, plus the fp32 rounding of the transformed values)."""
+    xc, xs = O.quantize_rows(X, qtype, s=s_x, s_mode=O.S_MUL_RECIP)
+    wc, ws = O.quantize_rows(W, qtype, s=s_w, s_mode=O.S_MUL)
+    _, _, acc = O.linear(qtype, xc, xs, wc, ws, O.F32)
+    xp = X.astype(np.float64) / s_x.astype(np.float64)   # the exact transformed operands
+    wp = W.astype(np.float64) * s_w.astype(np.float64)
+
+    def delta(v, S):
+        if qtype == O.INT8:
+            return np.full_like(v, 0.5) * S[:, None]
+        return np.maximum(np.abs(v / S[:, None]) * 2.0 ** -4, 2.0 ** -10) * S[:, None]
+
+    dx, dw = delta(xp, xs.astype(np.float64)), delta(wp, ws.astype(np.float64))
+    worst = 0.0
+    for i in range(X.shape[0]):
+        for c in range(W.shape[0]):
+            exact = sum(Fraction(float(X[i, j])) * Fraction(float(W[c, j])) for j in range(X.shape[1]))
+            y = Fraction(float(acc[i, c])) * Fraction(float(xs[i])) * Fraction(float(ws[c]))
+            bound = float(np.sum(np.abs(xp[i]) * dw[c] + np.abs(wp[c]) * dx[i] + dx[i] * dw[c]))
+            bound += float(np.sum(np.abs(xp[i] * wp[c]))) * 2.0 ** -21  # fp32 rounding of x / s and w s
+            worst = max(worst, abs(float(y - exact)) / bound)
+    return worst
+
+
+@pytest.mark.parametrize("qtype", QT)
+def test_unquantized_product_invariant_under_transform(qtype):
+    """X W^T = (X diag(1/s)) (W diag(s))^T exactly (QuRL section 4.3), in rational arithmetic; and the oracle's
+    quantized product with the transform folded into both quantizers stays within the closed-form quantization
+    error of the transformed operands from that exact product. The same s on the wrong side (W diag(1/s)) is far
+    outside the bound."""
     rng = np.random.default_rng(7)
-    X = rng.standard_normal((3, 5)).astype(np.float32)
-    W = rng.standard_normal((4, 5)).astype(np.float32)
-    s = rng.uniform(0.5, 2, 5).astype(np.float32)
+    X = rng.standard_normal((3, 32)).astype(np.float32)
+    X[:, 5] *= np.float32(20)
+    W = (rng.standard_normal((4, 32)) * 0.02).astype(np.float32)
+    s = rng.uniform(0.5, 2, 32).astype(np.float32)
     for i in range(3):
         for c in range(4):
-            lhs = sum(Fraction(float(X[i, j])) * Fraction(float(W[c, j])) for j in range(5))
+            lhs = sum(Fraction(float(X[i, j])) * Fraction(float(W[c, j])) for j in range(32))
             rhs = sum((Fraction(float(X[i, j])) / Fraction(float(s[j]))) *
-                      (Fraction(float(W[c, j])) * Fraction(float(s[j]))) for j in range(5))
+                      (Fraction(float(W[c, j])) * Fraction(float(s[j]))) for j in range(32))
             assert lhs == rhs
+    assert _transform_bound_check(qtype, X, W, s, s) <= 1.0
+    assert _transform_bound_check(qtype, X, W, (1.0 / s).astype(np.float32), s) > 1.0
 
 
 def test_int8_range_is_symmetric():
