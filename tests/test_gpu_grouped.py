@@ -7,7 +7,8 @@ import quantized_rollout_amd as qr
 from oracle import core as O
 from quantized_rollout_amd import synth
 
-from gpu_util import assert_y_close, dev, host, log
+from gpu_util import (QT_NAMES, assert_codes_equal, assert_grouped_within_bound, assert_scales_equal,
+                      assert_y_close, assert_y_within_bound, dev, grouped_exact, host, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +39,7 @@ def test_grouped_parity_small(oq, gq):
     y = qr.qr_w8a8_grouped_linear(gq, dev(off), dev(rows), rows.size, dev(xc), dev(xs), dev(wc), dev(ws))
     torch.cuda.synchronize()
     assert_y_close(host(y), y_ref, "grouped small")
+    assert_grouped_within_bound(host(y), oq, off, rows, xc, xs, wc, ws, "grouped small")
     # INT8: outputs come from exact accumulators, so per-expert rows equal the plain linear's bitwise
     if oq == O.INT8:
         for e in range(E):
@@ -62,6 +64,13 @@ def test_grouped_identity_rows_and_many_rows_per_expert(oq, gq):
     y = qr.qr_w8a8_grouped_linear(gq, dev(off), None, total, dev(xc), dev(xs), dev(wc), dev(ws))
     torch.cuda.synchronize()
     assert_y_close(host(y), y_ref, "grouped identity")
+    assert_grouped_within_bound(host(y), oq, off, None, xc, xs, wc, ws, "grouped identity")
+
+
+def _assert_rows_within_bound(y, keep, oq, off, rows, xc, xs, wc, ws, what):
+    """The element-wise bound on the rows marked in keep (the others are checked by the caller)."""
+    acc, bnd, xw = grouped_exact(oq, off, rows, xc, xs, wc, ws)
+    assert_y_within_bound(y[keep], acc[keep], None, None, None if bnd is None else bnd[keep], what, xw=xw[keep])
 
 
 # every compiled grouped variant: (64-byte steps per K slice, 16-channel tiles per block)
@@ -100,6 +109,9 @@ def test_every_grouped_variant(u, tb, waves, monkeypatch):
         assert not y[20].any()
         y_ref[20] = 0
         assert_y_close(y, y_ref, "grouped variant u=%d tb=%d" % (u, tb))
+        keep = np.ones(total, bool)
+        keep[20] = False  # the out-of-range row is checked above (zeros)
+        _assert_rows_within_bound(y, keep, oq, off, rows, xc, xs, wc, ws, "grouped variant u=%d tb=%d" % (u, tb))
 
 
 def test_grouped_full_size_qwen3_moe_fp8_sampled():
@@ -124,6 +136,8 @@ def test_grouped_full_size_qwen3_moe_fp8_sampled():
         cols = np.sort(rng.choice(n, 16, replace=False))
         y_ref = O.grouped_linear(O.FP8, inp.expert_offsets, rows, acts, scales, wc[:, cols], ws[:, cols])
         assert_y_close(host(y)[:, cols], y_ref, "moe " + name)
+        assert_grouped_within_bound(host(y)[:, cols], O.FP8, inp.expert_offsets, rows, acts, scales, wc[:, cols],
+                                    ws[:, cols], "moe " + name)
 
 
 @pytest.mark.parametrize("oq,gq", QT)
@@ -151,20 +165,48 @@ def test_count_code_changes_parity(oq, gq):
         assert list(host(got)) == list(ref)
 
 
+@pytest.fixture(scope="module")
+def requant_7b():
+    """Config 4 inputs: the four 7B-shaped linears' fp32 masters W ~ N(0, 0.02), W2 = fl32(W + dW) with
+    dW ~ N(0, 1e-5), and per-input-channel s ~ U(0.5, 2) (seed 0)."""
+    log("generating the 7B requantization inputs (fp32 W, W + dW, s)")
+    return synth.make_requant()
+
+
 @pytest.mark.parametrize("oq,gq", QT)
-def test_requant_full_size_on_gpu_matches_oracle_counts(oq, gq):
-    """The weight publish between RL steps on one 7B linear (o-proj, 3584x3584, fp32 masters): quantize W
-    and W + dW on the GPU, count changed codes on the GPU; the oracle does the same from the same inputs."""
-    inp = synth.make_requant(linears=["o"])
-    w, w2, s = inp.w["o"], inp.w2["o"], inp.s["o"]
-    for with_s in (False, True):
-        sd = dev(s) if with_s else None
-        a, sa = qr.qr_quantize_weights(dev(w), gq, s=sd)
-        b, sb = qr.qr_quantize_weights(dev(w2), gq, s=sd)
-        got = qr.qr_count_code_changes(a, b, gq, sa, sb)
-        torch.cuda.synchronize()
-        ra, rsa = O.quantize_rows(w, oq, s=s if with_s else None)
-        rb, rsb = O.quantize_rows(w2, oq, s=s if with_s else None)
-        ref = O.count_code_changes(ra, rb, oq, rsa, rsb)
-        log("requant o %s s=%s changed bytes %d of %d" % (oq, with_s, ref[0], w.size))
-        assert list(host(got)) == list(ref)
+def test_requant_full_size_7b_all_linears(oq, gq, requant_7b):
+    """The weight publish between RL steps on all four 7B linears at full size (qkv 4608x3584, o 3584x3584,
+    gate/up 37888x3584, down 3584x18944; fp32 masters), with and without s: every code byte and scale of W and
+    W + dW quantized on the GPU equals the oracle's, the changed-code triple counted on the GPU equals the
+    oracle's over the whole tensor, and the fused requantize + diff publishes the same codes and triple."""
+    inp = requant_7b
+    for name in ("qkv", "o", "gate_up", "down"):
+        w, w2, s = inp.w[name], inp.w2[name], inp.s[name]
+        wd, w2d = dev(w), dev(w2)
+        for with_s in (False, True):
+            what = "requant 7b %s %s s=%s n=%d k=%d" % (name, QT_NAMES[oq], with_s, w.shape[0], w.shape[1])
+            log(what)
+            sd = dev(s) if with_s else None
+            a, sa = qr.qr_quantize_weights(wd, gq, s=sd)
+            b, sb = qr.qr_quantize_weights(w2d, gq, s=sd)
+            got = qr.qr_count_code_changes(a, b, gq, sa, sb)
+            c, sc, rc, o3 = qr.qr_requantize_weights(w2d, gq, a, sa, s=sd)
+            torch.cuda.synchronize()
+            ra, rsa = O.quantize_rows_threaded(w, oq, s=s if with_s else None)
+            rb, rsb = O.quantize_rows_threaded(w2, oq, s=s if with_s else None)
+            assert_codes_equal(host(a), ra, what + " codes of W")
+            assert_scales_equal(host(sa), rsa, what + " scales of W")
+            assert_codes_equal(host(b), rb, what + " codes of W + dW")
+            assert_scales_equal(host(sb), rsb, what + " scales of W + dW")
+            ref = O.count_code_changes(ra, rb, oq, rsa, rsb)
+            log("  changed: %d bytes, %d values, %d scales of %d codes (%.4f%%)"
+                % (ref[0], ref[1], ref[2], w.size, 100.0 * ref[0] / w.size))
+            assert list(host(got)) == list(ref), (what, host(got), ref)
+            assert list(host(o3)) == list(ref), (what, host(o3), ref)
+            assert torch.equal(c, b) and torch.equal(sc, sb), what
+            assert 0 < ref[0] < w.size
+            del a, b, c, sa, sb, sc, rc
+        del wd, w2d
+        torch.cuda.empty_cache()
+
+

@@ -210,3 +210,44 @@ def test_abs_sum_closed_forms(qtype):
     _, _, acc = O.linear(qtype, x, np.ones(2, np.float32), w, np.ones(1, np.float32), O.F32)
     assert a[0, 0] == q2 * k and acc[0, 0] == -q2 * k
     assert a[1, 0] == q2 * k and acc[1, 0] == 0
+
+
+def _pow2_code(e, neg=False):
+    c = ((e + 7) << 3) if e >= -6 else (1 << (e + 9))
+    return c | (0x80 if neg else 0)
+
+
+def test_fp8_mfma_truncation_tolerance():
+    """The tolerance of FP8 accumulators on the matrix cores (measured on gfx950: products added inside one
+    instruction are aligned to the largest exponent sum and truncated 13 bits below it): cases the probes of the
+    hardware fixed, and the bound's own invariants."""
+    k = 512
+
+    def row(entries):
+        a = np.zeros((1, k), np.uint8)
+        b = np.zeros((1, k), np.uint8)
+        for j, ea, eb, neg in entries:
+            a[0, j], b[0, j] = _pow2_code(ea, neg), _pow2_code(eb)
+        return a, b
+
+    T = lambda e: O.fp8_mfma_truncation(*row(e))[0, 0]  # noqa: E731
+    assert T([(0, 4, 4, False)]) == 0.0                                   # one product: exact
+    assert T([(0, 4, 4, False), (1, -5, -5, False)]) == 2.0 ** -10        # 2^8 + 2^-10: dropped (probe: lost)
+    assert T([(0, 4, 4, False), (1, -5, -5, True)]) == 2.0 ** -10         # the same below zero
+    assert T([(0, 4, 4, False), (1, -2, -3, False)]) == 0.0               # 2^-5 = 13 below 2^8: kept (probe: kept)
+    assert T([(0, 4, 4, False), (1, -3, -3, False)]) == 2.0 ** -6         # 2^-6: dropped (probe: lost)
+    assert T([(0, 4, 4, False), (500, -5, -5, False)]) == 0.0             # far apart: never in one instruction
+    # 2^8 with fifteen 2^-6 after it: at most all fifteen dropped (probe: the seven in its 8-block were)
+    assert T([(0, 4, 4, False)] + [(j, -3, -3, False) for j in range(1, 16)]) == 15 * 2.0 ** -6
+    # all-448 rows: every product on the grid, the accumulator exact (the closed form checked on the GPU)
+    x = np.full((2, k), 0x7E, np.uint8)
+    w = np.full((3, k), 0xFE, np.uint8)
+    assert not O.fp8_mfma_truncation(x, w).any()
+    # random codes: 0 <= T <= sum |p|
+    rng = np.random.default_rng(95)
+    x = rng.integers(0, 256, (4, 1040)).astype(np.uint8)
+    w = rng.integers(0, 256, (5, 1040)).astype(np.uint8)
+    x[(x & 0x7F) == 0x7F] = 0x38
+    w[(w & 0x7F) == 0x7F] = 0x38
+    t = O.fp8_mfma_truncation(x, w)
+    assert (t >= 0).all() and (t <= O.linear_abs_sum(O.FP8, x, w)).all() and t.max() > 0
