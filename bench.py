@@ -1,36 +1,38 @@
 #!/usr/bin/env python3
-"""Throughput of the quantized-actor W8A8 linear path on one MI355X.
+"""Throughput of the quantized-actor W8A8 linear on one MI355X, on the 7B-shaped FP8 workload.
 
-Workload of one step (the Qwen2.5-1.5B-shaped INT8 W8A8 decoder linears, stacked to the model's 28 layers
-so that the weights streamed per pass -- 1.31 GB of INT8 codes, 2.62 GB of bf16 masters -- are far larger
-than the 256 MB last-level cache and every read comes from HBM):
-  1. publish, once per RL step ("QuRL: Efficient Reinforcement Learning with Quantized Rollout", section 4):
-     a1  quantize every bf16 master weight to INT8 codes + one fp32 scale per output channel;
-     a5  count the codes (and scales) that changed since the previously published set (section 4.3);
-  2. decode, at every batch M in (1, 16, 64) ("QuRL" section 5: token-wise activation scales), for each
-     layer and each of qkv 1536->2048, o 1536->1536, gate/up 1536->2x8960, down 8960->1536:
-     a2  quantize the layer's bf16 activations per token;
-     a3  the W8A8 linear with its dequantization epilogue, bf16 out;
-     at M = 1 both run in one launch (qr_w8a8_linear_bf16: each workgroup quantizes the token row into its LDS,
-     the same codes and outputs bit for bit), at M = 16 and 64 as two launches.
-The step is captured once in a HIP graph (about 680 launches, most of them a few microseconds long) and
-replayed; inputs are resident in HBM before the timed region starts.
+Workload of one step: the four linears of a 7B-shaped decoder layer in FP8 E4M3 W8A8 -- qkv 3584->4608,
+o 3584->3584, gate/up 3584->2x18944, down 18944->3584 -- at every batch M in (1, 16, 128, 512, 2048): for
+each M, each of LAYERS distinct layers and each linear,
+  a2  the per-token quantization of the bf16 activations ("QuRL: Efficient Reinforcement Learning with
+      Quantized Rollout", section 5: token-wise activation scales), and
+  a3  the W8A8 linear with its dequantization epilogue, bf16 out (QuRL section 5; "QaRL: Rollout-Aligned
+      Quantization-Aware RL ...", sections 2.2 and 3.1),
+through qr_w8a8_linear_bf16 (at M = 1 the activation quantization runs inside the linear's kernel where that
+pays; otherwise the two launches run back to back). The layers' FP8 codes (LAYERS x 233 MB) are distinct and
+far larger than the 256 MB last-level cache, so every weight read comes from HBM. The codes are published once
+by a1 before the timed region (the publish is measured on its own in `extra`). The step is captured once in a
+HIP graph and replayed; inputs are resident in HBM before the timed region starts.
 
-value = algorithmic HBM bytes of one step (what the method must move: codes, scales, bf16 inputs and
-outputs) x steps / elapsed seconds. The JSON line also carries, per step of the path, the average launch
-duration from HIP events on the stream the kernels run on, the roofline of the dominant kernel (its measured
-HBM traffic when profiles/ holds a FETCH_SIZE / WRITE_SIZE summary taken on the current kernel sources), the CPU
-oracle timed on a bounded sample of the same step, and (unless --quick) the FP8 7B-shaped linears at the
-MFMA-bound batches and the grouped MoE FFN linears.
+value = operations of one step (2 M N K summed over every linear, layer and M) x steps / elapsed seconds, in
+TOPS (FP8 operations). The JSON line also carries, per M, the time of one layer and its fraction of the
+binding roofline (HBM 8 TB/s for M <= 128, FP8 MFMA 5.0 PFLOP/s for M >= 512); per linear and M, the linear's
+own kernel time on codes; the roofline of the dominant kernel (the FP8 gate/up GEMM at M = 2048, its measured
+HBM traffic when profiles/ holds a FETCH_SIZE / WRITE_SIZE summary taken on the current kernel sources), the
+decode layer's HBM fraction at M <= 16, and the CPU oracle timed on a bounded sample of the same step (one
+thread and all host cores). Unless --quick, `extra` holds the other workloads: the publish between RL steps on
+the 7B linears (fp32 masters, INT8 and FP8, with and without s; changed-code counts), the grouped MoE FFN, the
+1.5B-shaped INT8 linears, and W4A16.
 
 Counter runs for the traffic figure (each counter in a run of its own):
-  rocprofv3 --pmc FETCH_SIZE -d DIR_F -o t --output-format csv -- python3 bench.py --profile-row ROW
-  rocprofv3 --pmc WRITE_SIZE -d DIR_W -o t --output-format csv -- python3 bench.py --profile-row ROW
-  python3 bench.py --profile-row ROW --traffic-summary DIR_F DIR_W > profiles/traffic_ROW.md
+  rocprofv3 --pmc FETCH_SIZE -d DIR_F -o t --output-format csv -- python3 bench.py --profile-kernel NAME
+  rocprofv3 --pmc WRITE_SIZE -d DIR_W -o t --output-format csv -- python3 bench.py --profile-kernel NAME
+  python3 bench.py --profile-kernel NAME --traffic-summary DIR_F DIR_W > profiles/traffic_NAME.md
 """
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -40,15 +42,27 @@ if ROOT not in sys.path:
 
 METRIC = "W8A8 linear TOPS (MFMA % peak) + HBM GB/s at rollout decode shapes, 1 GPU"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
-MFMA_PEAK_TOPS = 5000.0       # MI355X dense INT8 POP/s and FP8 PFLOP/s, published (x1000)
+MFMA_PEAK_TOPS = 5000.0       # MI355X dense FP8 PFLOP/s and INT8 POP/s, published (x1000)
 
-LAYERS = 28
-LINEARS = (("qkv", 2048, 1536), ("o", 1536, 1536), ("gate_up", 17920, 1536), ("down", 1536, 8960))
-BATCHES = (1, 16, 64)
-FUSED_BATCHES = (1,)          # decode batches whose activation quantization runs inside the linear
-M_MAX = max(BATCHES)
+LINEARS_7B = (("qkv", 4608, 3584), ("o", 3584, 3584), ("gate_up", 37888, 3584), ("down", 3584, 18944))
+BATCHES_7B = (1, 16, 128, 512, 2048)
+MFMA_BOUND_M = 512            # M >= 512: bound by the FP8 MFMA peak; below, by HBM
+LAYERS = 5                    # distinct layers of codes in the step (5 x 233 MB)
+LINEARS_1P5B = (("qkv", 2048, 1536), ("o", 1536, 1536), ("gate_up", 17920, 1536), ("down", 1536, 8960))
+BATCHES_1P5B = (1, 16, 64)
 WEIGHT_STD = 0.02
 W4_GROUP = 128                # input channels per INT4 scale group (W4A16)
+DOMINANT = ("gate_up", 2048)  # the kernel that dominates the step: the FP8 gate/up GEMM at M = 2048
+
+# kernels the counter runs profile: name -> (format, m, n, k) of one W8A8 linear on codes
+PROFILE_KERNELS = {
+    "a3_fp8_gate_up_m2048": ("fp8", 2048, 37888, 3584),
+    "a3_fp8_gate_up_m512": ("fp8", 512, 37888, 3584),
+    "a3_fp8_gate_up_m1": ("fp8", 1, 37888, 3584),
+    "a3_fp8_gate_up_m16": ("fp8", 16, 37888, 3584),
+    "a3_fp8_down_m1": ("fp8", 1, 3584, 18944),
+    "a3_fp8_down_m16": ("fp8", 16, 3584, 18944),
+}
 
 
 def log(msg):
@@ -57,7 +71,7 @@ def log(msg):
 
 
 # ----------------------------------------------------------------------------------------------------------
-# algorithmic bytes and operations per call
+# algorithmic bytes and operations per call (what the method must move: codes, scales, bf16 in and out)
 # ----------------------------------------------------------------------------------------------------------
 def bytes_quantize(rows, k, in_bytes):
     return rows * k * in_bytes + rows * k + 4 * rows
@@ -67,12 +81,28 @@ def bytes_linear(m, n, k, out_bytes=2):
     return n * k + 4 * n + m * k + 4 * m + m * n * out_bytes
 
 
+def bytes_linear_bf16(m, n, k, out_bytes=2):
+    """the linear on bf16 activations (a2 inside or before a3): bf16 activations in instead of codes"""
+    return n * k + 4 * n + 2 * m * k + m * n * out_bytes
+
+
 def bytes_count(codes, scales):
     return 2 * codes + 2 * 4 * scales
 
 
 def ops_linear(m, n, k):
     return 2 * m * n * k
+
+
+def bound_of(m):
+    return "mfma" if m >= MFMA_BOUND_M else "hbm"
+
+
+def frac_of(m, nbytes, ops, ms):
+    """fraction of the binding roofline of a call sequence taking ms milliseconds"""
+    if bound_of(m) == "mfma":
+        return ops / ms / 1e9 / MFMA_PEAK_TOPS
+    return nbytes / ms / 1e6 / HBM_PEAK_GBS
 
 
 # ----------------------------------------------------------------------------------------------------------
@@ -128,263 +158,324 @@ class TimedGraph:
 
 
 # ----------------------------------------------------------------------------------------------------------
-# the main workload
+# the main workload: the 7B-shaped FP8 linears at every batch of the configuration
 # ----------------------------------------------------------------------------------------------------------
-class DecoderStack:
+class Dense7B:
+    """LAYERS distinct 7B-shaped layers: bf16 N(0, 0.02) masters published once (a1) to FP8 codes and scales,
+    bf16 N(0, 1) activations with 4 outlier channels x20 at the largest batch (smaller batches use row
+    prefixes), bf16 outputs."""
+
     def __init__(self, dev, seed=0):
         import torch
 
         import quantized_rollout_amd as qr
 
-        self.qr = qr
-        self.dev = dev
+        self.qr, self.dev = qr, dev
         gen = torch.Generator(device=dev)
         gen.manual_seed(seed)
-        rows_total = sum(LAYERS * n for _, n, _ in LINEARS)
-        codes_total = sum(LAYERS * n * k for _, n, k in LINEARS)
-        self.codes_total, self.rows_total = codes_total, rows_total
-        # one contiguous code / scale buffer for the whole published set (the changed-code count is one pass)
-        self.codes = torch.empty(codes_total, dtype=torch.uint8, device=dev)
-        self.scales = torch.empty(rows_total, dtype=torch.float32, device=dev)
-        self.prev_codes = torch.empty_like(self.codes)
-        self.prev_scales = torch.empty_like(self.scales)
-        self.count = torch.zeros(3, dtype=torch.int64, device=dev)
-        self.w, self.wc, self.ws, self.pc, self.ps = {}, {}, {}, {}, {}
-        self.x, self.xc, self.xs, self.y = {}, {}, {}, {}
-        co, so = 0, 0
-        for name, n, k in LINEARS:
-            self.w[name] = normal_bf16(gen, (LAYERS * n, k), WEIGHT_STD, dev)
-            self.wc[name] = self.codes[co:co + LAYERS * n * k].view(LAYERS * n, k)
-            self.pc[name] = self.prev_codes[co:co + LAYERS * n * k].view(LAYERS * n, k)
-            self.ws[name] = self.scales[so:so + LAYERS * n]
-            self.ps[name] = self.prev_scales[so:so + LAYERS * n]
-            co += LAYERS * n * k
-            so += LAYERS * n
-        # the previously published set: the same masters before an update dW ~ N(0, 1e-5)
-        for name, n, k in LINEARS:
-            w_prev = (self.w[name].float() - torch.randn(self.w[name].shape, generator=gen, device=dev) * 1e-5)
-            qr.qr_quantize_weights(w_prev.to(torch.bfloat16), qr.QR_INT8, codes=self.pc[name], scales=self.ps[name])
-            del w_prev
-        for name, n, k in LINEARS:
-            self.x[name] = activations_bf16(gen, LAYERS, M_MAX, k, dev)
-            self.xc[name] = torch.empty((LAYERS, M_MAX, k), dtype=torch.uint8, device=dev)
-            self.xs[name] = torch.empty((LAYERS, M_MAX), dtype=torch.float32, device=dev)
-            self.y[name] = torch.empty((M_MAX, n), dtype=torch.bfloat16, device=dev)
+        self.wc, self.ws, self.x, self.xc, self.xs, self.y = {}, {}, {}, {}, {}, {}
+        m_max = max(BATCHES_7B)
+        for name, n, k in LINEARS_7B:
+            codes = torch.empty((LAYERS * n, k), dtype=torch.uint8, device=dev)
+            scales = torch.empty((LAYERS * n,), dtype=torch.float32, device=dev)
+            for l in range(LAYERS):
+                w = normal_bf16(gen, (n, k), WEIGHT_STD, dev)
+                qr.qr_quantize_weights(w, qr.QR_FP8_E4M3, codes=codes[l * n:(l + 1) * n],
+                                       scales=scales[l * n:(l + 1) * n])
+                del w
+            self.wc[name], self.ws[name] = codes, scales
+            self.x[name] = activations_bf16(gen, LAYERS, m_max, k, dev)
+            # the activations' codes, for the linear's own kernel timed on codes
+            self.xc[name] = torch.empty((LAYERS, m_max, k), dtype=torch.uint8, device=dev)
+            self.xs[name] = torch.empty((LAYERS, m_max), dtype=torch.float32, device=dev)
+            for l in range(LAYERS):
+                qr.qr_quantize_acts(self.x[name][l], qr.QR_FP8_E4M3, codes=self.xc[name][l], scales=self.xs[name][l])
+            self.y[name] = torch.empty((m_max, n), dtype=torch.bfloat16, device=dev)
         self.wsp = qr.Workspace()
-        need = max(max(qr.qr_workspace_bytes(qr.QR_INT8, m, n, k),
-                       qr.qr_w8a8_linear_bf16_workspace_bytes(qr.QR_INT8, m, n, k))
-                   for m in BATCHES for _, n, k in LINEARS)
+        need = max(max(qr.qr_workspace_bytes(qr.QR_FP8_E4M3, m, n, k),
+                       qr.qr_w8a8_linear_bf16_workspace_bytes(qr.QR_FP8_E4M3, m, n, k))
+                   for m in BATCHES_7B for _, n, k in LINEARS_7B)
         self.wsp.get(need)
         torch.cuda.synchronize()
 
-    # the pieces of one step -------------------------------------------------------------------------------
-    def publish_quantize(self):
-        qr = self.qr
-        for name, n, k in LINEARS:
-            qr.qr_quantize_weights(self.w[name], qr.QR_INT8, codes=self.wc[name], scales=self.ws[name])
+    def w(self, name, l):
+        n = dict((a, b) for a, b, _ in LINEARS_7B)[name]
+        return self.wc[name][l * n:(l + 1) * n], self.ws[name][l * n:(l + 1) * n]
 
-    def publish_count(self):
+    # pieces of the step -----------------------------------------------------------------------------------
+    def linear_bf16(self, name, m, l):
+        """a2 + a3 of one linear on bf16 activations (one launch where the quantization runs inside)"""
         qr = self.qr
-        qr.qr_count_code_changes(self.codes, self.prev_codes, qr.QR_INT8, self.scales, self.prev_scales,
-                                 out3=self.count)
+        wc, ws = self.w(name, l)
+        qr.qr_w8a8_linear_bf16(qr.QR_FP8_E4M3, self.x[name][l, :m], wc, ws, y=self.y[name][:m], workspace=self.wsp)
 
-    def decode_acts(self, m):
+    def linear_codes(self, name, m, l):
+        """a3 alone, on the activation codes"""
         qr = self.qr
+        wc, ws = self.w(name, l)
+        qr.qr_w8a8_linear(qr.QR_FP8_E4M3, self.xc[name][l, :m], self.xs[name][l, :m], wc, ws, y=self.y[name][:m],
+                          workspace=self.wsp)
+
+    def acts(self, name, m, l):
+        """a2 alone"""
+        qr = self.qr
+        qr.qr_quantize_acts(self.x[name][l, :m], qr.QR_FP8_E4M3, codes=self.xc[name][l, :m],
+                            scales=self.xs[name][l, :m])
+
+    def batch(self, m):
         for l in range(LAYERS):
-            for name, n, k in LINEARS:
-                qr.qr_quantize_acts(self.x[name][l, :m], qr.QR_INT8, codes=self.xc[name][l, :m],
-                                    scales=self.xs[name][l, :m])
-
-    def decode_linears(self, m):
-        qr = self.qr
-        for l in range(LAYERS):
-            for name, n, k in LINEARS:
-                qr.qr_w8a8_linear(qr.QR_INT8, self.xc[name][l, :m], self.xs[name][l, :m],
-                                  self.wc[name][l * n:(l + 1) * n], self.ws[name][l * n:(l + 1) * n],
-                                  y=self.y[name][:m], workspace=self.wsp)
-
-    def decode_separate(self, m):
-        """a2 then a3 for every linear: two launches each"""
-        qr = self.qr
-        for l in range(LAYERS):
-            for name, n, k in LINEARS:
-                qr.qr_quantize_acts(self.x[name][l, :m], qr.QR_INT8, codes=self.xc[name][l, :m],
-                                    scales=self.xs[name][l, :m])
-                qr.qr_w8a8_linear(qr.QR_INT8, self.xc[name][l, :m], self.xs[name][l, :m],
-                                  self.wc[name][l * n:(l + 1) * n], self.ws[name][l * n:(l + 1) * n],
-                                  y=self.y[name][:m], workspace=self.wsp)
-
-    def decode_fused(self, m):
-        """a2 inside a3 (qr_w8a8_linear_bf16 on the bfloat16 activations): one launch per linear"""
-        qr = self.qr
-        for l in range(LAYERS):
-            for name, n, k in LINEARS:
-                qr.qr_w8a8_linear_bf16(qr.QR_INT8, self.x[name][l, :m], self.wc[name][l * n:(l + 1) * n],
-                                       self.ws[name][l * n:(l + 1) * n], y=self.y[name][:m], workspace=self.wsp)
-
-    def decode(self, m):
-        # single-token decode runs the activation quantization inside the linear's kernel (the same codes and
-        # outputs, bit for bit, one launch instead of two); larger batches quantize first, then run the linear
-        if m in FUSED_BATCHES:
-            self.decode_fused(m)
-        else:
-            self.decode_separate(m)
+            for name, _, _ in LINEARS_7B:
+                self.linear_bf16(name, m, l)
 
     def step(self):
-        self.publish_quantize()
-        self.publish_count()
-        for m in BATCHES:
-            self.decode(m)
+        for m in BATCHES_7B:
+            self.batch(m)
 
-    # algorithmic work ---------------------------------------------------------------------------------------
     @staticmethod
-    def row_work():
-        """{row: (bytes, ops, launches)} of one step."""
-        w = {}
-        w["a1_quantize_weights"] = (sum(bytes_quantize(LAYERS * n, k, 2) for _, n, k in LINEARS), 0, len(LINEARS))
-        codes = sum(LAYERS * n * k for _, n, k in LINEARS)
-        rows = sum(LAYERS * n for _, n, _ in LINEARS)
-        w["a5_count_changes"] = (bytes_count(codes, rows), 0, 1)
-        for m in BATCHES:
-            w["a2_quantize_acts_m%d" % m] = (LAYERS * sum(bytes_quantize(m, k, 2) for _, n, k in LINEARS), 0,
-                                             LAYERS * len(LINEARS))
-            w["a3_linear_m%d" % m] = (LAYERS * sum(bytes_linear(m, n, k) for _, n, k in LINEARS),
-                                      LAYERS * sum(ops_linear(m, n, k) for _, n, k in LINEARS),
-                                      LAYERS * len(LINEARS))
-        return w
+    def step_work():
+        """(bytes, ops) of one step"""
+        nb = LAYERS * sum(bytes_linear_bf16(m, n, k) for m in BATCHES_7B for _, n, k in LINEARS_7B)
+        no = LAYERS * sum(ops_linear(m, n, k) for m in BATCHES_7B for _, n, k in LINEARS_7B)
+        return nb, no
 
     def snapshot(self):
         import torch
 
-        out = [self.codes.clone(), self.scales.clone(), self.count.clone()]
-        for name, _, _ in LINEARS:
-            out += [self.y[name].clone(), self.xc[name].clone(), self.xs[name].clone()]
+        out = [self.y[name].clone() for name, _, _ in LINEARS_7B]
         torch.cuda.synchronize()
         return out
+
+
+def measure_rows(d, reps):
+    """Per batch: one layer's four linears on bf16 activations (a2 + a3, as in the step); per batch and linear:
+    the linear's own kernels on codes (a3) and the activation quantization alone (a2). HIP events around graph
+    replays on the stream the kernels run on; LAYERS distinct layers per replay."""
+    per_m, per_linear = {}, {}
+    for m in BATCHES_7B:
+        g = TimedGraph(lambda m=m: d.batch(m), LAYERS * len(LINEARS_7B))
+        ms = g.time_ms(reps) / LAYERS
+        del g
+        nb = sum(bytes_linear_bf16(m, n, k) for _, n, k in LINEARS_7B)
+        no = sum(ops_linear(m, n, k) for _, n, k in LINEARS_7B)
+        per_m["m%d" % m] = {"us_per_layer": round(ms * 1e3, 2), "TOPS": round(no / ms / 1e9, 1),
+                            "GB/s": round(nb / ms / 1e6, 1), "bound": bound_of(m),
+                            "frac": round(frac_of(m, nb, no, ms), 4)}
+        for name, n, k in LINEARS_7B:
+            g = TimedGraph(lambda m=m, name=name: [d.linear_codes(name, m, l) for l in range(LAYERS)], LAYERS)
+            ms = g.time_ms(reps) / LAYERS
+            del g
+            g = TimedGraph(lambda m=m, name=name: [d.acts(name, m, l) for l in range(LAYERS)], LAYERS)
+            ms_a = g.time_ms(reps) / LAYERS
+            del g
+            nb, no = bytes_linear(m, n, k), ops_linear(m, n, k)
+            per_linear["m%d_%s" % (m, name)] = {
+                "us": round(ms * 1e3, 2), "TOPS": round(no / ms / 1e9, 1), "GB/s": round(nb / ms / 1e6, 1),
+                "bound": bound_of(m), "frac": round(frac_of(m, nb, no, ms), 4),
+                "a2_us": round(ms_a * 1e3, 2)}
+    return per_m, per_linear
+
+
+def measure_dominant(d, reps):
+    """The dominant kernel: the FP8 gate/up GEMM at M = 2048 on codes, LAYERS distinct weights per replay; its
+    average launch duration from HIP events on the stream it runs on."""
+    name, m = DOMINANT
+    n, k = dict((a, (b, c)) for a, b, c in LINEARS_7B)[name]
+    g = TimedGraph(lambda: [d.linear_codes(name, m, l) for l in range(LAYERS)], LAYERS)
+    ms = g.time_ms(reps) / LAYERS
+    del g
+    return ms, ops_linear(m, n, k), bytes_linear(m, n, k)
+
+
+def cpu_baseline(budget_s):
+    """The oracle (plain C, test infrastructure) on a bounded sample of the step: for every batch M and linear of
+    the workload, the activation quantization (a2) of M bf16 rows and the W8A8 linear (a3) of those rows with a
+    subset of the output channels, sized so that each (M, linear) pair is about the same number of
+    multiply-adds. Run once on one thread and once on every host core (threads over output channels); the value
+    is operations per second (2 multiply-adds) in TOPS. Inputs: seeded numpy draws of the workload's
+    distributions, quantized by the oracle itself."""
+    import numpy as np
+
+    from oracle import core as O
+
+    rng = np.random.default_rng(0)
+    pairs = [(m, name, n, k) for m in BATCHES_7B for name, n, k in LINEARS_7B]
+    # multiply-adds per pair: half the budget for each run, from the oracle's ~0.18 G MAC/s per thread
+    macs_per_pair = budget_s / 2 * 0.18e9 / len(pairs)
+
+    acts = {}
+
+    def inputs(m, n_cols, k):
+        if (m, k) not in acts:  # the same activations for both runs
+            x = rng.standard_normal((m, k)).astype(np.float32)
+            x[:, rng.choice(k, 4, replace=False)] *= np.float32(20)
+            u = x.view(np.uint32).astype(np.uint64)
+            acts[(m, k)] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        w = (rng.standard_normal((n_cols, k)) * WEIGHT_STD).astype(np.float32)
+        wc, ws = O.quantize_rows_threaded(w, O.FP8)
+        return acts[(m, k)], wc, ws
+
+    def run(threads, scale):
+        t_total, ops, cols_used = 0.0, 0, 0
+        for m, name, n, k in pairs:
+            n_cols = int(max(1, min(n, scale * macs_per_pair / (m * k))))
+            xb, wc, ws = inputs(m, n_cols, k)
+            t0 = time.perf_counter()
+            if threads == 1:
+                xc, xs = O.quantize_rows(xb, O.FP8, s_mode=O.S_MUL_RECIP)
+                O.linear(O.FP8, xc, xs, wc, ws, O.BF16)
+            else:
+                xc, xs = O.quantize_rows_threaded(xb, O.FP8, s_mode=O.S_MUL_RECIP, threads=threads)
+                O.linear_threaded(O.FP8, xc, xs, wc, ws, O.BF16, threads=threads)
+            t_total += time.perf_counter() - t0
+            ops += ops_linear(m, n_cols, k)
+            cols_used += n_cols
+        return ops / t_total / 1e12, t_total, ops
+
+    cores = O.host_threads()
+    v1, t1, o1 = run(1, 1.0)
+    vn, tn, on = run(cores, float(cores))
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(vn, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": "every (M, linear) pair of the step, M in %s: a2 on the M bf16 rows and a3 on a subset of "
+                      "the output channels (about equal multiply-adds per pair), %.2e FP8 ops in %.1f s on %d "
+                      "threads; CPU %s" % (list(BATCHES_7B), on, tn, cores, cpu),
+            "seconds": round(tn, 2),
+            "single_thread": {"value": round(v1, 6), "unit": "TOPS", "cores": 1, "seconds": round(t1, 2),
+                              "ops": o1}}
 
 
 # ----------------------------------------------------------------------------------------------------------
 # other configurations of the path (side measurements, not part of `value`)
 # ----------------------------------------------------------------------------------------------------------
-def measure_fp8_7b(dev, reps):
-    """7B-shaped FP8 linears (qkv 3584->4608, o 3584->3584, gate/up 3584->2x18944, down 18944->3584), codes
-    of 5 distinct layers (1.17 GB) rotated; every batch of the configuration."""
+def measure_publish_7b(dev, reps):
+    """The publish between RL steps on the four 7B-shaped linears (233 M parameters): fp32 masters W ~ N(0, 0.02)
+    and W2 = W + dW, dW ~ N(0, 1e-5), per-input-channel s ~ U(0.5, 2). For INT8 and FP8, with and without s:
+    a1 quantizes W (the previous publish, untimed) and W2 (timed), a5 counts the codes, values and scales that
+    changed (timed), and the fused requantize + diff publishes W2 against W's codes in one pass (timed); the
+    fused codes and counts must equal the separate ones. Counts are reported with their fraction of P."""
     import torch
 
     import quantized_rollout_amd as qr
 
-    L = 5
-    lins = (("qkv", 4608, 3584), ("o", 3584, 3584), ("gate_up", 37888, 3584), ("down", 3584, 18944))
-    batches = (1, 16, 128, 512, 2048)
     gen = torch.Generator(device=dev)
-    gen.manual_seed(1)
-    wc, ws, xc, xs, y = {}, {}, {}, {}, {}
-    for name, n, k in lins:
-        w = normal_bf16(gen, (L * n, k), WEIGHT_STD, dev)
-        wc[name], ws[name] = qr.qr_quantize_weights(w, qr.QR_FP8_E4M3)
-        del w
-        x = activations_bf16(gen, 1, max(batches), k, dev)[0]
-        xc[name], xs[name] = qr.qr_quantize_acts(x, qr.QR_FP8_E4M3)
-        y[name] = torch.empty((max(batches), n), dtype=torch.bfloat16, device=dev)
-    wsp = qr.Workspace()
-    wsp.get(max(qr.qr_workspace_bytes(qr.QR_FP8_E4M3, m, n, k) for m in batches for _, n, k in lins))
-    out = {}
-    for m in batches:
-        def run(m=m):
-            for l in range(L):
-                for name, n, k in lins:
-                    qr.qr_w8a8_linear(qr.QR_FP8_E4M3, xc[name][:m], xs[name][:m], wc[name][l * n:(l + 1) * n],
-                                      ws[name][l * n:(l + 1) * n], y=y[name][:m], workspace=wsp)
-        g = TimedGraph(run, L * len(lins))
-        ms = g.time_ms(reps)
-        nb = L * sum(bytes_linear(m, n, k) for _, n, k in lins)
-        no = L * sum(ops_linear(m, n, k) for _, n, k in lins)
-        out["m%d" % m] = {"us_per_layer": round(ms * 1e3 / L, 2), "GB/s": round(nb / ms / 1e6, 1),
-                          "TFLOP/s": round(no / ms / 1e9, 1), "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 3),
-                          "mfma_frac": round(no / ms / 1e9 / MFMA_PEAK_TOPS, 3)}
-        del g
-    # per-shape at the MFMA-bound batches
-    for m in (512, 2048):
-        for name, n, k in lins:
-            def run1(m=m, name=name, n=n):
-                for l in range(L):
-                    qr.qr_w8a8_linear(qr.QR_FP8_E4M3, xc[name][:m], xs[name][:m], wc[name][l * n:(l + 1) * n],
-                                      ws[name][l * n:(l + 1) * n], y=y[name][:m], workspace=wsp)
-            g = TimedGraph(run1, L)
-            ms = g.time_ms(reps)
-            no = L * ops_linear(m, n, k)
-            out["m%d_%s" % (m, name)] = {"us": round(ms * 1e3 / L, 2), "TFLOP/s": round(no / ms / 1e9, 1),
-                                         "mfma_frac": round(no / ms / 1e9 / MFMA_PEAK_TOPS, 3)}
-            del g
-    del wc, ws, xc, xs, y, wsp
+    gen.manual_seed(4)
+    P = sum(n * k for _, n, k in LINEARS_7B)
+    rows = sum(n for _, n, _ in LINEARS_7B)
+    w, w2, s = {}, {}, {}
+    for name, n, k in LINEARS_7B:
+        w[name] = torch.randn((n, k), generator=gen, device=dev) * WEIGHT_STD
+        w2[name] = w[name] + torch.randn((n, k), generator=gen, device=dev) * 1e-5
+        s[name] = torch.rand((k,), generator=gen, device=dev) * 1.5 + 0.5
+    codes = {name: [torch.empty((n, k), dtype=torch.uint8, device=dev) for _ in range(3)]
+             for name, n, k in LINEARS_7B}
+    scales = {name: [torch.empty((n,), dtype=torch.float32, device=dev) for _ in range(3)]
+              for name, n, k in LINEARS_7B}
+    rc = {name: torch.empty((n, 3), dtype=torch.int32, device=dev) for name, n, _ in LINEARS_7B}
+    cnt = torch.zeros((len(LINEARS_7B), 3), dtype=torch.int64, device=dev)
+    o3 = torch.zeros((len(LINEARS_7B), 3), dtype=torch.int64, device=dev)
+    out = {"params": P}
+    for qname, q in (("int8", qr.QR_INT8), ("fp8", qr.QR_FP8_E4M3)):
+        for with_s in (False, True):
+            key = "%s%s" % (qname, "_s" if with_s else "")
+            sv = lambda name: s[name] if with_s else None  # noqa: E731
+
+            def prev():
+                for name, _, _ in LINEARS_7B:
+                    qr.qr_quantize_weights(w[name], q, s=sv(name), codes=codes[name][0], scales=scales[name][0])
+
+            def quant():
+                for name, _, _ in LINEARS_7B:
+                    qr.qr_quantize_weights(w2[name], q, s=sv(name), codes=codes[name][1], scales=scales[name][1])
+
+            def count():
+                for i, (name, _, _) in enumerate(LINEARS_7B):
+                    qr.qr_count_code_changes(codes[name][0], codes[name][1], q, scales[name][0], scales[name][1],
+                                             out3=cnt[i])
+
+            def fused():
+                for i, (name, _, _) in enumerate(LINEARS_7B):
+                    qr.qr_requantize_weights(w2[name], q, codes[name][0], scales[name][0], s=sv(name),
+                                             codes=codes[name][2], scales=scales[name][2], row_counts=rc[name],
+                                             out3=o3[i])
+            prev()
+            gq, gc, gf = (TimedGraph(quant, len(LINEARS_7B)), TimedGraph(count, len(LINEARS_7B)),
+                          TimedGraph(fused, 2 * len(LINEARS_7B)))
+            ms_q, ms_c, ms_f = gq.time_ms(reps), gc.time_ms(reps), gf.time_ms(reps)
+            del gq, gc, gf
+            torch.cuda.synchronize()
+            same = all(torch.equal(codes[name][1], codes[name][2]) and torch.equal(scales[name][1], scales[name][2])
+                       for name, _, _ in LINEARS_7B) and torch.equal(cnt, o3)
+            tot = cnt.sum(dim=0).tolist()
+            nb_q = sum(bytes_quantize(n, k, 4) for _, n, k in LINEARS_7B) + (4 * sum(k for _, _, k in LINEARS_7B)
+                                                                             if with_s else 0)
+            nb_c = bytes_count(P, rows)
+            nb_f = 4 * P + 2 * P + 8 * rows + 12 * rows
+            out[key] = {
+                "changed_bytes": int(tot[0]), "changed_values": int(tot[1]), "changed_scales": int(tot[2]),
+                "changed_frac": round(tot[0] / P, 6), "changed_value_frac": round(tot[1] / P, 6),
+                "changed_scale_frac": round(tot[2] / rows, 6),
+                "per_linear_changed_bytes": {name: int(cnt[i, 0]) for i, (name, _, _) in enumerate(LINEARS_7B)},
+                "a1_us": round(ms_q * 1e3, 1), "a1_GB/s": round(nb_q / ms_q / 1e6, 1),
+                "a1_hbm_frac": round(nb_q / ms_q / 1e6 / HBM_PEAK_GBS, 4),
+                "a5_us": round(ms_c * 1e3, 1), "a5_GB/s": round(nb_c / ms_c / 1e6, 1),
+                "a5_hbm_frac": round(nb_c / ms_c / 1e6 / HBM_PEAK_GBS, 4),
+                "fused_us": round(ms_f * 1e3, 1), "fused_GB/s": round(nb_f / ms_f / 1e6, 1),
+                "fused_hbm_frac": round(nb_f / ms_f / 1e6 / HBM_PEAK_GBS, 4),
+                "fused_equals_separate": bool(same)}
+    del w, w2, s, codes, scales, rc
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
 
 
-def measure_publish_fused(stack, reps):
-    """The publish of the 1.5B stack (112 matrices, bf16 masters -> INT8) as one fused requantize + diff pass per
-    weight (codes, scales, per-row change triples and their sums) against the step's separate quantize (a1) and
-    changed-code count (a5); both out of place against the same previous publish, so they can be compared."""
+def measure_int8_1p5b(dev, reps):
+    """The Qwen2.5-1.5B-shaped INT8 W8A8 linears (qkv 1536->2048, o 1536->1536, gate/up 1536->2x8960, down
+    8960->1536) at M = 1, 16, 64 on bf16 activations (a2 + a3 through qr_w8a8_linear_bf16), codes of 28 distinct
+    layers (1.31 GB) rotated."""
     import torch
 
-    qr = stack.qr
-    rc = {name: torch.empty((LAYERS * n, 3), dtype=torch.int32, device=stack.dev) for name, n, _ in LINEARS}
-    o3 = torch.empty((len(LINEARS), 3), dtype=torch.int64, device=stack.dev)
+    import quantized_rollout_amd as qr
 
-    def fused():
-        for i, (name, n, k) in enumerate(LINEARS):
-            qr.qr_requantize_weights(stack.w[name], qr.QR_INT8, stack.pc[name], stack.ps[name],
-                                     codes=stack.wc[name], scales=stack.ws[name], row_counts=rc[name], out3=o3[i])
-
-    def separate():
-        stack.publish_quantize()
-        stack.publish_count()
-
-    gs, gf = TimedGraph(separate, len(LINEARS) + 2), TimedGraph(fused, 2 * len(LINEARS))
-    ms_sep, ms_fused = gs.time_ms(reps), gf.time_ms(reps)
-    gs.replay()
+    L = 28
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    wc, ws, x, y = {}, {}, {}, {}
+    for name, n, k in LINEARS_1P5B:
+        wc[name] = torch.empty((L * n, k), dtype=torch.uint8, device=dev)
+        ws[name] = torch.empty((L * n,), dtype=torch.float32, device=dev)
+        for l in range(L):
+            qr.qr_quantize_weights(normal_bf16(gen, (n, k), WEIGHT_STD, dev), qr.QR_INT8,
+                                   codes=wc[name][l * n:(l + 1) * n], scales=ws[name][l * n:(l + 1) * n])
+        x[name] = activations_bf16(gen, L, max(BATCHES_1P5B), k, dev)
+        y[name] = torch.empty((max(BATCHES_1P5B), n), dtype=torch.bfloat16, device=dev)
+    wsp = qr.Workspace()
+    wsp.get(max(qr.qr_w8a8_linear_bf16_workspace_bytes(qr.QR_INT8, m, n, k) for m in BATCHES_1P5B
+                for _, n, k in LINEARS_1P5B))
+    out = {}
+    for m in BATCHES_1P5B:
+        def run(m=m):
+            for l in range(L):
+                for name, n, k in LINEARS_1P5B:
+                    qr.qr_w8a8_linear_bf16(qr.QR_INT8, x[name][l, :m], wc[name][l * n:(l + 1) * n],
+                                           ws[name][l * n:(l + 1) * n], y=y[name][:m], workspace=wsp)
+        g = TimedGraph(run, L * len(LINEARS_1P5B))
+        ms = g.time_ms(reps) / L
+        del g
+        nb = sum(bytes_linear_bf16(m, n, k) for _, n, k in LINEARS_1P5B)
+        out["m%d" % m] = {"us_per_layer": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                          "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del wc, ws, x, y, wsp
     torch.cuda.synchronize()
-    sep_codes, sep_count = stack.codes.clone(), stack.count.clone()
-    gf.replay()
-    torch.cuda.synchronize()
-    same = bool(torch.equal(stack.codes, sep_codes) and torch.equal(o3.sum(dim=0), sep_count))
-    codes, rows = stack.codes_total, stack.rows_total
-    nb = 2 * codes + codes + codes + 4 * rows + 4 * rows + 12 * rows  # masters, previous codes, new codes, scales
-    del gs, gf
-    return {"us_fused": round(ms_fused * 1e3, 1), "us_separate": round(ms_sep * 1e3, 1),
-            "speedup": round(ms_sep / ms_fused, 3), "GB/s": round(nb / ms_fused / 1e6, 1),
-            "hbm_frac": round(nb / ms_fused / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nb),
-            "changed": [int(v) for v in sep_count.tolist()], "matches_separate": same}
-
-
-def measure_decode_fused(stack, reps):
-    """The m = 1 decode of the 1.5B stack (112 linears) on bfloat16 activations with the activation quantization
-    inside the linear (qr_w8a8_linear_bf16) against the step's two launches per linear (a2 then a3); both are
-    replayed as HIP graphs and their outputs compared bit for bit."""
-    import torch
-
-    qr = stack.qr
-
-    def fused():
-        for l in range(LAYERS):
-            for name, n, k in LINEARS:
-                qr.qr_w8a8_linear_bf16(qr.QR_INT8, stack.x[name][l, :1], stack.wc[name][l * n:(l + 1) * n],
-                                       stack.ws[name][l * n:(l + 1) * n], y=stack.y[name][:1], workspace=stack.wsp)
-
-    g2, gf = (TimedGraph(lambda: stack.decode_separate(1), 2 * LAYERS * len(LINEARS)),
-              TimedGraph(fused, LAYERS * len(LINEARS)))
-    ms2, msf = g2.time_ms(reps), gf.time_ms(reps)
-    outs = []
-    for g in (g2, gf):
-        g.replay()
-        torch.cuda.synchronize()
-        outs.append([stack.y[name][:1].clone() for name, _, _ in LINEARS])
-    same = all(torch.equal(a, b) for a, b in zip(*outs))
-    del g2, gf
-    return {"us_two_launches": round(ms2 * 1e3, 1), "us_fused": round(msf * 1e3, 1),
-            "speedup": round(ms2 / msf, 3), "us_per_layer_fused": round(msf * 1e3 / LAYERS, 2),
-            "y_matches_two_launches": same}
+    torch.cuda.empty_cache()
+    return out
 
 
 def bytes_w4a16(m, n, k, out_bytes=2):
@@ -548,117 +639,46 @@ def measure_moe(dev, reps):
 
 
 # ----------------------------------------------------------------------------------------------------------
-# CPU baseline: the oracle on a bounded sample of the same step
-# ----------------------------------------------------------------------------------------------------------
-def cpu_baseline(stack, budget_s):
-    """The oracle (plain C, one thread) runs the step of the main workload layer by layer -- a1 and a5 on
-    the layer's four weight matrices, a2 and a3 at M = 1, 16, 64 -- until `budget_s` seconds have passed.
-    It also checks the GPU's published codes and scales of each sampled layer bit for bit."""
-    import numpy as np
-    import torch
-
-    from oracle import core as O
-
-    def bits(t):
-        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-
-    t_total, nbytes, layers, parity = 0.0, 0, 0, True
-    while t_total < budget_s and layers < LAYERS:
-        l = layers
-        host = {}
-        for name, n, k in LINEARS:
-            host[name] = (bits(stack.w[name][l * n:(l + 1) * n]), bits(stack.x[name][l]),
-                          stack.pc[name][l * n:(l + 1) * n].cpu().numpy(), stack.ps[name][l * n:(l + 1) * n].cpu().numpy(),
-                          stack.wc[name][l * n:(l + 1) * n].cpu().numpy(), stack.ws[name][l * n:(l + 1) * n].cpu().numpy())
-        t0 = time.perf_counter()
-        for name, n, k in LINEARS:
-            w, x, pc, ps, _, _ = host[name]
-            wc, ws = O.quantize_rows(w, O.INT8)
-            O.count_code_changes(wc, pc, O.INT8, ws, ps)
-            nbytes += bytes_quantize(n, k, 2) + bytes_count(n * k, n)
-            for m in BATCHES:
-                xc, xs = O.quantize_rows(x[:m], O.INT8, s_mode=O.S_MUL_RECIP)
-                O.linear(O.INT8, xc, xs, wc, ws, O.BF16)
-                nbytes += bytes_quantize(m, k, 2) + bytes_linear(m, n, k)
-            host[name] = host[name] + (wc, ws)
-        t_total += time.perf_counter() - t0
-        for name, n, k in LINEARS:
-            gc, gs, wc, ws = host[name][4], host[name][5], host[name][6], host[name][7]
-            parity = parity and np.array_equal(gc, wc) and np.array_equal(gs.view(np.uint32), ws.view(np.uint32))
-        layers += 1
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d layers of the step (a1+a5 on the 4 weight matrices, a2+a3 at M=1,16,64), "
-                      "%.1f s of single-thread CPU time; host has %d cores available"
-                      % (layers, LAYERS, t_total, len(os.sched_getaffinity(0))),
-            "seconds": round(t_total, 2), "publish_codes_match_gpu": bool(parity)}
-
-
-# ----------------------------------------------------------------------------------------------------------
-# ----------------------------------------------------------------------------------------------------------
-# measured HBM traffic of a row (rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a plain copy)
+# measured HBM traffic of a kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a plain copy)
 # ----------------------------------------------------------------------------------------------------------
 TRAFFIC_COPY_BYTES = 256 << 20  # the scale reference: a device copy of 256 MiB (reads and writes that many)
 
-
-def row_pieces(stack):
-    """{row: function that launches that row's kernels once}, as timed in `rows`."""
-    pieces = {"a1_quantize_weights": stack.publish_quantize, "a5_count_changes": stack.publish_count}
-    for m in BATCHES:
-        pieces["a2_quantize_acts_m%d" % m] = lambda m=m: stack.decode_acts(m)
-        pieces["a3_linear_m%d" % m] = lambda m=m: stack.decode_linears(m)
-    return pieces
-
-
-# the library sources each row's kernels are built from (plus the shared device and host headers and the ABI,
-# which holds the planners' inputs): a measured traffic figure stays valid while these files are unchanged
+# the library sources each kernel is built from (plus the shared device and host headers and the ABI, which
+# holds the planners' inputs): a measured traffic figure stays valid while these files are unchanged
 ROW_SOURCES = {"a1": ["qr_quantize.hip"], "a2": ["qr_quantize.hip"], "a5": ["qr_grouped.hip"],
                "a3": ["qr_linear.hip", "qr_gemm.hip"]}
 SHARED_SOURCES = ["qr_device.hpp", "qr_internal.hpp", "qr_abi.hip"]
 
 
-def sources_digest(row):
-    """sha256 over the library sources of `row`'s kernels: a traffic figure is only reported for the sources it
+def sources_digest(name):
+    """sha256 over the library sources of `name`'s kernels: a traffic figure is only reported for the sources it
     was measured on."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_rollout_amd", "csrc")
-    for name in sorted(ROW_SOURCES[row.split("_")[0]] + SHARED_SOURCES):
-        h.update(name.encode())
-        with open(os.path.join(csrc, name), "rb") as f:
+    for fname in sorted(ROW_SOURCES[name.split("_")[0]] + SHARED_SOURCES):
+        h.update(fname.encode())
+        with open(os.path.join(csrc, fname), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def profile_row(stack, name, reps):
-    """The launches the counter runs look at: a plain device copy, `reps` eager passes of one row, the copy
-    again (the copies bracket the row and give the counters' scale)."""
-    import torch
-
-    fn = row_pieces(stack)[name]
-    # an elementwise kernel (never a DMA-engine copy): reads and writes TRAFFIC_COPY_BYTES of fp32
-    src = torch.ones(TRAFFIC_COPY_BYTES // 4, dtype=torch.float32, device=stack.dev)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    for _ in range(reps):
-        fn()
-    torch.cuda.synchronize()
-    torch.neg(src, out=dst)
-    torch.cuda.synchronize()
+def kernel_work(name):
+    """(algorithmic bytes, ops) of one call of a profiled kernel"""
+    _, m, n, k = PROFILE_KERNELS[name]
+    return bytes_linear(m, n, k), ops_linear(m, n, k)
 
 
-def profile_linear(dev, spec, reps):
-    """One W8A8 linear shape for counter runs: `spec` = "int8|fp8:M:N:K"; distinct weight-code copies (together
-    past the caches) are used in turn for `reps` calls between two elementwise copies (the markers)."""
+def profile_kernel(dev, name, reps):
+    """One W8A8 linear shape for counter runs: distinct weight-code copies (together past the caches) are used in
+    turn for `reps` calls between two elementwise copies (the markers that give the counters' scale)."""
     import torch
 
     import quantized_rollout_amd as qr
 
-    qname, m, n, k = spec.split(":")
+    qname, m, n, k = PROFILE_KERNELS[name]
     q = {"int8": qr.QR_INT8, "fp8": qr.QR_FP8_E4M3}[qname]
-    m, n, k = int(m), int(n), int(k)
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
     copies = max(2, min(reps, int(1.2e9 // (n * k)) + 1))
@@ -677,7 +697,7 @@ def profile_linear(dev, spec, reps):
     torch.cuda.synchronize()
     torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log("profiled %d calls of %s" % (reps, spec))
+    log("profiled %d calls of %s (%s m=%d n=%d k=%d)" % (reps, name, qname, m, n, k))
 
 
 def _counter_dispatches(directory, counter):
@@ -701,10 +721,9 @@ def _counter_dispatches(directory, counter):
 
 
 def traffic_summary(fetch_dir, write_dir, name, reps, command):
-    """Markdown summary of the two counter runs of `profile_row`: per-dispatch FETCH_SIZE / WRITE_SIZE of the
-    row's launches between the two copies, each scaled by what the counter reads for the copy."""
-    launches = DecoderStack.row_work()[name][2]
-    nbytes = DecoderStack.row_work()[name][0]
+    """Markdown summary of the two counter runs of `profile_kernel`: per-call FETCH_SIZE / WRITE_SIZE of the
+    kernel's launches between the two copies, each scaled by what the counter reads for the copy."""
+    nbytes, _ = kernel_work(name)
     out = {}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         ds = _counter_dispatches(directory, counter)
@@ -713,16 +732,14 @@ def traffic_summary(fetch_dir, write_dir, name, reps, command):
             raise SystemExit("copy markers not found in %s" % directory)
         a, b = copies[-2], copies[-1]
         row = [d for d in ds[a + 1:b] if "qr::" in d[1]]
-        # a launch of the row is one library call; a call may run more than one kernel (a split-K reduction
-        # after the linear), so every library dispatch between the copies counts, per call
-        if len(row) < reps * launches:
-            raise SystemExit("%s: %d row dispatches between the copies, expected at least %d"
-                             % (counter, len(row), reps * launches))
+        # a call may run more than one kernel (a split-K reduction after the linear): every library dispatch
+        # between the copies counts, per call
+        if len(row) < reps:
+            raise SystemExit("%s: %d dispatches between the copies, expected at least %d" % (counter, len(row), reps))
         copy_kib = (ds[a][2] + ds[b][2]) / 2
         scale = TRAFFIC_COPY_BYTES / (copy_kib * 1024.0)
-        out[counter] = (sum(v for _, _, v in row) / (reps * launches), copy_kib, scale, len(row))
-    per_launch = sum(v * 1024.0 * sc for v, _, sc, _ in out.values())
-    dispatches = out["FETCH_SIZE"][3]
+        out[counter] = (sum(v for _, _, v in row) / reps, copy_kib, scale, len(row))
+    per_call = sum(v * 1024.0 * sc for v, _, sc, _ in out.values())
     lines = [
         "# HBM traffic of `%s` (rocprofv3 FETCH_SIZE / WRITE_SIZE), one MI355X" % name,
         "",
@@ -732,25 +749,26 @@ def traffic_summary(fetch_dir, write_dir, name, reps, command):
         command,
         "```",
         "",
-        "The row's %d launches (library calls) are run %d times between two elementwise passes over %d MiB of fp32 "
-        "(a plain copy that reads and writes %d MiB): %d kernel dispatches. Each counter's readings (KiB) are "
-        "summed per call and scaled by the copy's to bytes." % (
-            launches, reps, TRAFFIC_COPY_BYTES >> 20, TRAFFIC_COPY_BYTES >> 20, dispatches),
+        "The call (%s m=%d n=%d k=%d) runs %d times between two elementwise passes over %d MiB of fp32 (a plain "
+        "copy that reads and writes %d MiB): %d kernel dispatches. Each counter's readings (KiB) are summed per "
+        "call and scaled by the copy's to bytes." % (PROFILE_KERNELS[name] + (reps, TRAFFIC_COPY_BYTES >> 20,
+                                                                              TRAFFIC_COPY_BYTES >> 20,
+                                                                              out["FETCH_SIZE"][3])),
         "",
-        "| counter | mean per row launch (KiB) | copy reading (KiB) | scale to bytes per KiB |",
+        "| counter | mean per call (KiB) | copy reading (KiB) | scale to bytes per KiB |",
         "|---|---|---|---|",
     ]
     for counter, (v, ck, sc, _) in out.items():
         lines.append("| %s | %.1f | %.1f | %.4f x 1024 |" % (counter, v, ck, sc))
     lines += [
         "",
-        "| | bytes per launch |",
+        "| | bytes per call |",
         "|---|---|",
-        "| algorithmic (what the method must move) | %d |" % (nbytes // launches),
-        "| measured HBM traffic (fetch + write, scaled) | %d |" % int(per_launch),
+        "| algorithmic (what the method must move) | %d |" % nbytes,
+        "| measured HBM traffic (fetch + write, scaled) | %d |" % int(per_call),
         "",
         "traffic_row: %s" % name,
-        "traffic_bytes_per_launch: %d" % int(per_launch),
+        "traffic_bytes_per_launch: %d" % int(per_call),
         "traffic_sources_sha256: %s" % sources_digest(name),
         "",
     ]
@@ -758,7 +776,7 @@ def traffic_summary(fetch_dir, write_dir, name, reps, command):
 
 
 def read_traffic(name):
-    """Measured traffic per launch of `name` from profiles/, or None when absent or taken on other sources."""
+    """Measured traffic per call of `name` from profiles/, or None when absent or taken on other sources."""
     import glob
 
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
@@ -776,24 +794,23 @@ def read_traffic(name):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--reps", type=int, default=50, help="replays per per-row timing")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="replays per per-row timing")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="skip the FP8 7B and MoE side measurements")
-    ap.add_argument("--profile-row", metavar="ROW", help="only run ROW between two device copies (for the "
+    ap.add_argument("--quick", action="store_true", help="skip the side workloads in `extra`")
+    ap.add_argument("--profile-kernel", metavar="NAME", choices=sorted(PROFILE_KERNELS),
+                    help="only run one W8A8 linear shape --profile-reps times between two device copies (for the "
                     "rocprofv3 counter runs) and exit")
     ap.add_argument("--profile-reps", type=int, default=3)
-    ap.add_argument("--profile-linear", metavar="Q:M:N:K", help="only run one W8A8 linear shape (int8 or fp8) "
-                    "--profile-reps times between two device copies (for the rocprofv3 counter runs) and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="print the markdown summary of the two counter runs of --profile-row ROW and exit")
+                    help="print the markdown summary of the two counter runs of --profile-kernel NAME and exit")
     ap.add_argument("--traffic-command", default="", help="the command lines recorded in that summary")
     args = ap.parse_args()
 
     if args.traffic_summary:
-        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.profile_row,
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.profile_kernel,
                               args.profile_reps, args.traffic_command))
         return 0
 
@@ -814,25 +831,20 @@ def main():
     torch.cuda.set_device(dev)
     log("device %s, libqr %s" % (torch.cuda.get_device_name(dev), qr.qr_version()))
 
-    if args.profile_linear:
-        profile_linear(dev, args.profile_linear, args.profile_reps)
+    if args.profile_kernel:
+        profile_kernel(dev, args.profile_kernel, args.profile_reps)
         return 0
-    stack = DecoderStack(dev)
-    if args.profile_row:
-        profile_row(stack, args.profile_row, args.profile_reps)
-        return 0
-    work = stack.row_work()
-    step_bytes = sum(v[0] for v in work.values())
-    step_ops = sum(v[1] for v in work.values())
-    log("inputs resident: %.2f GB of bf16 masters, %.2f GB of codes" %
-        (sum(w.numel() * 2 for w in stack.w.values()) / 1e9, stack.codes_total / 1e9))
+
+    d = Dense7B(dev)
+    step_bytes, step_ops = d.step_work()
+    log("inputs resident: %d layers of 7B-shaped FP8 codes (%.2f GB), bf16 activations up to M = %d"
+        % (LAYERS, LAYERS * sum(n * k for _, n, k in LINEARS_7B) / 1e9, max(BATCHES_7B)))
 
     # eager reference of one step, then the graph of the whole step
-    stack.step()
-    ref = stack.snapshot()
-    step_graph = TimedGraph(stack.step, None)
+    d.step()
+    ref = d.snapshot()
+    step_graph = TimedGraph(d.step, None)
     log("step graph captured")
-
     for _ in range(args.warmup):
         step_graph.replay()
     torch.cuda.synchronize()
@@ -848,67 +860,62 @@ def main():
     ms_step = ms_total / args.steps
     log("timed %d steps: %.3f ms/step (events), %.3f ms/step (host clock)" % (args.steps, ms_step,
                                                                               wall * 1e3 / args.steps))
-
-    # every replay reproduces the eager step bit for bit (INT8 path: exact integers, fixed epilogue)
-    got = stack.snapshot()
-    replay_ok = all(torch.equal(a, b) for a, b in zip(ref, got))
+    # the replays reproduce the eager step bit for bit (FP8 outputs are deterministic for a given shape)
+    got = d.snapshot()
+    replay_ok = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, got))
     if not replay_ok:
         log("ERROR: graph replay differs from the eager step")
+    del step_graph
 
-    # per-row launch timing (HIP events on the stream the kernels run on)
-    rows = {}
-    for name, fn in row_pieces(stack).items():
-        nb, no, launches = work[name]
-        g = TimedGraph(fn, launches)
-        ms = g.time_ms(args.reps)
-        rows[name] = {"launches": launches, "us_per_launch": round(ms * 1e3 / launches, 3),
-                      "us_total": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
-                      "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
-        if no:
-            rows[name]["TOPS"] = round(no / ms / 1e9, 2)
-        del g
-    dominant = max(rows, key=lambda r: rows[r]["us_total"])
-    d = rows[dominant]
-    nb = work[dominant][0]
-    achieved = nb / (d["us_total"] * 1e3)  # GB/s
-    traffic = read_traffic(dominant)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dominant,
-                "bytes_per_launch": int(nb // d["launches"]), "us_per_launch": d["us_per_launch"]}
+    per_m, per_linear = measure_rows(d, args.reps)
+    ms_dom, ops_dom, bytes_dom = measure_dominant(d, args.reps)
+    dom_name = "a3_fp8_%s_m%d" % DOMINANT
+    achieved = ops_dom / ms_dom / 1e9  # TFLOP/s
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_PEAK_TOPS, 4), "traffic": read_traffic(dom_name),
+                "kernel": dom_name, "flops_per_launch": int(ops_dom), "bytes_per_launch": int(bytes_dom),
+                "us_per_launch": round(ms_dom * 1e3, 2)}
+    decode = {}
+    for m in (1, 16):
+        r = per_m["m%d" % m]
+        decode["m%d" % m] = {"bound": "hbm", "achieved": r["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": r["frac"], "us_per_layer": r["us_per_layer"]}
 
     extra = {}
     if not args.quick:
-        del step_graph
+        del d
         torch.cuda.synchronize()
-        log("FP8 7B-shaped linears")
-        extra["fp8_7b_linears"] = measure_fp8_7b(dev, max(5, args.reps // 5))
-        log("MoE grouped linears")
-        extra["moe_fp8_grouped"] = measure_moe(dev, max(5, args.reps // 5))
+        torch.cuda.empty_cache()
+        r = max(5, args.reps // 2)
+        log("publish of the 7B linears (fp32 masters, INT8 / FP8, with and without s)")
+        extra["publish_7b"] = measure_publish_7b(dev, r)
+        log("MoE grouped FFN (Qwen3-30B-A3B-shaped, FP8)")
+        extra["moe_fp8"] = measure_moe(dev, r)
+        log("1.5B-shaped INT8 linears")
+        extra["int8_1p5b_linears"] = measure_int8_1p5b(dev, r)
         log("W4A16 7B-shaped linears")
-        extra["w4a16_7b_linears"] = measure_w4a16_7b(dev, max(5, args.reps // 5))
-        log("fused requantize + diff publish")
-        extra["publish_fused_requant_diff"] = measure_publish_fused(stack, max(5, args.reps // 5))
-        log("decode at m = 1 with the activation quantization fused")
-        extra["decode_m1_fused_act_quant"] = measure_decode_fused(stack, max(5, args.reps // 5))
+        extra["w4a16_7b_linears"] = measure_w4a16_7b(dev, r)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
-        cpu = cpu_baseline(stack, args.cpu_budget)
+        cpu = cpu_baseline(args.cpu_budget)
 
-    value = step_bytes * args.steps / (ms_total / 1e3) / 1e9
+    value = step_ops * args.steps / (ms_total / 1e3) / 1e12
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": round(value, 1), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "qwen2.5-1.5b-shaped INT8 W8A8 decoder linears x %d layers: publish (a1+a5) + "
-                               "decode at M=1,16,64 (a2+a3; at M=1 in one launch)" % LAYERS,
-                   "layers": LAYERS, "linears": {n: [nn, k] for n, nn, k in LINEARS}, "batches": list(BATCHES),
-                   "weights": "bf16 N(0,0.02)", "acts": "bf16 N(0,1), 4 outlier channels x20"},
-        "tops": round(step_ops * args.steps / (ms_total / 1e3) / 1e12, 3),
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "step_bytes": int(step_bytes), "replay_matches_eager": bool(replay_ok),
-        "roofline": roofline, "cpu_baseline": cpu, "rows": rows, "extra": extra,
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "7B-shaped FP8 E4M3 W8A8 decoder-layer linears at M=%s: per-token activation "
+                               "quantization (a2) + W8A8 linear with dequant epilogue (a3), bf16 in and out, "
+                               "%d distinct layers of codes per step" % (",".join(map(str, BATCHES_7B)), LAYERS),
+                   "linears": {n: [nn, k] for n, nn, k in LINEARS_7B}, "batches": list(BATCHES_7B),
+                   "layers": LAYERS, "weights": "bf16 N(0,0.02) published to FP8 codes (a1, before timing)",
+                   "acts": "bf16 N(0,1), 4 outlier channels x20"},
+        "hbm_GBps": round(step_bytes * args.steps / (ms_total / 1e3) / 1e9, 1),
+        "step_bytes": int(step_bytes), "step_ops": int(step_ops), "replay_matches_eager": bool(replay_ok),
+        "roofline": roofline, "roofline_decode": decode, "cpu_baseline": cpu,
+        "per_m": per_m, "per_linear": per_linear, "extra": extra,
     }
     print(json.dumps(line), flush=True)
     return 0 if replay_ok else 1

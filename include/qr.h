@@ -25,6 +25,11 @@
  *    and qr_last_error() (thread-local) explains it. A failed launch returns QR_ERR_HIP with the HIP error
  *    text. Inputs must be finite (NaN/Inf give unspecified codes).
  *  - Calls on different streams must not share a workspace buffer.
+ *  - Kernel choice is automatic and depends only on the arguments. Tuning overrides for kernel sweeps
+ *    (environment variables QR_GEMV_*, QR_GEMM_*, QR_GROUPED_*, QR_W4_*, QR_COUNT_*, QR_FUSE_*,
+ *    QR_FORCE_VARIANT, and the plan trace QR_TRACE) are read only if QR_TUNE is set (non-empty, not "0") when
+ *    the library is loaded; without it no variable is consulted, so the output bits of a call cannot change
+ *    with the environment.
  */
 #ifndef QR_H
 #define QR_H

@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+
 #include "qr_internal.hpp"
 
 namespace {
@@ -80,6 +81,44 @@ qr_status quantize_common(const void *in, qr_dtype in_type, int64_t rows, int64_
     return hip_status(e, "quantize launch");
 }
 
+// validation shared by the two W8A8 linear entry points; on QR_OK, *p is the plan and *empty tells whether the
+// call has nothing to do (m == 0 or n == 0)
+qr_status check_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes, const float *x_scales,
+                       const void *w_codes, const float *w_scales, const void *y, qr_dtype y_type,
+                       const void *acc_out, qr::LinearPlan *p, bool *empty) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if ((st = check_dtype(y_type, "output dtype")) != QR_OK) return st;
+    if (m < 0 || n < 0) return fail(QR_ERR_ARG, "negative size m=%lld n=%lld", (long long)m, (long long)n);
+    if ((st = check_k(k)) != QR_OK) return st;
+    if (m > kMaxRows || n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "m or n too large");
+    *empty = m == 0 || n == 0;
+    if (*empty) return ok();
+    if (x_codes == nullptr || x_scales == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
+        return fail(QR_ERR_ARG, "null operand pointer");
+    if (!aligned(x_codes, 16) || !aligned(w_codes, 16)) return fail(QR_ERR_ALIGN, "codes must be 16-byte aligned");
+    if (!aligned(x_scales, 4) || !aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    if (!aligned(y, 16) || (acc_out != nullptr && !aligned(acc_out, 16)))
+        return fail(QR_ERR_ALIGN, "y and acc_out must be 16-byte aligned");
+    *p = qr::plan_linear((int)q, m, n, k);
+    return QR_OK;
+}
+
+qr_status run_linear(const qr::LinearPlan &p, qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes,
+                     const float *x_scales, const void *w_codes, const float *w_scales, void *y, qr_dtype y_type,
+                     void *acc_out, void *workspace, void *stream) {
+    if (qr::trace_enabled())
+        fprintf(stderr, "[qr] linear q=%d m=%lld n=%lld k=%lld kind=%d mt=%d waves=%d unroll=%d tiles=%d pf=%d ksub=%d gemm=%d "
+                "bm=%d splits=%d dp=%d ws=%zu\n",
+                (int)q, (long long)m, (long long)n, (long long)k, p.kind, p.m_tiles, p.waves, p.unroll, p.tiles,
+                p.prefetch ? 1 : 0, p.kind == 0 ? p.ksub : 1, p.gemm.tile, p.gemm.bm, p.kind == 0 ? p.splits : p.gemm.splits,
+                p.kind == 0 ? 0 : p.gemm.dp_tiles, p.ws_bytes);
+    const hipError_t e = qr::launch_linear(p, (int)q, m, n, k, static_cast<const uint8_t *>(x_codes), x_scales,
+                                           static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
+                                           acc_out, workspace, static_cast<hipStream_t>(stream));
+    return hip_status(e, "linear launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,36 +142,17 @@ size_t qr_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k, int64_t n
 qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes, const float *x_scales,
                          const void *w_codes, const float *w_scales, void *y, qr_dtype y_type, void *acc_out,
                          void *workspace, size_t workspace_bytes, void *stream) {
-    qr_status st;
-    if ((st = check_q(q)) != QR_OK) return st;
-    if ((st = check_dtype(y_type, "output dtype")) != QR_OK) return st;
-    if (m < 0 || n < 0) return fail(QR_ERR_ARG, "negative size m=%lld n=%lld", (long long)m, (long long)n);
-    if ((st = check_k(k)) != QR_OK) return st;
-    if (m > kMaxRows || n > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "m or n too large");
-    if (m == 0 || n == 0) return ok();
-    if (x_codes == nullptr || x_scales == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
-        return fail(QR_ERR_ARG, "null operand pointer");
-    if (!aligned(x_codes, 16) || !aligned(w_codes, 16)) return fail(QR_ERR_ALIGN, "codes must be 16-byte aligned");
-    if (!aligned(x_scales, 4) || !aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
-    if (!aligned(y, 16) || (acc_out != nullptr && !aligned(acc_out, 16)))
-        return fail(QR_ERR_ALIGN, "y and acc_out must be 16-byte aligned");
-    const qr::LinearPlan p = qr::plan_linear((int)q, m, n, k);
+    qr::LinearPlan p;
+    bool empty = false;
+    qr_status st = check_linear(q, m, n, k, x_codes, x_scales, w_codes, w_scales, y, y_type, acc_out, &p, &empty);
+    if (st != QR_OK || empty) return st;
     if (p.ws_bytes > 0) {
         if (workspace == nullptr || workspace_bytes < p.ws_bytes)
             return fail(QR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
                         workspace == nullptr ? (size_t)0 : workspace_bytes);
         if (!aligned(workspace, 256)) return fail(QR_ERR_ALIGN, "workspace must be 256-byte aligned");
     }
-    if (getenv("QR_TRACE") != nullptr)
-        fprintf(stderr, "[qr] linear q=%d m=%lld n=%lld k=%lld kind=%d mt=%d waves=%d unroll=%d tiles=%d pf=%d ksub=%d gemm=%d "
-                "bm=%d splits=%d dp=%d ws=%zu\n",
-                (int)q, (long long)m, (long long)n, (long long)k, p.kind, p.m_tiles, p.waves, p.unroll, p.tiles,
-                p.prefetch ? 1 : 0, p.kind == 0 ? p.ksub : 1, p.gemm.tile, p.gemm.bm, p.kind == 0 ? p.splits : p.gemm.splits,
-                p.kind == 0 ? 0 : p.gemm.dp_tiles, p.ws_bytes);
-    const hipError_t e = qr::launch_linear(p, (int)q, m, n, k, static_cast<const uint8_t *>(x_codes), x_scales,
-                                           static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
-                                           acc_out, workspace, static_cast<hipStream_t>(stream));
-    return hip_status(e, "linear launch");
+    return run_linear(p, q, m, n, k, x_codes, x_scales, w_codes, w_scales, y, y_type, acc_out, workspace, stream);
 }
 
 size_t qr_w8a8_linear_bf16_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k) {
@@ -165,7 +185,7 @@ qr_status qr_w8a8_linear_bf16(qr_qtype q, int64_t m, int64_t n, int64_t k, const
                         workspace == nullptr ? (size_t)0 : workspace_bytes);
         if (!aligned(workspace, 256)) return fail(QR_ERR_ALIGN, "workspace must be 256-byte aligned");
     }
-    if (getenv("QR_TRACE") != nullptr)
+    if (qr::trace_enabled())
         fprintf(stderr, "[qr] linear_bf16 q=%d m=%lld n=%lld k=%lld fused=%d kind=%d mt=%d waves=%d unroll=%d tiles=%d "
                 "ksub=%d ws=%zu\n",
                 (int)q, (long long)m, (long long)n, (long long)k, qr::linear_bf16_fused(p, (int)q, m, k) ? 1 : 0, p.kind,
@@ -305,7 +325,7 @@ qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const 
     if (!aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
     if (!aligned(y, 16)) return fail(QR_ERR_ALIGN, "y must be 16-byte aligned");
     const qr::W4Plan p = qr::plan_w4a16(m, n, k);
-    if (getenv("QR_TRACE") != nullptr)
+    if (qr::trace_enabled())
         fprintf(stderr, "[qr] w4a16 m=%lld n=%lld k=%lld ring=%d tiles=%d waves=%d wk=%d depth=%d xlds=%d\n",
                 (long long)m, (long long)n, (long long)k, p.ring ? 1 : 0, p.tiles, p.waves, p.wk, p.depth,
                 p.x_lds ? 1 : 0);

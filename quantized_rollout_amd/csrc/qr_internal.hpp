@@ -114,7 +114,11 @@ hipError_t launch_moe_combine(const uint16_t *y_down, int64_t rows, const float 
                               const int32_t *pair_rows, int64_t T, int k, int64_t H, uint16_t *out,
                               hipStream_t stream);
 
-// Environment overrides used for tuning sweeps (0 / -1 = automatic).
+// Environment overrides used for tuning sweeps (0 / -1 = automatic): read only when QR_TUNE was set when the
+// library was loaded (tune_enabled()); otherwise env_int returns dflt without reading the environment.
+bool tune_enabled();
 int env_int(const char *name, int dflt);
+// QR_TRACE (under QR_TUNE): each call prints its plan to stderr
+bool trace_enabled();
 
 }  // namespace qr

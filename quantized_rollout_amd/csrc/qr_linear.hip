@@ -481,25 +481,23 @@ bool launch_gemv_ksub(const LinearPlan &p, int64_t m, int64_t n, int64_t k, cons
     return false;
 }
 
+// false when the plan names no compiled variant (plan_linear only produces compiled ones; a caller that gets
+// false reports hipErrorInvalidConfiguration instead of launching anything)
 template <int QT>
-void launch_gemv_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+bool launch_gemv_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
                    const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
                    hipStream_t stream) {
-    if (p.ksub > 1) {
-        if (launch_gemv_ksub<QT, kXCodes>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, (size_t)p.waves * 1024,
-                                          nullptr, nullptr, stream))
-            return;
-        abort();  // plan_linear only produces the cases above
-    }
+    if (p.ksub > 1)
+        return launch_gemv_ksub<QT, kXCodes>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, (size_t)p.waves * 1024,
+                                             nullptr, nullptr, stream);
 #define QR_GEMV_CASE(MT_, U_, TB_, W_)                                                                          \
     if (p.m_tiles == MT_ && p.unroll == U_ && p.tiles == TB_) {                                                 \
         launch_gemv_t<QT, MT_, U_, TB_, W_>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream); \
-        return;                                                                                                 \
+        return true;                                                                                            \
     }
     QR_GEMV_VARIANTS(QR_GEMV_CASE)
 #undef QR_GEMV_CASE
-    // plan_linear only produces the cases above
-    abort();
+    return false;
 }
 
 // dynamic LDS of the GEMV with in-kernel activation quantization: the reduction area (always reserved: the codes
@@ -548,11 +546,26 @@ bool launch_gemv_fused_q(const LinearPlan &p, int64_t m, int64_t n, int64_t k, c
 
 }  // namespace
 
+// Tuning overrides (forced kernel variants, split counts, tile sizes) and the plan trace are read from the
+// environment only when QR_TUNE is set (non-empty, not "0") in the environment at the time the library is
+// loaded; otherwise every plan is the automatic one and no variable is read, so a stray variable can change
+// neither the kernels chosen nor the FP8 summation order.
+static bool read_tune_switch() {
+    const char *v = getenv("QR_TUNE");
+    return v != nullptr && *v != '\0' && !(v[0] == '0' && v[1] == '\0');
+}
+static const bool g_tune = read_tune_switch();
+
+bool tune_enabled() { return g_tune; }
+
 int env_int(const char *name, int dflt) {
+    if (!g_tune) return dflt;
     const char *v = getenv(name);
     if (v == nullptr || *v == '\0') return dflt;
     return atoi(v);
 }
+
+bool trace_enabled() { return g_tune && getenv("QR_TRACE") != nullptr; }
 
 LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unroll, bool fused_quant) {
     (void)qtype;
@@ -746,10 +759,10 @@ hipError_t launch_linear(const LinearPlan &p, int qtype, int64_t m, int64_t n, i
                          const float *xs, const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out,
                          void *workspace, hipStream_t stream) {
     if (p.kind == 0) {
-        if (qtype == kInt8)
-            launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
-        else
-            launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+        const bool ok = qtype == kInt8
+                            ? launch_gemv_q<kInt8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream)
+                            : launch_gemv_q<kFp8>(p, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+        if (!ok) return hipErrorInvalidConfiguration;
     } else {
         return launch_gemm(p.gemm, qtype, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
     }

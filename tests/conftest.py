@@ -4,6 +4,10 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# The library reads its tuning overrides (QR_GEMV_*, QR_GEMM_*, ...) and QR_TRACE only when QR_TUNE is set at
+# load time; the tests force kernel variants through them, so the switch is set before anything loads libqr.so.
+os.environ.setdefault("QR_TUNE", "1")
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 

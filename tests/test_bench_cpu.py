@@ -25,8 +25,9 @@ def _write_counters(directory, counter, rows):
 
 
 def test_traffic_summary_scales_by_the_copy(tmp_path):
-    row = "a3_linear_m64"
-    nbytes, _, launches = bench.DecoderStack.row_work()[row]
+    row = "a3_fp8_gate_up_m2048"
+    nbytes, _ = bench.kernel_work(row)
+    launches = 1
     copy_kib = bench.TRAFFIC_COPY_BYTES / 1024
     neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel>"
     # an earlier copy-like kernel from set-up, then the two markers around 2 passes of the row; the fetch
@@ -40,7 +41,8 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert fields["traffic_row"] == row
     assert int(fields["traffic_bytes_per_launch"]) == (100 * 2 + 10) * 1024
     assert fields["traffic_sources_sha256"] == bench.sources_digest(row)
-    assert "| algorithmic (what the method must move) | %d |" % (nbytes // launches) in md
+    assert "| algorithmic (what the method must move) | %d |" % nbytes in md
+    assert nbytes == 37888 * 3584 + 4 * 37888 + 2048 * 3584 + 4 * 2048 + 2 * 2048 * 37888
     # a call that runs two kernels (a split-K reduction after the linear): both count toward that call
     fetch2 = fetch[:-1] + [("qr::splitk_reduce_kernel", 50.0)] * (2 * launches) + fetch[-1:]
     write2 = write[:-1] + [("qr::splitk_reduce_kernel", 4.0)] * (2 * launches) + write[-1:]
@@ -60,16 +62,28 @@ def test_traffic_is_only_reported_for_the_current_sources(tmp_path, monkeypatch)
     csrc.mkdir(parents=True)
     for name in bench.SHARED_SOURCES + sum(bench.ROW_SOURCES.values(), []) + ["qr_moe.hip"]:
         (csrc / name).write_text("v1 " + name)
-    digest = bench.sources_digest("a3_linear_m64")
+    digest = bench.sources_digest("a3_fp8_gate_up_m2048")
     (tmp_path / "profiles" / "traffic_x.md").write_text(
-        "traffic_row: a3_linear_m64\ntraffic_bytes_per_launch: 123\ntraffic_sources_sha256: %s\n" % digest)
-    assert bench.read_traffic("a3_linear_m64") == 123
-    assert bench.read_traffic("a1_quantize_weights") is None
+        "traffic_row: a3_fp8_gate_up_m2048\ntraffic_bytes_per_launch: 123\ntraffic_sources_sha256: %s\n" % digest)
+    assert bench.read_traffic("a3_fp8_gate_up_m2048") == 123
+    assert bench.read_traffic("a3_fp8_gate_up_m512") is None
     (csrc / "qr_moe.hip").write_text("v2")  # not a source of the row's kernels
-    assert bench.read_traffic("a3_linear_m64") == 123
+    assert bench.read_traffic("a3_fp8_gate_up_m2048") == 123
     (csrc / "qr_linear.hip").write_text("v2")
-    assert bench.read_traffic("a3_linear_m64") is None
+    assert bench.read_traffic("a3_fp8_gate_up_m2048") is None
     (csrc / "qr_linear.hip").write_text("v1 qr_linear.hip")
-    assert bench.read_traffic("a3_linear_m64") == 123
+    assert bench.read_traffic("a3_fp8_gate_up_m2048") == 123
     (csrc / "qr_device.hpp").write_text("v2")
-    assert bench.read_traffic("a3_linear_m64") is None
+    assert bench.read_traffic("a3_fp8_gate_up_m2048") is None
+
+
+def test_step_work_and_roofline_bounds():
+    """The step's operations (2 M N K over every linear, layer and batch) and the binding roofline per batch."""
+    nb, no = bench.Dense7B.step_work()
+    lins = [(4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944)]
+    ms = (1, 16, 128, 512, 2048)
+    assert no == bench.LAYERS * sum(2 * m * n * k for m in ms for n, k in lins)
+    assert nb == bench.LAYERS * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for m in ms for n, k in lins)
+    assert [bench.bound_of(m) for m in ms] == ["hbm", "hbm", "hbm", "mfma", "mfma"]
+    assert abs(bench.frac_of(2048, 0, 5e12, 1.0) - 1.0) < 1e-12        # 5 TFLOP in 1 ms = 5 PFLOP/s
+    assert abs(bench.frac_of(16, 8e9, 0, 1.0) - 1.0) < 1e-12           # 8 GB in 1 ms = 8 TB/s
