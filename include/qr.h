@@ -100,6 +100,23 @@ qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The W8A8 linear of qr_w8a8_linear for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and the same result bit for bit (y and
+ * acc_out) as qr_w8a8_linear, with no workspace argument. Where K is split across workgroups the partial sums go
+ * to a device scratch array of QR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends; a call whose plan needs more (qr_workspace_bytes(q, m, n, k, 1) > QR_NOALLOC_SCRATCH_BYTES)
+ * returns QR_ERR_UNSUPPORTED before launching anything. The call allocates nothing and calls no allocating
+ * routine. The scratch of the current device is used, so `stream` must belong to the current device; every
+ * call on one GPU shares that scratch, so calls that overlap on one GPU (on different streams, or from
+ * different threads) race on it and must be serialized by the caller. Its contents are not preserved
+ * between calls and need no initialisation. Other arguments, limits and errors as for qr_w8a8_linear.
+ */
+#define QR_NOALLOC_SCRATCH_BYTES (64u << 20)
+qr_status qr_w8a8_linear_noalloc(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes,
+                                 const float *x_scales, const void *w_codes, const float *w_scales, void *y,
+                                 qr_dtype y_type, void *acc_out, void *stream);
+
+/*
  * The W8A8 linear on bfloat16 activations (next row: the activation quantization fused with the linear):
  * the same result, bit for bit, as qr_quantize_acts(x, QR_BF16, m, k, s, q, ...) followed by qr_w8a8_linear on
  * its codes and scales (including acc_out). For single-token decode (m = 1; with FP8 for k <= 8192) the

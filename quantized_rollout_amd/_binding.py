@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
            "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
            "qr_w4a16_linear", "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_w8a8_linear_bf16_workspace_bytes",
-           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine")
+           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine", "qr_w8a8_linear_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # QR_NOALLOC_SCRATCH_BYTES
 W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
 
@@ -62,6 +63,7 @@ def lib():
                 L.qr_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
                 L.qr_requantize_weights.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
                 L.qr_w8a8_linear_bf16.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+                L.qr_w8a8_linear_noalloc.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp]
                 L.qr_w8a8_linear_bf16_workspace_bytes.argtypes = [i32, i64, i64, i64]
                 L.qr_w8a8_linear_bf16_workspace_bytes.restype = sz
                 L.qr_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
@@ -70,7 +72,7 @@ def lib():
                 for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
                           "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear",
                           "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_moe_route", "qr_silu_mul_quantize",
-                          "qr_moe_combine"):
+                          "qr_moe_combine", "qr_w8a8_linear_noalloc"):
                     getattr(L, f).restype = ctypes.c_int
                 L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
                 L.qr_workspace_bytes.restype = sz
@@ -262,6 +264,33 @@ def qr_w8a8_linear(qtype, x_codes, x_scales, w_codes, w_scales, y=None, y_dtype=
     ws = (workspace if workspace is not None else default_workspace(dev)).get(nbytes)
     _check(lib().qr_w8a8_linear(int(qtype), m, n, k, _ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales),
                                 _ptr(y), _dtype_code(y), _ptr(acc_out), _ptr(ws), nbytes, _stream(stream)))
+    return (y, acc_out) if want_acc else y
+
+
+def qr_w8a8_linear_noalloc(qtype, x_codes, x_scales, w_codes, w_scales, y=None, y_dtype=torch.bfloat16,
+                           acc_out=None, stream=None):
+    """qr_w8a8_linear without a workspace: split-K partial sums go to the library's device scratch (the same
+    result bit for bit; QRError QR_ERR_UNSUPPORTED where the plan needs more scratch than the library holds).
+    Allocates nothing when y (and acc_out, if wanted) are passed in."""
+    m, k = x_codes.shape
+    n, k2 = w_codes.shape
+    _need(k == k2, "k mismatch")
+    dev = x_codes.device
+    for t in (x_codes, x_scales, w_codes, w_scales):
+        _need(t.is_cuda and t.is_contiguous(), "operands must be contiguous CUDA tensors")
+    _need(x_codes.dtype == torch.uint8 and w_codes.dtype == torch.uint8, "codes must be uint8")
+    _need(x_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
+    _need(x_scales.shape == (m,) and w_scales.shape == (n,), "scale shapes")
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype, device=dev)
+    _need(y.shape == (m, n) and y.is_contiguous(), "bad y")
+    want_acc = acc_out is not None and acc_out is not False
+    if acc_out is True:
+        acc_out = torch.empty((m, n), dtype=torch.int32 if qtype == QR_INT8 else torch.float32, device=dev)
+    elif acc_out is False:
+        acc_out = None
+    _check(lib().qr_w8a8_linear_noalloc(int(qtype), m, n, k, _ptr(x_codes), _ptr(x_scales), _ptr(w_codes),
+                                        _ptr(w_scales), _ptr(y), _dtype_code(y), _ptr(acc_out), _stream(stream)))
     return (y, acc_out) if want_acc else y
 
 

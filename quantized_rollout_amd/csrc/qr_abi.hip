@@ -10,6 +10,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 
 #include "qr_internal.hpp"
 
@@ -119,6 +121,38 @@ qr_status run_linear(const qr::LinearPlan &p, qr_qtype q, int64_t m, int64_t n, 
     return hip_status(e, "linear launch");
 }
 
+// Device scratch of qr_w8a8_linear_noalloc: the split-K partial sums of a linear whose K is split across
+// workgroups, for callers that cannot allocate. Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` is only a host-side stand-in for the symbol: its device address on each device
+// comes from hipGetSymbolAddress (taken once per device, with that device current) and only that address is
+// ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[QR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the device address of the current device's scratch (looked up on the first call on that device)
+qr_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(QR_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the device scratch");
+            if (ptr == nullptr) return fail(QR_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch");
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return QR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +187,25 @@ qr_status qr_w8a8_linear(qr_qtype q, int64_t m, int64_t n, int64_t k, const void
         if (!aligned(workspace, 256)) return fail(QR_ERR_ALIGN, "workspace must be 256-byte aligned");
     }
     return run_linear(p, q, m, n, k, x_codes, x_scales, w_codes, w_scales, y, y_type, acc_out, workspace, stream);
+}
+
+qr_status qr_w8a8_linear_noalloc(qr_qtype q, int64_t m, int64_t n, int64_t k, const void *x_codes,
+                                 const float *x_scales, const void *w_codes, const float *w_scales, void *y,
+                                 qr_dtype y_type, void *acc_out, void *stream) {
+    qr::LinearPlan p;
+    bool empty = false;
+    qr_status st = check_linear(q, m, n, k, x_codes, x_scales, w_codes, w_scales, y, y_type, acc_out, &p, &empty);
+    if (st != QR_OK || empty) return st;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        if (p.ws_bytes > (size_t)QR_NOALLOC_SCRATCH_BYTES)
+            return fail(QR_ERR_UNSUPPORTED,
+                        "this linear splits K over %zu bytes of partial sums, more than the %zu-byte device scratch "
+                        "of qr_w8a8_linear_noalloc; call qr_w8a8_linear with a workspace",
+                        p.ws_bytes, (size_t)QR_NOALLOC_SCRATCH_BYTES);
+        if ((st = scratch_address(&ws)) != QR_OK) return st;
+    }
+    return run_linear(p, q, m, n, k, x_codes, x_scales, w_codes, w_scales, y, y_type, acc_out, ws, stream);
 }
 
 size_t qr_w8a8_linear_bf16_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k) {

@@ -74,6 +74,33 @@ def test_linear_validation():
     assert call(n=0, x=NULL) == B.QR_OK
 
 
+def test_linear_noalloc_validation():
+    """The no-allocation linear validates like qr_w8a8_linear and rejects plans whose split-K partial sums exceed
+    its device scratch before launching anything (no GPU call is reached on any of these paths)."""
+    L = B.lib()
+    base = dict(q=0, m=16, n=1536, k=8960, x=P, xs=P, w=P, wsc=P, y=P, yt=1, acc=NULL)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.qr_w8a8_linear_noalloc(a["q"], a["m"], a["n"], a["k"], a["x"], a["xs"], a["w"], a["wsc"], a["y"],
+                                        a["yt"], a["acc"], S0)
+
+    assert call(k=8968) == B.QR_ERR_UNSUPPORTED and "multiple of 16" in _err()
+    assert call(m=-1) == B.QR_ERR_ARG
+    assert call(q=7) == B.QR_ERR_ARG
+    assert call(x=NULL) == B.QR_ERR_ARG
+    assert call(w=MIS) == B.QR_ERR_ALIGN
+    assert call(m=0) == B.QR_OK and _err() == ""
+    # a plan whose partial sums exceed the scratch: rejected with a clear message
+    big = None
+    for m, n, k in ((1024, 3584, 131072), (2048, 3584, 131072)):
+        if B.qr_workspace_bytes(0, m, n, k) > B.NOALLOC_SCRATCH_BYTES:
+            big = (m, n, k)
+            break
+    assert big is not None
+    assert call(m=big[0], n=big[1], k=big[2]) == B.QR_ERR_UNSUPPORTED and "scratch" in _err()
+
+
 def test_quantize_validation():
     L = B.lib()
     for fn in (L.qr_quantize_weights, L.qr_quantize_acts):
