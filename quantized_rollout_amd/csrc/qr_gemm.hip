@@ -522,6 +522,324 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     });
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// Wide-wave GEMM: 256 x 256 outputs per workgroup and 2 x 2 wavefronts of 128 x 128
+// outputs each (4 x 4 fragments of the 32x32 MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit
+// block scales, or two v_mfma_i32_32x32x32_i8), 256 accumulators per lane. A wavefront's fragments of one
+// 64-byte K step are 8 reads of 2 KiB for 16 MFMAs, half of what the ring kernel's 64 x 64 wavefronts read per
+// MFMA, so the LDS carries less per operation.
+// K advances in 128-byte stages through two LDS buffers. Every thread loads its 16-byte pieces of stage s + 1
+// into registers (raw buffer loads: rows past m or n and bytes past k read as zero) while the MFMAs of stage s
+// run, and writes them to the other buffer before the stage's barrier. A buffer holds the stage's 256
+// activation rows, then its 256 weight rows, 128 bytes each, with logical 16-byte piece c of row r stored at
+// physical piece c ^ ((r / 2) mod 8): a fragment read (32 consecutive rows at one logical piece, served 16 lanes
+// per cycle over 64 four-byte banks) and a row-major staging write then touch distinct banks. A fragment gives
+// lane l row (l & 31) and, for the 64-byte step u of the stage, logical pieces 4 u + 2 (l >> 5) and
+// 4 u + 2 (l >> 5) + 1 (FP8, one MFMA of K = 64) or 4 u + (l >> 5) and 4 u + 2 + (l >> 5) (INT8, two MFMAs of
+// K = 32), the same for both operands, so the dot products are those of the plain definition. Work items
+// (tiles, K splits, whole-K tiles then a split column band) are ordered per XCD as in the ring kernel.
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kWideK = 128;     // K bytes per stage
+constexpr int kWideN = 256;     // weight rows (output channels) per tile
+constexpr int kWideM = 256;     // activation rows per tile
+constexpr int kWideThreads = 256;
+constexpr int kWideBuf = (kWideM + kWideN) * kWideK;  // bytes per LDS buffer (64 KiB)
+constexpr int kWideChunks = kWideM * kWideK / 16 / kWideThreads;  // 16-byte pieces per thread per operand (8)
+
+__device__ __forceinline__ int wide_swizzle(int r) { return (r >> 1) & 7; }
+
+template <int QT>
+__global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
+    int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq, const float *__restrict__ xs,
+    const uint8_t *__restrict__ wq, const float *__restrict__ ws, void *__restrict__ y, int y_bf16,
+    void *__restrict__ acc_out, int tiles_m, int tiles_n, int splits, int stages_per_split,
+    void *__restrict__ partial, int dp_tiles) {
+    typedef typename Acc32<QT>::type acc_t;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];  // two stage buffers of kWideBuf bytes
+
+    // work item: the same order as the ring kernel (each XCD a contiguous run; whole-K tiles first)
+    const int tiles = tiles_m * tiles_n;
+    const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
+    int split = 0, tile;
+    bool to_partial;
+    if (dp_tiles == 0) {
+        const int total = tiles * splits;
+        const int per_xcd = (total + 7) / 8;
+        const int order = xcd * per_xcd + slot;
+        if (order >= total) return;
+        split = order / tiles;
+        tile = order % tiles;
+        to_partial = splits > 1;
+    } else {
+        const int dpx = dp_tiles / 8;
+        if (slot < dpx) {
+            tile = xcd * dpx + slot;
+            to_partial = false;
+        } else {
+            const int rem = tiles - dp_tiles, pieces = rem * splits;
+            const int p = xcd * ((pieces + 7) / 8) + (slot - dpx);
+            if (p >= pieces) return;
+            split = p / rem;
+            tile = dp_tiles + p % rem;
+            to_partial = true;
+        }
+    }
+    const int64_t m0 = (int64_t)(tile % tiles_m) * kWideM;
+    const int64_t n0 = (int64_t)(tile / tiles_m) * kWideN;
+    const int64_t all_stages = (k + kWideK - 1) / kWideK;
+    const int64_t st0 = to_partial ? (int64_t)split * stages_per_split : 0;
+    const int64_t stages = to_partial ? std::min<int64_t>(stages_per_split, all_stages - st0) : all_stages;
+    const int64_t full = k / kWideK;  // stages with every piece inside k
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // staging: piece i of this thread is chunk t + 256 i of the stage, row (t / 8) + 32 i, logical piece t % 8;
+    // the row's swizzle (r / 2) mod 8 does not depend on i, so piece i sits 32 rows (4 KiB) after piece 0
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xq), (short)0,
+                                                                         (int)(m * k), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wq), (short)0,
+                                                                         (int)(n * k), kBufferFlags);
+    const int srow = t >> 3, spiece = t & 7;
+    const int lds0 = srow * kWideK + 16 * (spiece ^ wide_swizzle(srow));  // + 4096 i; weights + kWideM rows
+    const uint32_t rowstep = (uint32_t)(32 * k);                           // 32 rows of the operand
+    const uint32_t offa0 = (uint32_t)((m0 + srow) * k + 16 * spiece);
+    const uint32_t offb0 = (uint32_t)((n0 + srow) * k + 16 * spiece);
+    const int64_t rows_a = m - m0 - srow, rows_b = n - n0 - srow;  // piece i is in range while 32 i < rows
+    v4i ra[kWideChunks], rb[kWideChunks];
+    auto load = [&](int64_t gst) {  // global stage gst into the staging registers
+        const uint32_t k0 = (uint32_t)(gst * kWideK);
+        const bool kin = gst < full || (int64_t)k0 + 16 * spiece < k;
+#pragma unroll
+        for (int i = 0; i < kWideChunks; ++i) {
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rsa, (kin && 32 * i < rows_a) ? offa0 + rowstep * i + k0 : kOutOfRange, 0, 0);
+            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rsb, (kin && 32 * i < rows_b) ? offb0 + rowstep * i + k0 : kOutOfRange, 0, 0);
+        }
+    };
+    auto store = [&](uint8_t *buf) {  // the staging registers into an LDS buffer
+#pragma unroll
+        for (int i = 0; i < kWideChunks; ++i) {
+            *reinterpret_cast<v4i *>(buf + lds0 + 4096 * i) = ra[i];
+            *reinterpret_cast<v4i *>(buf + kWideM * kWideK + lds0 + 4096 * i) = rb[i];
+        }
+    };
+
+    acc_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{};
+
+    // one 64-byte step u of a stage: 16 fragment reads (lane row (l & 31), half h = l >> 5), 16 MFMA tiles; both
+    // split into single instructions so that the pipeline below can interleave them with other memory operations
+    const int fr = lane & 31, h = lane >> 5;
+    const int q0 = QT == kInt8 ? h : 2 * h, q1 = QT == kInt8 ? 2 + h : 2 * h + 1;
+    const int swz = wide_swizzle(fr);  // rows wm 128 + 32 i + fr and 128 wn + 32 j + fr share it
+    struct Frags {
+        uint4 a[4][2], b[4][2];
+    };
+    // read x of a step (x = 0..15): A fragment x / 4 piece x % 2 for x < 8, then B fragment (x - 8) / 2 piece x % 2
+    auto read_one = [&](const uint8_t *buf, int u, Frags &f, auto X) {
+        constexpr int x = decltype(X)::value;
+        const int pc = 16 * ((4 * u + ((x & 1) ? q1 : q0)) ^ swz);
+        if constexpr (x < 8)
+            f.a[x / 2][x & 1] = *reinterpret_cast<const uint4 *>(buf + (wm * 128 + (x / 2) * 32 + fr) * kWideK + pc);
+        else
+            f.b[(x - 8) / 2][x & 1] =
+                *reinterpret_cast<const uint4 *>(buf + (kWideM + wn * 128 + ((x - 8) / 2) * 32 + fr) * kWideK + pc);
+    };
+    // MFMA tile x of a step: fragments (x / 4, x % 4)
+    auto mfma_one = [&](const Frags &f, auto X) {
+        constexpr int x = decltype(X)::value, i = x / 4, j = x % 4;
+        if constexpr (QT == kInt8) {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(f.a[i][0]), v4(f.b[j][0]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(f.a[i][1]), v4(f.b[j][1]), acc[i][j], 0, 0, 0);
+        } else {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8(f.a[i][0], f.a[i][1]),
+                                                                         v8(f.b[j][0], f.b[j][1]), acc[i][j], 0, 0,
+                                                                         0, 127, 0, 127);
+        }
+    };
+    // staging piece x (x = 0..15): activation piece x for x < 8, weight piece x - 8 otherwise
+    auto store_one = [&](uint8_t *buf, auto X) {
+        constexpr int x = decltype(X)::value;
+        if constexpr (x < 8)
+            *reinterpret_cast<v4i *>(buf + lds0 + 4096 * x) = ra[x];
+        else
+            *reinterpret_cast<v4i *>(buf + kWideM * kWideK + lds0 + 4096 * (x - 8)) = rb[x - 8];
+    };
+    auto load_one = [&](int64_t gst, auto X) {
+        constexpr int x = decltype(X)::value;
+        const uint32_t k0 = (uint32_t)(gst * kWideK);
+        const bool kin = gst < full || (int64_t)k0 + 16 * spiece < k;
+        if constexpr (x < 8)
+            ra[x] = __builtin_amdgcn_raw_buffer_load_b128(
+                rsa, (kin && 32 * x < rows_a) ? offa0 + rowstep * x + k0 : kOutOfRange, 0, 0);
+        else
+            rb[x - 8] = __builtin_amdgcn_raw_buffer_load_b128(
+                rsb, (kin && 32 * (x - 8) < rows_b) ? offb0 + rowstep * (x - 8) + k0 : kOutOfRange, 0, 0);
+    };
+
+    // Pipeline (one wavefront per SIMD, so each wavefront hides its own latencies): stage s + 1 is in the staging
+    // registers while stage s runs, and the fragments of one 64-byte step are read while the MFMAs of the other
+    // run. Stage s runs in two phases around one barrier:
+    //  A: the first step's 16 MFMA tiles, each followed by one of the second step's fragment reads, one write of
+    //     the staged stage s + 1 into the other buffer (every wavefront finished reading it before the previous
+    //     barrier) and one load of stage s + 2;
+    //  the barrier (each wavefront's LDS accesses retired first): stage s's buffer is no longer read and stage
+    //     s + 1's is written;
+    //  B: the second step's 16 MFMA tiles, each followed by one of stage s + 1's first-step fragment reads.
+    // The memory instructions thus issue while the matrix core is busy. Scheduling barriers between the groups
+    // keep the compiler from regrouping them; the waits it inserts then cover one group's dependences only.
+    Frags f0, f1;
+    auto phase_a = [&](const uint8_t *cur, uint8_t *nxt, int64_t s, auto store_c, auto load_c) {
+        constexpr bool kStore = decltype(store_c)::value, kLoad = decltype(load_c)::value;
+        unroll<16>([&](auto X) {
+            mfma_one(f0, X);
+            read_one(cur, 1, f1, X);
+            if constexpr (kStore) store_one(nxt, X);
+            if constexpr (kLoad) load_one(st0 + s + 2, X);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    auto phase_b = [&](const uint8_t *nxt, auto next_c) {
+        constexpr bool kNext = decltype(next_c)::value;
+        unroll<16>([&](auto X) {
+            mfma_one(f1, X);
+            if constexpr (kNext) read_one(nxt, 0, f0, X);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    typedef std::integral_constant<bool, true> yes;
+    typedef std::integral_constant<bool, false> no;
+    load(st0);
+    store(lds);
+    if (stages > 1) load(st0 + 1);
+    __syncthreads();
+    unroll<16>([&](auto X) { read_one(lds, 0, f0, X); });
+    int64_t s = 0;
+    for (; s + 2 < stages; ++s) {  // steady state: stage s + 2 exists
+        const uint8_t *cur = lds + (int)(s & 1) * kWideBuf;
+        uint8_t *nxt = lds + (int)((s + 1) & 1) * kWideBuf;
+        phase_a(cur, nxt, s, yes{}, yes{});
+        __syncthreads();
+        phase_b(nxt, yes{});
+    }
+    if (s + 1 < stages) {  // the last but one stage: nothing more to load
+        const uint8_t *cur = lds + (int)(s & 1) * kWideBuf;
+        uint8_t *nxt = lds + (int)((s + 1) & 1) * kWideBuf;
+        phase_a(cur, nxt, s, yes{}, no{});
+        __syncthreads();
+        phase_b(nxt, yes{});
+        ++s;
+    }
+    {  // the last stage
+        const uint8_t *cur = lds + (int)(s & 1) * kWideBuf;
+        phase_a(cur, nullptr, s, no{}, no{});
+        __syncthreads();
+        phase_b(nullptr, no{});
+    }
+    __syncthreads();  // every fragment read is retired before the epilogue reuses the LDS
+
+    const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
+    if (to_partial) {
+        typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
+        const int64_t n_lo = dp_tiles == 0 ? 0 : (int64_t)(dp_tiles / tiles_m) * kWideN, nb = n - n_lo;
+        part_t *P = static_cast<part_t *>(partial) + (int64_t)split * m * nb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = wcol0 + j * 32 + fr;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                    if (row < m && col < n) P[row * nb + (col - n_lo)] = acc[i][j][e];
+                }
+            }
+        return;
+    }
+
+    // epilogue: y = acc * x_scale[row] * w_scale[col]
+    float sw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t col = wcol0 + j * 32 + fr;
+        sw[j] = ws[col < n ? col : n - 1];
+    }
+    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + kWideN <= n;  // uniform per workgroup
+    if (fast) {
+        // the wavefront's 128 x 128 bf16 outputs go through its own 32 KiB of LDS (row stride 256 bytes; the last
+        // barrier of the loop has retired every fragment read), then out as 16-byte row pieces with buffer stores
+        // (rows past m fall outside the buffer and are dropped); a wavefront reads back only what it wrote
+        constexpr int kStride = 256;
+        uint8_t *stage = lds + wave * (128 * kStride);
+        unroll<4>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            float sx[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                sx[e] = xs[row < m ? row : m - 1];
+            }
+            unroll<4>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int r = i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                    const float v = acc_to_f32(acc[i][j][e]) * sx[e] * sw[j];
+                    *reinterpret_cast<uint16_t *>(stage + r * kStride + (j * 32 + fr) * 2) = f32_to_bf16(v);
+                }
+            });
+        });
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)(m * n * 2), kBufferFlags);
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int c = lane + 64 * q;  // 16-byte piece: row c / 16, columns 8 (c % 16) ..
+            const int r = c >> 4, c8 = (c & 15) * 8;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kStride + c8 * 2);
+            const int64_t row = wrow0 + r;
+            const uint32_t off = row < m ? (uint32_t)((row * n + wcol0 + c8) * 2) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ry, off, 0, 0);
+        }
+        return;
+    }
+    unroll<4>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        float sx[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+            sx[e] = xs[row < m ? row : m - 1];
+        }
+        unroll<4>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const int64_t col = wcol0 + j * 32 + fr;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                if (row < m && col < n) {
+                    const float v = acc_to_f32(acc[i][j][e]) * sx[e] * sw[j];
+                    if (y_bf16)
+                        static_cast<uint16_t *>(y)[row * n + col] = f32_to_bf16(v);
+                    else
+                        static_cast<float *>(y)[row * n + col] = v;
+                    if (acc_out != nullptr) {
+                        if constexpr (QT == kInt8)
+                            static_cast<int32_t *>(acc_out)[row * n + col] = acc[i][j][e];
+                        else
+                            static_cast<float *>(acc_out)[row * n + col] = acc[i][j][e];
+                    }
+                }
+            }
+        });
+    });
+}
+
 // Split-K: acc = the partial sums of the splits added in split order (exact for INT32; a fixed order for FP32,
 // so repeated calls agree bit for bit), then the epilogue y = acc * x_scale[row] * w_scale[col]. The partial
 // sums cover the columns n_lo .. n - 1 ([split][m][nb], nb = n - n_lo). Four consecutive outputs per thread
@@ -586,6 +904,30 @@ hipError_t launch_ring(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const
     return hipGetLastError();
 }
 
+template <int QT>
+hipError_t launch_wide(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
+                       const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
+                       hipStream_t stream) {
+    // more than 64 KiB of dynamic LDS per workgroup is opted into once per kernel
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wide_kernel<QT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kWideBuf);
+    if (attr != hipSuccess) return attr;
+    const int tiles_m = (int)((m + kWideM - 1) / kWideM), tiles_n = (int)((n + kWideN - 1) / kWideN);
+    int grid;
+    if (g.dp_tiles == 0) {
+        grid = ((tiles_m * tiles_n * g.splits + 7) / 8) * 8;
+    } else {
+        const int pieces = (tiles_m * tiles_n - g.dp_tiles) * g.splits;
+        grid = 8 * (g.dp_tiles / 8 + (pieces + 7) / 8);
+    }
+    hipLaunchKernelGGL((gemm_wide_kernel<QT>), dim3(grid), dim3(kWideThreads), 2 * kWideBuf, stream, m, n, k, xq,
+                       xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits, g.stages_per_split,
+                       workspace, g.dp_tiles);
+    if (g.splits > 1)
+        launch_splitk_reduce(QT, m, n, g.splits, workspace, xs, ws, y, y_bf16, acc_out, stream, g.n_lo);
+    return hipGetLastError();
+}
+
 template <int QT, int BM, int BN>
 hipError_t launch_t(int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs, const uint8_t *wq,
                     const float *ws, void *y, bool y_bf16, void *acc_out, hipStream_t stream) {
@@ -606,6 +948,8 @@ hipError_t launch_q(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const ui
             if (g.bm == 128)
                 return launch_ring<QT, 128>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
             return launch_ring<QT, 256>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+        case kGemmWide:
+            return launch_wide<QT>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
         case 1: return launch_t<QT, 256, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
         case 2: return launch_t<QT, 128, 256>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
         default: return launch_t<QT, 128, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
@@ -633,27 +977,37 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
             g.tile = count(256, 128) >= 256 ? 1 : (count(128, 256) >= 256 ? 2 : 3);
         return g;
     }
-    g.tile = kGemmRing;
+    // The wide-wave kernel where measured faster than the ring (MI355X, 7B-shaped FP8 linears, weights past the
+    // caches): batches above 128 rows with at least 128 output tiles of 256 x 256 or a deep K (gate/up at m = 512
+    // 98 -> 92 us and at m = 2048 282 -> 267 us, down 56 -> 54 and 149 -> 133 us, qkv at m = 2048 47 -> 45 us);
+    // the ring kernel elsewhere (its 128-row tiles at small batches, and few-tile shapes split over K: qkv and o at
+    // m = 512 29 / 27 us against 36 / 33, o at m = 2048 39 against 44 us)
+    const bool wide_pays = m > 128 && (count(kWideM, kWideN) >= 128 || k >= 8192);
+    g.tile = forced == kGemmWide || (forced < 0 && wide_pays) ? kGemmWide : kGemmRing;
     // Cost model, fitted to the 7B-shaped FP8 linears at m = 128, 512, 2048 on MI355X: a workgroup takes about
-    // 0.65 us per 64-byte stage with 128 activation rows per tile and 0.83 us with 256; workgroups beyond the
+    // 0.65 us per 64 bytes of K with 128 activation rows per tile and 0.83 us with 256; workgroups beyond the
     // 256 CUs run in further rounds; a split adds its partial sums (written and read back, about 5 TB/s) and
-    // the reduction launch (about 5 us). The cheapest (rows per tile, splits) wins; splits keep >= 4 stages.
-    const int64_t stages = (k + kRingK - 1) / kRingK;
+    // the reduction launch (about 5 us). The cheapest (rows per tile, splits) wins; splits keep >= 256 bytes of K.
+    const int stage_bytes = g.tile == kGemmWide ? kWideK : kRingK;
+    const int64_t min_stages = 256 / stage_bytes;
+    const int64_t stages = (k + stage_bytes - 1) / stage_bytes;
+    const double per64 = (double)stage_bytes / 64.0;
     const int fbm = env_int("QR_GEMM_BM", 0);
     const int fs = env_int("QR_GEMM_SPLITS", 0);
     const int64_t forced_sp = fs >= 1 ? std::min<int64_t>(fs, stages) : 0;
-    g.bm = m <= 128 ? 128 : 256;
+    g.bm = (m <= 128 && g.tile != kGemmWide) ? 128 : 256;
     g.stages_per_split = (int)stages;
     double best = 1e30;
     for (int bm : {128, 256}) {
         if ((fbm == 128 || fbm == 256) && fbm != bm) continue;
+        if (g.tile == kGemmWide && bm != kWideM) continue;
         const int64_t tiles = count(bm, kRingN);
         for (int64_t sp = forced_sp ? forced_sp : 1; sp <= (forced_sp ? forced_sp : 16); ++sp) {
-            if (!forced_sp && sp > 1 && (stages + sp - 1) / sp < 4) break;
+            if (!forced_sp && sp > 1 && (stages + sp - 1) / sp < min_stages) break;
             const int64_t sps = (stages + sp - 1) / sp;
             const int64_t used = (stages + sps - 1) / sps;  // no split without a stage
             const int64_t rounds = (tiles * used + 255) / 256;
-            double t = (double)rounds * (double)sps * (bm == 128 ? 0.65 : 0.83);
+            double t = (double)rounds * (double)sps * (bm == 128 ? 0.65 : 0.83) * per64;
             if (used > 1) t += 5.0 + (double)used * (double)m * (double)n * 8.0 / 5.0e6;
             if (t < best) {
                 best = t;
@@ -672,6 +1026,7 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
     if (fh != 0 && !(fs >= 1)) {
         for (int bm : {128, 256}) {
             if ((fbm == 128 || fbm == 256) && fbm != bm) continue;
+            if (g.tile == kGemmWide && bm != kWideM) continue;
             const int64_t tm = (m + bm - 1) / bm, tiles = count(bm, kRingN);
             if (tiles <= round || round % tm != 0 || tiles % round == 0) continue;
             const int64_t dp = tiles / round * round, rem = tiles - dp;
@@ -680,8 +1035,8 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
                 const int64_t sps = (stages + sp - 1) / sp;
                 const int64_t used = (stages + sps - 1) / sps;
                 if (used < 2) break;
-                if (fh < 2 && (sps < 4 || rem * used > round)) continue;
-                const double c = bm == 128 ? 0.65 : 0.83;
+                if (fh < 2 && (sps < min_stages || rem * used > round)) continue;
+                const double c = (bm == 128 ? 0.65 : 0.83) * per64;
                 const double t = (double)(dp / round) * (double)stages * c + (double)((rem * used + round - 1) / round) *
                                  (double)sps * c + 5.0 + (double)used * (double)m * (double)(n - n_lo) * 8.0 / 5.0e6;
                 if (fh >= 2 || t < best) {

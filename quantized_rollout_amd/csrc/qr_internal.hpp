@@ -23,11 +23,13 @@ hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t
 // Plan of a W8A8 linear (which kernel, its split of K and the workspace it needs).
 // Tiled MFMA GEMM for large m (qr_gemm.hip).
 constexpr int kGemmRing = 0;
+constexpr int kGemmWide = 4;
 struct GemmPlan {
-    int tile;              // kGemmRing = LDS-ring kernel; register-staged 1 = 256x128, 2 = 128x256, 3 = 128x128
+    int tile;              // kGemmRing = LDS-ring kernel, kGemmWide = wide-wave kernel (128 x 128 per wavefront);
+                           // register-staged 1 = 256x128, 2 = 128x256, 3 = 128x128
     int bm;                // ring: activation rows per tile (128 or 256)
     int splits;            // ring: K splits (1 = none; else partial sums in the workspace + a reduction)
-    int stages_per_split;  // ring: 64-byte K stages per split
+    int stages_per_split;  // ring / wide: K stages per split (64 bytes each for the ring, 128 for the wide kernel)
     int dp_tiles;          // ring: > 0: the first dp_tiles tiles (whole CU rounds) run over all of K and only the
                            // remaining tiles, a band of output columns from n_lo, are split; 0: every tile alike
     int64_t n_lo;          // ring: first column of the split band (0 unless dp_tiles > 0)

@@ -236,13 +236,15 @@ def test_every_gemv_variant(mt, u, tb, monkeypatch, capfd):
 
 
 # every large-batch GEMM kernel: 0 = the LDS-ring kernel (256 or 128 activation rows per tile, with or without
-# split K), 1..3 = register-staged 256x128, 128x256, 128x128; shapes with ragged m and n, k with a partial last
-# stage, a single partial stage and fewer stages than the ring holds, n not a multiple of 8 (element-wise
-# epilogue) and whole 256-column tiles (the vectorized bf16 epilogue)
+# split K), 4 = the wide-wave kernel (128 x 128 outputs per wavefront, 128-byte stages; with or without split K),
+# 1..3 = register-staged 256x128, 128x256, 128x128; shapes with ragged m and n, k with a partial last stage, a
+# single partial stage and fewer stages than the ring holds, n not a multiple of 8 (element-wise epilogue) and
+# whole 256-column tiles (the vectorized bf16 epilogue)
 GEMM_SHAPES = [(65, 264, 16), (300, 512, 1040), (257, 520, 176), (130, 333, 4160), (512, 768, 2048),
                (100, 1000, 1552)]
-GEMM_CASES = [(0, None, None), (0, 1, 128), (0, 1, 256), (0, 3, 128), (0, 3, 256), (0, 64, 256), (1, None, None),
-              (2, None, None), (3, None, None)]
+GEMM_CASES = [(0, None, None), (0, 1, 128), (0, 1, 256), (0, 3, 128), (0, 3, 256), (0, 64, 256), (4, None, None),
+              (4, 1, 256), (4, 3, 256), (4, 64, 256), (1, None, None), (2, None, None), (3, None, None)]
+STAGE_BYTES = {0: 64, 4: 128}
 
 
 @pytest.mark.parametrize("tile,splits,bm", GEMM_CASES)
@@ -265,7 +267,7 @@ def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
             if bm is not None:
                 assert "bm=%d" % bm in err, err
             if splits is not None:
-                stages = -(-k // 64)
+                stages = -(-k // STAGE_BYTES[tile])
                 sps = -(-stages // min(splits, stages))
                 assert "splits=%d" % (-(-stages // sps)) in err, err
             # without accumulators: the bf16 output takes the kernel's other epilogue where it has one, and
@@ -284,26 +286,28 @@ def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
 # (m, n, k, rows per tile, splits, whole-K tiles): 2 x 11 tiles with a ragged 3-tile band and a partial last
 # stage; 2 x 9 tiles with a one-tile band of 253 columns (element-wise reduction) and a one-stage last split;
 # 1 x 9 tiles with 13 splits of 5 stages
-HYB_CASES = [(300, 2600, 1040, 256, 3, 16), (512, 2301, 1040, 256, 5, 16), (100, 2304, 4160, 128, 16, 8)]
+HYB_CASES = [(0, 300, 2600, 1040, 256, 3, 16), (0, 512, 2301, 1040, 256, 5, 16), (0, 100, 2304, 4160, 128, 16, 8),
+             (4, 300, 2600, 1040, 256, 3, 16), (4, 512, 2301, 1040, 256, 5, 16), (4, 200, 2304, 4160, 256, 16, 8)]
 
 
-@pytest.mark.parametrize("m,n,k,bm,splits,dp", HYB_CASES)
-def test_gemm_whole_tiles_then_split_band(m, n, k, bm, splits, dp, monkeypatch, capfd):
+@pytest.mark.parametrize("tile,m,n,k,bm,splits,dp", HYB_CASES)
+def test_gemm_whole_tiles_then_split_band(tile, m, n, k, bm, splits, dp, monkeypatch, capfd):
+    monkeypatch.setenv("QR_GEMM_TILE", str(tile))
     monkeypatch.setenv("QR_GEMM_ROUND", "8")
     monkeypatch.setenv("QR_GEMM_HYB", str(splits))
     monkeypatch.setenv("QR_GEMM_BM", str(bm))
     monkeypatch.setenv("QR_TRACE", "1")
-    stages = -(-k // 64)
+    stages = -(-k // STAGE_BYTES[tile])
     sps = -(-stages // splits)
     used = -(-stages // sps)
     wsp = qr.Workspace()
     for oq in (O.INT8, O.FP8):
         xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1700 + m + oq)
-        what = "gemm band split %s m=%d n=%d k=%d bm=%d splits=%d" % (oq, m, n, k, bm, splits)
+        what = "gemm band split tile=%d %s m=%d n=%d k=%d bm=%d splits=%d" % (tile, oq, m, n, k, bm, splits)
         log(what)
         _check(oq, xc, xs, wc, ws, what)
         err = capfd.readouterr().err
-        assert "kind=1" in err and "bm=%d splits=%d dp=%d " % (bm, used, dp) in err, err
+        assert "kind=1" in err and "gemm=%d bm=%d splits=%d dp=%d " % (tile, bm, used, dp) in err, err
         y_acc, _ = _run(oq, xc, xs, wc, ws)
         for rep in range(2):  # one workspace object, called again: the same bytes
             y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
