@@ -248,8 +248,9 @@ class Dense7B:
 
 def measure_rows(d, reps):
     """Per batch: one layer's four linears on bf16 activations (a2 + a3, as in the step); per batch and linear:
-    the linear's own kernels on codes (a3) and the activation quantization alone (a2). HIP events around graph
-    replays on the stream the kernels run on; LAYERS distinct layers per replay."""
+    the linear's own kernels on codes (a3, `us`), the activation quantization alone (`a2_us`) and the two through
+    the bf16 entry point as in the step (`a2_a3_us`). HIP events around graph replays on the stream the kernels
+    run on; LAYERS distinct layers per replay."""
     per_m, per_linear = {}, {}
     for m in BATCHES_7B:
         g = TimedGraph(lambda m=m: d.batch(m), LAYERS * len(LINEARS_7B))
@@ -267,11 +268,14 @@ def measure_rows(d, reps):
             g = TimedGraph(lambda m=m, name=name: [d.acts(name, m, l) for l in range(LAYERS)], LAYERS)
             ms_a = g.time_ms(reps) / LAYERS
             del g
+            g = TimedGraph(lambda m=m, name=name: [d.linear_bf16(name, m, l) for l in range(LAYERS)], LAYERS)
+            ms_b = g.time_ms(reps) / LAYERS
+            del g
             nb, no = bytes_linear(m, n, k), ops_linear(m, n, k)
             per_linear["m%d_%s" % (m, name)] = {
                 "us": round(ms * 1e3, 2), "TOPS": round(no / ms / 1e9, 1), "GB/s": round(nb / ms / 1e6, 1),
                 "bound": bound_of(m), "frac": round(frac_of(m, nb, no, ms), 4),
-                "a2_us": round(ms_a * 1e3, 2)}
+                "a2_us": round(ms_a * 1e3, 2), "a2_a3_us": round(ms_b * 1e3, 2)}
     return per_m, per_linear
 
 

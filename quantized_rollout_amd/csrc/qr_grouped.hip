@@ -233,12 +233,15 @@ __global__ void zero3_kernel(unsigned long long *out3) {
 }
 
 // One streaming pass over both code sets: each lane keeps kCountUnroll pairs of 16-byte loads in flight (grid-
-// stride over 16-byte words), compares bytes four at a time, and the counts are summed over the wave and added
-// with one 64-bit atomic per wave and count. The loads are non-temporal (each byte is read once, so it should
-// not displace cached data). Measured on MI355X over two 1.31 GB code sets: 4 pairs in flight on 2048
-// workgroups 550 us; 8 pairs, non-temporal, 768 workgroups (3 per CU) 415 us = 6.3 TB/s.
+// stride over 16-byte words), compares bytes four at a time, and the counts are summed over the workgroup and
+// added with one 64-bit atomic per workgroup and count. The loads are non-temporal (each byte is read once, so it
+// should not displace cached data). Measured on MI355X over two 1.31 GB code sets: 4 pairs in flight on 2048
+// workgroups 550 us; 8 pairs, non-temporal, 768 workgroups of 256 lanes 415 us = 6.3 TB/s. With one atomic per
+// wavefront the 233 M codes of a 7B layer took 129 us in one call and 303 us in four (one per linear): the
+// atomics, not the loads, set the time.
 constexpr int kCountUnroll = 8;
-constexpr int kCountBlocks = 768;
+constexpr int kCountThreads = 1024;
+constexpr int kCountBlocks = 256;
 
 template <bool NT>
 __device__ __forceinline__ uint4 count_load(const uint4 *p) {
@@ -251,7 +254,7 @@ __device__ __forceinline__ uint4 count_load(const uint4 *p) {
 }
 
 template <int UNR, bool NT>
-__global__ __launch_bounds__(256) void count_kernel(const uint8_t *__restrict__ a, const uint8_t *__restrict__ b,
+__global__ __launch_bounds__(kCountThreads) void count_kernel(const uint8_t *__restrict__ a, const uint8_t *__restrict__ b,
                                                     int64_t count, int fp8, const uint32_t *__restrict__ sa,
                                                     const uint32_t *__restrict__ sb, int64_t n_scales,
                                                     unsigned long long *__restrict__ out3) {
@@ -287,13 +290,23 @@ __global__ __launch_bounds__(256) void count_kernel(const uint8_t *__restrict__ 
     for (int64_t t = n16 * 16 + tid; t < count; t += stride) count_word(a[t], b[t], fp8 != 0, nb, nv);
     for (int64_t t = tid; t < n_scales; t += stride) ns += (sa[t] != sb[t]) ? 1ull : 0ull;
 
+    // the workgroup's sums (wavefronts, then LDS), one atomic per counter and workgroup: atomics on the same three
+    // words serialize (about 14 ns each on MI355X), so their number, not the streaming, bounded the count when
+    // every wavefront added its own
     nb = wave_sum_u64(nb);
     nv = wave_sum_u64(nv);
     ns = wave_sum_u64(ns);
+    __shared__ unsigned long long part[3][kCountThreads / 64];
     if ((threadIdx.x & 63) == 0) {
-        if (nb) atomicAdd(out3 + 0, nb);
-        if (nv) atomicAdd(out3 + 1, nv);
-        if (ns) atomicAdd(out3 + 2, ns);
+        part[0][threadIdx.x >> 6] = nb;
+        part[1][threadIdx.x >> 6] = nv;
+        part[2][threadIdx.x >> 6] = ns;
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        unsigned long long v = 0;
+        for (int w = 0; w < kCountThreads / 64; ++w) v += part[threadIdx.x][w];
+        if (v) atomicAdd(out3 + threadIdx.x, v);
     }
 }
 
@@ -349,16 +362,16 @@ hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t coun
     hipLaunchKernelGGL(zero3_kernel, dim3(1), dim3(64), 0, stream, o);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // enough 256-thread blocks for every CU to hold several (2048 = 256 CUs x 8), fewer for small inputs
+    // one 1024-lane workgroup per CU at most (16 wavefronts each), fewer for small inputs
     const int64_t work = count / 16 > n_scales ? count / 16 : n_scales;
     const int unr = env_int("QR_COUNT_UNROLL", kCountUnroll) == 4 ? 4 : kCountUnroll;
     const bool nt = env_int("QR_COUNT_NT", 1) > 0;
-    int64_t blocks = (work + 256 * unr - 1) / (256 * unr);
+    int64_t blocks = (work + (int64_t)kCountThreads * unr - 1) / ((int64_t)kCountThreads * unr);
     const int64_t max_blocks = env_int("QR_COUNT_BLOCKS", kCountBlocks);
     if (blocks > max_blocks) blocks = max_blocks;
     if (blocks < 1) blocks = 1;
 #define QR_COUNT(U_, NT_)                                                                                    \
-    hipLaunchKernelGGL((count_kernel<U_, NT_>), dim3((unsigned)blocks), dim3(256), 0, stream, a, b, count, \
+    hipLaunchKernelGGL((count_kernel<U_, NT_>), dim3((unsigned)blocks), dim3(kCountThreads), 0, stream, a, b, count, \
                        qtype == kFp8 ? 1 : 0, reinterpret_cast<const uint32_t *>(sa),                      \
                        reinterpret_cast<const uint32_t *>(sb), n_scales, o)
     if (unr == 8) {

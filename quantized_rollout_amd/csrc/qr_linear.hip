@@ -190,16 +190,12 @@ __global__ __launch_bounds__(WMAX * 64) void gemv_kernel(int64_t m, int64_t n, i
             for (int64_t c = threadIdx.x; c < k / 8; c += blockDim.x) {
                 float w[8];
                 x_elems(r, c, w);
-                uint32_t q[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    float v = fast ? div_by_scale(w[i], S, R) : w[i] / S;
-                    v = fminf(fmaxf(v, -qmax), qmax);
-                    q[i] = encode_code<QT>(v);
+                    const float v = fast ? div_by_scale(w[i], S, R) : w[i] / S;
+                    w[i] = fminf(fmaxf(v, -qmax), qmax);
                 }
-                *reinterpret_cast<uint2 *>(xlds + r * k + 8 * c) =
-                    make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                               q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+                *reinterpret_cast<uint2 *>(xlds + r * k + 8 * c) = make_uint2(encode_code4<QT>(w), encode_code4<QT>(w + 4));
             }
         }
         __syncthreads();
@@ -719,13 +715,15 @@ LinearPlan plan_linear_bf16(int qtype, int64_t m, int64_t n, int64_t k) {
 
 bool linear_bf16_fused(const LinearPlan &p, int qtype, int64_t m, int64_t k) {
     // Every workgroup quantizes the token rows itself, so the prologue is repeated per workgroup and only its
-    // own latency is hidden by other workgroups. Measured on MI355X (graph replay, weights past the caches):
-    // at m = 1 it beats the two launches on the 1.5B INT8 layer (39.3 -> 33.8 us) and on the 7B FP8 qkv, o and
-    // gate/up, but not on the 7B FP8 down (k = 18944: 22.7 -> 30.2 us, the software E4M3 encoder over a long
-    // row), nor at m = 2 or 4.
+    // own latency is hidden by other workgroups. Measured on MI355X (graph replay, weights past the caches,
+    // against the activation quantizer with wide per-row teams and the hardware E4M3 conversion, about 4 us):
+    // at m = 1 it pays on few workgroups (7B FP8 o 9.6 -> 8.9 us, qkv even) but not on the many of the 7B FP8
+    // gate/up (2368: 29.2 -> 31.4 us), nor on the 7B FP8 down (k = 18944, a long row in every workgroup), nor
+    // at m = 2 or 4.
     const int64_t max_m = env_int("QR_FUSE_MAX_M", 1);
     if (qtype == kFp8 && k > env_int("QR_FUSE_MAX_K_FP8", 8192)) return false;
-    return p.kind == 0 && p.m_tiles == 1 && p.splits == 1 && p.unroll == 4 &&
+    const int64_t blocks = (p.n_tiles + p.tiles - 1) / p.tiles;
+    return p.kind == 0 && p.m_tiles == 1 && p.splits == 1 && p.unroll == 4 && blocks < env_int("QR_FUSE_MAX_BLOCKS", 1024) &&
            m <= std::min<int64_t>(max_m, kFuseRows) && gemv_fused_lds_bytes(p, m, k) <= 65536;
 }
 

@@ -268,14 +268,13 @@ __global__ __launch_bounds__(256) void silu_mul_quant_kernel(const uint16_t *__r
 
     uint8_t *dst = codes + row * I;
     auto emit = [&](const float *hv, int64_t c) {
-        uint32_t q[4];
+        float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float v = fast ? div_by_scale(hv[j], Sc, r) : hv[j] / Sc;
-            v = fminf(fmaxf(v, -qmax), qmax);
-            q[j] = encode_code<QT>(v);
+            const float x = fast ? div_by_scale(hv[j], Sc, r) : hv[j] / Sc;
+            v[j] = fminf(fmaxf(x, -qmax), qmax);
         }
-        *reinterpret_cast<uint32_t *>(dst + 4 * c) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        *reinterpret_cast<uint32_t *>(dst + 4 * c) = encode_code4<QT>(v);
     };
 #pragma unroll
     for (int i = 0; i < kHold; ++i) {

@@ -179,24 +179,22 @@ __global__ __launch_bounds__(THREADS * RPB) void quantize_rows_kernel(const void
     auto emit = [&](const uint4 &chunk, int64_t c, const cword_t &old) {
         float w[E];
         expand_chunk<BF16, SMODE>(chunk, s, c * E, w);
-        uint32_t q[E];
 #pragma unroll
         for (int j = 0; j < E; ++j) {
-            float v = fast ? div_by_scale(w[j], S, r) : w[j] / S;
-            v = fminf(fmaxf(v, -qmax), qmax);
-            q[j] = encode_code<QT>(v);
+            const float v = fast ? div_by_scale(w[j], S, r) : w[j] / S;
+            w[j] = fminf(fmaxf(v, -qmax), qmax);
         }
         if constexpr (BF16) {
             uint2 o;
-            o.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-            o.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+            o.x = encode_code4<QT>(w);
+            o.y = encode_code4<QT>(w + 4);
             if constexpr (DIFF) {
                 count_word(old.x, o.x, QT == kFp8, nb, nv);
                 count_word(old.y, o.y, QT == kFp8, nb, nv);
             }
             st_codes<NT>(dst + c * 8, o);
         } else {
-            const uint32_t o = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            const uint32_t o = encode_code4<QT>(w);
             if constexpr (DIFF) count_word(old, o, QT == kFp8, nb, nv);
             st_codes<NT>(dst + c * 4, o);
         }
@@ -273,14 +271,27 @@ hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uin
 #define QR_QROWS(T, R, G)                                                                                      \
     hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, T, R, DIFF, NT>), G, dim3(T * R), 0, stream, in, rows, \
                        k, s, codes, scales, d.prev_codes, d.prev_scales, d.row_counts)
-    if (nch <= 64 * kC) {
+    // Lanes per row: the smallest power of two of at least half the row's chunks (64..1024), halved while the
+    // launch exceeds 2^20 threads; a row of one wavefront shares its workgroup with three others. Rows are
+    // latency-bound when few (a lane encodes its chunks one after the other), so few long rows (activations) get
+    // wide teams and many rows (weights) one wavefront each. Measured on MI355X (bf16 to FP8, graph replay):
+    // K = 3584 at 1..512 rows 7.1 -> 4.0-4.9 us with 512 lanes, at 2048 rows 11.2 -> 9.8 us with 256; K = 18944
+    // at 1..128 rows 6.2-7.6 -> 5.7-6.8 us with 1024, at 2048 rows 32.9 -> 31.2 us with 512.
+    int lanes = 64;
+    while (lanes < 1024 && 2 * lanes < nch) lanes *= 2;
+    while (lanes > 64 && rows * lanes > ((int64_t)1 << 20)) lanes /= 2;
+    const int minimum = nch <= 64 * kC ? 64 : nch <= 128 * kC ? 128 : nch <= 256 * kC ? 256 : nch <= 512 * kC ? 512 : 1024;
+    if (lanes < minimum) lanes = minimum;  // the register budget: at most kC chunks per lane held
+    const int forced = env_int("QR_QUANT_THREADS", 0);  // tuning sweeps
+    if (forced == 64 || forced == 128 || forced == 256 || forced == 512 || forced == 1024) lanes = forced;
+    if (lanes == 64) {
         constexpr int kRows = 4;
         QR_QROWS(64, kRows, dim3((unsigned)((rows + kRows - 1) / kRows)));
-    } else if (nch <= 128 * kC) {
+    } else if (lanes == 128) {
         QR_QROWS(128, 1, grid);
-    } else if (nch <= 256 * kC) {
+    } else if (lanes == 256) {
         QR_QROWS(256, 1, grid);
-    } else if (nch <= 512 * kC) {
+    } else if (lanes == 512) {
         QR_QROWS(512, 1, grid);
     } else {
         QR_QROWS(1024, 1, grid);
