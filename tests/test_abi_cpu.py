@@ -195,8 +195,10 @@ def test_linear_bf16_validation_and_workspace(monkeypatch):
     assert call(m=0) == B.QR_OK
     ws = B.qr_w8a8_linear_bf16_workspace_bytes if hasattr(B, "qr_w8a8_linear_bf16_workspace_bytes") else None
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
-        # m = 1: the activation quantization runs inside the linear, no workspace (FP8: for k <= 8192)
-        assert ws(q, 1, 17920, 1536) == 0 and ws(q, 1, 3584, 3584) == 0
+        # m = 1: the activation quantization runs inside the linear, no workspace (FP8: for k <= 8192), on plans
+        # of fewer than 1024 workgroups; the 1120 workgroups of n = 17920 quantize into the workspace first
+        assert ws(q, 1, 3584, 3584) == 0
+        assert ws(q, 1, 17920, 1536) == 1536 + 256
         assert ws(q, 1, 1536, 8960) == (0 if q == B.QR_INT8 else 8960 + 256)
         # larger batches: the activation codes (m k bytes) and scales (4 m), each rounded up to 256 bytes,
         # then the linear's own workspace
