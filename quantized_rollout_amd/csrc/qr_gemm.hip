@@ -528,10 +528,10 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
 // block scales, or two v_mfma_i32_32x32x32_i8), 256 accumulators per lane. A wavefront's fragments of one
 // 64-byte K step are 8 reads of 2 KiB for 16 MFMAs, half of what the ring kernel's 64 x 64 wavefronts read per
 // MFMA, so the LDS carries less per operation.
-// K advances in 128-byte stages through two LDS buffers. Every thread loads its 16-byte pieces of stage s + 1
-// into registers (raw buffer loads: rows past m or n and bytes past k read as zero) while the MFMAs of stage s
-// run, and writes them to the other buffer before the stage's barrier. A buffer holds the stage's 256
-// activation rows, then its 256 weight rows, 128 bytes each, with logical 16-byte piece c of row r stored at
+// K (a multiple of 128 bytes) advances in 128-byte stages through two LDS buffers. Every thread loads its
+// 16-byte pieces of stage s + 1 into registers (raw buffer loads: rows past m or n read as zero) while the MFMAs
+// of stage s run, and writes them to the other buffer before the stage's barrier. A buffer holds the stage's 256
+// activation rows and its 256 weight rows, 128 bytes each, with logical 16-byte piece c of row r stored at
 // physical piece c ^ ((r / 2) mod 8): a fragment read (32 consecutive rows at one logical piece, served 16 lanes
 // per cycle over 64 four-byte banks) and a row-major staging write then touch distinct banks. A fragment gives
 // lane l row (l & 31) and, for the 64-byte step u of the stage, logical pieces 4 u + 2 (l >> 5) and
@@ -543,7 +543,8 @@ constexpr int kWideK = 128;     // K bytes per stage
 constexpr int kWideN = 256;     // weight rows (output channels) per tile
 constexpr int kWideM = 256;     // activation rows per tile
 constexpr int kWideThreads = 256;
-constexpr int kWideBuf = (kWideM + kWideN) * kWideK;  // bytes per LDS buffer (64 KiB)
+constexpr int kWideBuf = (kWideM + kWideN) * kWideK;  // bytes per LDS stage buffer (64 KiB)
+constexpr int kWideHalf = kWideM * kWideK;              // one operand's rows of a stage (32 KiB)
 constexpr int kWideChunks = kWideM * kWideK / 16 / kWideThreads;  // 16-byte pieces per thread per operand (8)
 
 __device__ __forceinline__ int wide_swizzle(int r) { return (r >> 1) & 7; }
@@ -589,42 +590,49 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     const int64_t all_stages = (k + kWideK - 1) / kWideK;
     const int64_t st0 = to_partial ? (int64_t)split * stages_per_split : 0;
     const int64_t stages = to_partial ? std::min<int64_t>(stages_per_split, all_stages - st0) : all_stages;
-    const int64_t full = k / kWideK;  // stages with every piece inside k
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // staging: piece i of this thread is chunk t + 256 i of the stage, row (t / 8) + 32 i, logical piece t % 8;
-    // the row's swizzle (r / 2) mod 8 does not depend on i, so piece i sits 32 rows (4 KiB) after piece 0
+    // LDS: stage buffer b holds its activation rows at b * kWideHalf and its weight rows at kWideBuf + b * kWideHalf,
+    // so that every access below is a register plus an immediate offset, and moving to the other buffer flips one
+    // address bit (kWideHalf) of a few registers once per stage.
+    // Staging: piece i of this thread is chunk t + 256 i of the stage, row (t / 8) + 32 i, logical piece t % 8;
+    // the row's swizzle (r / 2) mod 8 does not depend on i, so piece i sits 32 rows (4 KiB) after piece 0.
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xq), (short)0,
                                                                          (int)(m * k), kBufferFlags);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wq), (short)0,
                                                                          (int)(n * k), kBufferFlags);
     const int srow = t >> 3, spiece = t & 7;
-    const int lds0 = srow * kWideK + 16 * (spiece ^ wide_swizzle(srow));  // + 4096 i; weights + kWideM rows
-    const uint32_t rowstep = (uint32_t)(32 * k);                           // 32 rows of the operand
-    const uint32_t offa0 = (uint32_t)((m0 + srow) * k + 16 * spiece);
-    const uint32_t offb0 = (uint32_t)((n0 + srow) * k + 16 * spiece);
+    const int lds0 = srow * kWideK + 16 * (spiece ^ wide_swizzle(srow));
     const int64_t rows_a = m - m0 - srow, rows_b = n - n0 - srow;  // piece i is in range while 32 i < rows
+    // byte offsets of the pieces at K = 0, or kOutOfRange (past every operand) for rows outside the operand
+    uint32_t va[kWideChunks], vb[kWideChunks];
+#pragma unroll
+    for (int i = 0; i < kWideChunks; ++i) {
+        va[i] = 32 * i < rows_a ? (uint32_t)((m0 + srow + 32 * i) * k + 16 * spiece) : kOutOfRange;
+        vb[i] = 32 * i < rows_b ? (uint32_t)((n0 + srow + 32 * i) * k + 16 * spiece) : kOutOfRange;
+    }
     v4i ra[kWideChunks], rb[kWideChunks];
-    auto load = [&](int64_t gst) {  // global stage gst into the staging registers
-        const uint32_t k0 = (uint32_t)(gst * kWideK);
-        const bool kin = gst < full || (int64_t)k0 + 16 * spiece < k;
-#pragma unroll
-        for (int i = 0; i < kWideChunks; ++i) {
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rsa, (kin && 32 * i < rows_a) ? offa0 + rowstep * i + k0 : kOutOfRange, 0, 0);
-            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rsb, (kin && 32 * i < rows_b) ? offb0 + rowstep * i + k0 : kOutOfRange, 0, 0);
-        }
+    // staging piece x of global stage gst (x < 8: activations, else weights). K is a whole number of stages here,
+    // so the stage's K offset goes in the scalar offset, with no per-lane arithmetic; a row outside the operand
+    // stays out of range with or without it.
+    auto load_one = [&](int64_t gst, auto X) {
+        constexpr int x = decltype(X)::value;
+        const int k0 = (int)(gst * kWideK);
+        if constexpr (x < 8)
+            ra[x] = __builtin_amdgcn_raw_buffer_load_b128(rsa, va[x], k0, 0);
+        else
+            rb[x - 8] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vb[x - 8], k0, 0);
     };
-    auto store = [&](uint8_t *buf) {  // the staging registers into an LDS buffer
-#pragma unroll
-        for (int i = 0; i < kWideChunks; ++i) {
-            *reinterpret_cast<v4i *>(buf + lds0 + 4096 * i) = ra[i];
-            *reinterpret_cast<v4i *>(buf + kWideM * kWideK + lds0 + 4096 * i) = rb[i];
-        }
+    // staging piece x into the buffer whose staging addresses are wa (activations) and wb (weights)
+    auto store_one = [&](int wa, int wb, auto X) {
+        constexpr int x = decltype(X)::value;
+        if constexpr (x < 8)
+            *reinterpret_cast<v4i *>(lds + wa + 4096 * x) = ra[x];
+        else
+            *reinterpret_cast<v4i *>(lds + wb + 4096 * (x - 8)) = rb[x - 8];
     };
 
     acc_t acc[4][4];
@@ -638,18 +646,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     const int fr = lane & 31, h = lane >> 5;
     const int q0 = QT == kInt8 ? h : 2 * h, q1 = QT == kInt8 ? 2 + h : 2 * h + 1;
     const int swz = wide_swizzle(fr);  // rows wm 128 + 32 i + fr and 128 wn + 32 j + fr share it
+    // the lane's fragment addresses in buffer 0 for step u and piece parity p (the first or second 16 bytes)
+    auto frag_a = [&](int u, int p) { return (wm * 128 + fr) * kWideK + 16 * ((4 * u + (p ? q1 : q0)) ^ swz); };
+    auto frag_b = [&](int u, int p) {
+        return kWideBuf + (wn * 128 + fr) * kWideK + 16 * ((4 * u + (p ? q1 : q0)) ^ swz);
+    };
     struct Frags {
         uint4 a[4][2], b[4][2];
     };
-    // read x of a step (x = 0..15): A fragment x / 4 piece x % 2 for x < 8, then B fragment (x - 8) / 2 piece x % 2
-    auto read_one = [&](const uint8_t *buf, int u, Frags &f, auto X) {
+    // read x (x = 0..15) at fragment addresses fa, fb: A fragment x / 2 piece x % 2 for x < 8, then B fragment
+    // (x - 8) / 2 piece x % 2
+    auto read_one = [&](const int (&fa)[2], const int (&fb)[2], Frags &f, auto X) {
         constexpr int x = decltype(X)::value;
-        const int pc = 16 * ((4 * u + ((x & 1) ? q1 : q0)) ^ swz);
         if constexpr (x < 8)
-            f.a[x / 2][x & 1] = *reinterpret_cast<const uint4 *>(buf + (wm * 128 + (x / 2) * 32 + fr) * kWideK + pc);
+            f.a[x / 2][x & 1] = *reinterpret_cast<const uint4 *>(lds + fa[x & 1] + (x / 2) * 4096);
         else
-            f.b[(x - 8) / 2][x & 1] =
-                *reinterpret_cast<const uint4 *>(buf + (kWideM + wn * 128 + ((x - 8) / 2) * 32 + fr) * kWideK + pc);
+            f.b[(x - 8) / 2][x & 1] = *reinterpret_cast<const uint4 *>(lds + fb[x & 1] + ((x - 8) / 2) * 4096);
     };
     // MFMA tile x of a step: fragments (x / 4, x % 4)
     auto mfma_one = [&](const Frags &f, auto X) {
@@ -663,25 +675,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
                                                                          0, 127, 0, 127);
         }
     };
-    // staging piece x (x = 0..15): activation piece x for x < 8, weight piece x - 8 otherwise
-    auto store_one = [&](uint8_t *buf, auto X) {
-        constexpr int x = decltype(X)::value;
-        if constexpr (x < 8)
-            *reinterpret_cast<v4i *>(buf + lds0 + 4096 * x) = ra[x];
-        else
-            *reinterpret_cast<v4i *>(buf + kWideM * kWideK + lds0 + 4096 * (x - 8)) = rb[x - 8];
-    };
-    auto load_one = [&](int64_t gst, auto X) {
-        constexpr int x = decltype(X)::value;
-        const uint32_t k0 = (uint32_t)(gst * kWideK);
-        const bool kin = gst < full || (int64_t)k0 + 16 * spiece < k;
-        if constexpr (x < 8)
-            ra[x] = __builtin_amdgcn_raw_buffer_load_b128(
-                rsa, (kin && 32 * x < rows_a) ? offa0 + rowstep * x + k0 : kOutOfRange, 0, 0);
-        else
-            rb[x - 8] = __builtin_amdgcn_raw_buffer_load_b128(
-                rsb, (kin && 32 * (x - 8) < rows_b) ? offb0 + rowstep * (x - 8) + k0 : kOutOfRange, 0, 0);
-    };
 
     // Pipeline (one wavefront per SIMD, so each wavefront hides its own latencies): stage s + 1 is in the staging
     // registers while stage s runs, and the fragments of one 64-byte step are read while the MFMAs of the other
@@ -694,54 +687,59 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     //  B: the second step's 16 MFMA tiles, each followed by one of stage s + 1's first-step fragment reads.
     // The memory instructions thus issue while the matrix core is busy. Scheduling barriers between the groups
     // keep the compiler from regrouping them; the waits it inserts then cover one group's dependences only.
-    Frags f0, f1;
-    auto phase_a = [&](const uint8_t *cur, uint8_t *nxt, int64_t s, auto store_c, auto load_c) {
-        constexpr bool kStore = decltype(store_c)::value, kLoad = decltype(load_c)::value;
-        unroll<16>([&](auto X) {
-            mfma_one(f0, X);
-            read_one(cur, 1, f1, X);
-            if constexpr (kStore) store_one(nxt, X);
-            if constexpr (kLoad) load_one(st0 + s + 2, X);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-    auto phase_b = [&](const uint8_t *nxt, auto next_c) {
-        constexpr bool kNext = decltype(next_c)::value;
-        unroll<16>([&](auto X) {
-            mfma_one(f1, X);
-            if constexpr (kNext) read_one(nxt, 0, f0, X);
-            __builtin_amdgcn_sched_barrier(0);
-        });
+    // Addresses: c1a / c1b the current buffer's second-step fragments, n0a / n0b the next buffer's first-step
+    // fragments, wa / wb the next buffer's staging pieces; all flip to the other buffer after each stage.
+    int c1a[2] = {frag_a(1, 0), frag_a(1, 1)}, c1b[2] = {frag_b(1, 0), frag_b(1, 1)};
+    int n0a[2] = {frag_a(0, 0) ^ kWideHalf, frag_a(0, 1) ^ kWideHalf};
+    int n0b[2] = {frag_b(0, 0) ^ kWideHalf, frag_b(0, 1) ^ kWideHalf};
+    int wa = lds0 ^ kWideHalf, wb = (kWideBuf + lds0) ^ kWideHalf;
+    auto flip = [&]() {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            c1a[p] ^= kWideHalf;
+            c1b[p] ^= kWideHalf;
+            n0a[p] ^= kWideHalf;
+            n0b[p] ^= kWideHalf;
+        }
+        wa ^= kWideHalf;
+        wb ^= kWideHalf;
     };
     typedef std::integral_constant<bool, true> yes;
     typedef std::integral_constant<bool, false> no;
-    load(st0);
-    store(lds);
-    if (stages > 1) load(st0 + 1);
+    Frags f0, f1;
+    auto run_stage = [&](int64_t s, auto store_c, auto load_c, auto next_c) {
+        constexpr bool kStore = decltype(store_c)::value, kLoad = decltype(load_c)::value,
+                       kNext = decltype(next_c)::value;
+        unroll<16>([&](auto X) {
+            mfma_one(f0, X);
+            read_one(c1a, c1b, f1, X);
+            if constexpr (kStore) store_one(wa, wb, X);
+            if constexpr (kLoad) load_one(st0 + s + 2, X);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        __syncthreads();
+        unroll<16>([&](auto X) {
+            mfma_one(f1, X);
+            if constexpr (kNext) read_one(n0a, n0b, f0, X);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        flip();
+    };
+    unroll<16>([&](auto X) { load_one(st0, X); });
+    unroll<16>([&](auto X) { store_one(lds0, kWideBuf + lds0, X); });
+    if (stages > 1) unroll<16>([&](auto X) { load_one(st0 + 1, X); });
     __syncthreads();
-    unroll<16>([&](auto X) { read_one(lds, 0, f0, X); });
-    int64_t s = 0;
-    for (; s + 2 < stages; ++s) {  // steady state: stage s + 2 exists
-        const uint8_t *cur = lds + (int)(s & 1) * kWideBuf;
-        uint8_t *nxt = lds + (int)((s + 1) & 1) * kWideBuf;
-        phase_a(cur, nxt, s, yes{}, yes{});
-        __syncthreads();
-        phase_b(nxt, yes{});
+    {
+        const int fa[2] = {frag_a(0, 0), frag_a(0, 1)}, fb[2] = {frag_b(0, 0), frag_b(0, 1)};
+        unroll<16>([&](auto X) { read_one(fa, fb, f0, X); });
     }
-    if (s + 1 < stages) {  // the last but one stage: nothing more to load
-        const uint8_t *cur = lds + (int)(s & 1) * kWideBuf;
-        uint8_t *nxt = lds + (int)((s + 1) & 1) * kWideBuf;
-        phase_a(cur, nxt, s, yes{}, no{});
-        __syncthreads();
-        phase_b(nxt, yes{});
+    int64_t s = 0;
+    for (; s + 2 < stages; ++s) run_stage(s, yes{}, yes{}, yes{});  // steady state: stage s + 2 exists
+    if (s + 1 < stages) {                                           // the last but one stage: nothing to load
+        run_stage(s, yes{}, no{}, yes{});
         ++s;
     }
-    {  // the last stage
-        const uint8_t *cur = lds + (int)(s & 1) * kWideBuf;
-        phase_a(cur, nullptr, s, no{}, no{});
-        __syncthreads();
-        phase_b(nullptr, no{});
-    }
+    run_stage(s, no{}, no{}, no{});  // the last stage
     __syncthreads();  // every fragment read is retired before the epilogue reuses the LDS
 
     const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
@@ -912,6 +910,7 @@ hipError_t launch_wide(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wide_kernel<QT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kWideBuf);
     if (attr != hipSuccess) return attr;
+    if (k % kWideK != 0) return hipErrorInvalidValue;  // the kernel's loads take whole 128-byte stages
     const int tiles_m = (int)((m + kWideM - 1) / kWideM), tiles_n = (int)((n + kWideN - 1) / kWideN);
     int grid;
     if (g.dp_tiles == 0) {
@@ -983,7 +982,7 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
     // the ring kernel elsewhere (its 128-row tiles at small batches, and few-tile shapes split over K: qkv and o at
     // m = 512 29 / 27 us against 36 / 33, o at m = 2048 39 against 44 us)
     const bool wide_pays = m > 128 && (count(kWideM, kWideN) >= 128 || k >= 8192);
-    g.tile = forced == kGemmWide || (forced < 0 && wide_pays) ? kGemmWide : kGemmRing;
+    g.tile = (forced == kGemmWide || (forced < 0 && wide_pays)) && k % kWideK == 0 ? kGemmWide : kGemmRing;
     // Cost model, fitted to the 7B-shaped FP8 linears at m = 128, 512, 2048 on MI355X: a workgroup takes about
     // 0.65 us per 64 bytes of K with 128 activation rows per tile and 0.83 us with 256; workgroups beyond the
     // 256 CUs run in further rounds; a split adds its partial sums (written and read back, about 5 TB/s) and

@@ -239,9 +239,12 @@ def test_every_gemv_variant(mt, u, tb, monkeypatch, capfd):
 # split K), 4 = the wide-wave kernel (128 x 128 outputs per wavefront, 128-byte stages; with or without split K),
 # 1..3 = register-staged 256x128, 128x256, 128x128; shapes with ragged m and n, k with a partial last stage, a
 # single partial stage and fewer stages than the ring holds, n not a multiple of 8 (element-wise epilogue) and
-# whole 256-column tiles (the vectorized bf16 epilogue)
+# whole 256-column tiles (the vectorized bf16 epilogue). The wide kernel takes K in whole 128-byte stages: its
+# shapes have one, two and many stages, and a K it does not take runs on the ring kernel.
 GEMM_SHAPES = [(65, 264, 16), (300, 512, 1040), (257, 520, 176), (130, 333, 4160), (512, 768, 2048),
                (100, 1000, 1552)]
+WIDE_SHAPES = [(65, 264, 128), (300, 512, 1024), (257, 520, 256), (130, 333, 4096), (512, 768, 2048),
+               (100, 1000, 1536), (300, 520, 1040)]
 GEMM_CASES = [(0, None, None), (0, 1, 128), (0, 1, 256), (0, 3, 128), (0, 3, 256), (0, 64, 256), (4, None, None),
               (4, 1, 256), (4, 3, 256), (4, 64, 256), (1, None, None), (2, None, None), (3, None, None)]
 STAGE_BYTES = {0: 64, 4: 128}
@@ -256,18 +259,19 @@ def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
         monkeypatch.setenv("QR_GEMM_BM", str(bm))
     monkeypatch.setenv("QR_TRACE", "1")
     wsp = qr.Workspace()
-    for i, (m, n, k) in enumerate(GEMM_SHAPES):
+    for i, (m, n, k) in enumerate(WIDE_SHAPES if tile == 4 else GEMM_SHAPES):
+        ran = tile if tile != 4 or k % 128 == 0 else 0
         for oq in (O.INT8, O.FP8):
             xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1300 + 10 * i + oq)
             what = "gemm tile=%s splits=%s bm=%s %s m=%d n=%d k=%d" % (tile, splits, bm, oq, m, n, k)
             log(what)
             _check(oq, xc, xs, wc, ws, what)
             err = capfd.readouterr().err
-            assert "kind=1" in err and "gemm=%d" % tile in err, err
+            assert "kind=1" in err and "gemm=%d" % ran in err, err
             if bm is not None:
                 assert "bm=%d" % bm in err, err
             if splits is not None:
-                stages = -(-k // STAGE_BYTES[tile])
+                stages = -(-k // STAGE_BYTES[ran])
                 sps = -(-stages // min(splits, stages))
                 assert "splits=%d" % (-(-stages // sps)) in err, err
             # without accumulators: the bf16 output takes the kernel's other epilogue where it has one, and
@@ -284,10 +288,10 @@ def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
 # Whole rounds of tiles over all of K first, then the remaining band of output columns split over K: the planner's
 # choice for tile counts just past a whole number of CU rounds, forced here with a round of 8 tiles.
 # (m, n, k, rows per tile, splits, whole-K tiles): 2 x 11 tiles with a ragged 3-tile band and a partial last
-# stage; 2 x 9 tiles with a one-tile band of 253 columns (element-wise reduction) and a one-stage last split;
-# 1 x 9 tiles with 13 splits of 5 stages
+# stage (wide kernel: a shorter last split); 2 x 9 tiles with a one-tile band of 253 columns (element-wise
+# reduction) and a one-stage last split; 1 x 9 tiles with 13 (wide kernel: 16) splits
 HYB_CASES = [(0, 300, 2600, 1040, 256, 3, 16), (0, 512, 2301, 1040, 256, 5, 16), (0, 100, 2304, 4160, 128, 16, 8),
-             (4, 300, 2600, 1040, 256, 3, 16), (4, 512, 2301, 1040, 256, 5, 16), (4, 200, 2304, 4160, 256, 16, 8)]
+             (4, 300, 2600, 1024, 256, 3, 16), (4, 512, 2301, 1024, 256, 5, 16), (4, 200, 2304, 4096, 256, 16, 8)]
 
 
 @pytest.mark.parametrize("tile,m,n,k,bm,splits,dp", HYB_CASES)
