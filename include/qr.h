@@ -30,6 +30,12 @@
  *    QR_FORCE_VARIANT, and the plan trace QR_TRACE) are read only if QR_TUNE is set (non-empty, not "0") when
  *    the library is loaded; without it no variable is consulted, so the output bits of a call cannot change
  *    with the environment.
+ *  - Test and debug hooks (read when the library is first used; neither changes an output bit):
+ *    QR_FAULT_INJECT=launch makes every call that passes validation return QR_ERR_HIP ("launch failure
+ *    injected") instead of launching, as a refused launch would; QR_DEBUG (non-empty, not "0"), or
+ *    qr_set_debug(1), adds device checks of device-side inputs that the host cannot see (the grouped linear's
+ *    token lists), after which the call waits on its stream for their verdict: a debug-mode call
+ *    synchronizes and must not be captured into a graph.
  */
 #ifndef QR_H
 #define QR_H
@@ -41,7 +47,16 @@
 extern "C" {
 #endif
 
-typedef enum qr_status {
+/* The enums are int-sized in C and C++ alike; in C++ they are declared with int as their underlying type, so
+ * that an out-of-range value a caller passes is a value the library can examine and refuse, not undefined
+ * behaviour. */
+#ifdef __cplusplus
+#define QR_ENUM_BASE : int
+#else
+#define QR_ENUM_BASE
+#endif
+
+typedef enum qr_status QR_ENUM_BASE {
     QR_OK = 0,
     QR_ERR_ARG = 1,         /* null pointer, negative or inconsistent size, bad enum          */
     QR_ERR_UNSUPPORTED = 2, /* k not a multiple of 16, or a size beyond the supported range     */
@@ -50,11 +65,11 @@ typedef enum qr_status {
     QR_ERR_HIP = 5          /* the HIP runtime refused a launch                                 */
 } qr_status;
 
-typedef enum qr_dtype { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
+typedef enum qr_dtype QR_ENUM_BASE { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
 
 /* INT8: symmetric, codes in [-127, 127], scale = max|row| / 127.
  * FP8:  E4M3FN (bias 7, largest finite 448, no infinity), scale = max|row| / 448. */
-typedef enum qr_qtype { QR_INT8 = 0, QR_FP8_E4M3 = 1 } qr_qtype;
+typedef enum qr_qtype QR_ENUM_BASE { QR_INT8 = 0, QR_FP8_E4M3 = 1 } qr_qtype;
 
 /*
  * Weight quantization, one scale per output channel ([QuRL] 5: channel-wise weight scales; [QaRL] 2.2: the
@@ -143,7 +158,9 @@ size_t qr_w8a8_linear_bf16_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int
  * row_ids: device int32 [total_rows] with values in [0, x_rows), or NULL for the identity.
  * w_codes: [num_experts, n, k]; w_scales: [num_experts, n]; y: [total_rows, n].
  * The device trusts the token lists but never reads outside them: a row whose row_ids entry is outside
- * [0, x_rows) gets zeros, and offsets are clamped to [0, total_rows].
+ * [0, x_rows) gets zeros, and offsets are clamped to [0, total_rows]. In debug mode (QR_DEBUG, qr_set_debug)
+ * the lists are checked on the device first, and a violation returns QR_ERR_ARG, naming the failed
+ * condition, before the linear is launched.
  * workspace: as for qr_w8a8_linear, qr_workspace_bytes(q, total_rows, n, k, num_experts) bytes.
  */
 qr_status qr_w8a8_grouped_linear(qr_qtype q, int64_t num_experts, int64_t n, int64_t k,
@@ -253,6 +270,10 @@ qr_status qr_moe_combine(const void *y_down, int64_t rows, int64_t hidden, const
 
 /* Device bytes of workspace a linear (num_experts == 1, m rows) or grouped call (m = total_rows) needs. */
 size_t qr_workspace_bytes(qr_qtype q, int64_t m, int64_t n, int64_t k, int64_t num_experts);
+
+/* Debug mode on (1) or off (0) for every later call in the process, overriding QR_DEBUG (see the common
+ * contract): device checks of device-side inputs, with a wait for their verdict. Not for captured streams. */
+void qr_set_debug(int on);
 
 /* Text of the last error on the calling thread ("" when none). */
 const char *qr_last_error(void);

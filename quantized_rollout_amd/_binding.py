@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
            "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
            "qr_w4a16_linear", "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_w8a8_linear_bf16_workspace_bytes",
-           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine", "qr_w8a8_linear_noalloc")
+           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine", "qr_w8a8_linear_noalloc", "qr_set_debug")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # QR_NOALLOC_SCRATCH_BYTES
 W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
@@ -80,6 +80,8 @@ def lib():
                 L.qr_last_error.restype = ctypes.c_char_p
                 L.qr_version.argtypes = []
                 L.qr_version.restype = ctypes.c_char_p
+                L.qr_set_debug.argtypes = [i32]
+                L.qr_set_debug.restype = None
                 _lib = L
     return _lib
 
@@ -110,6 +112,11 @@ def _dtype_code(t):
 def _need(cond, msg):
     if not cond:
         raise ValueError(msg)
+
+
+def qr_set_debug(on):
+    """Debug mode (device checks of device-side inputs, each call waiting for their verdict) on or off."""
+    lib().qr_set_debug(1 if on else 0)
 
 
 def qr_version():

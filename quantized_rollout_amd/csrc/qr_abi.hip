@@ -39,6 +39,35 @@ qr_status hip_status(hipError_t e, const char *what) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Test hook: with QR_FAULT_INJECT=launch in the environment when the library is first used, every call that
+// passes validation returns QR_ERR_HIP instead of launching, as a refused launch would (no GPU is touched).
+bool inject_launch() {
+    static const bool on = [] {
+        const char *v = getenv("QR_FAULT_INJECT");
+        return v != nullptr && strcmp(v, "launch") == 0;
+    }();
+    return on;
+}
+
+qr_status injected(const char *what) {
+    return fail(QR_ERR_HIP, "%s: launch failure injected (QR_FAULT_INJECT=launch)", what);
+}
+
+// Debug checks of device-side inputs (QR_DEBUG set, non-empty and not "0", when the library is first used, or
+// qr_set_debug): they run on the call's stream and the call waits for their verdict before launching.
+std::atomic<int> g_debug{-1};  // -1 until the environment is read
+
+bool debug_on() {
+    int d = g_debug.load(std::memory_order_relaxed);
+    if (d < 0) {
+        const char *v = getenv("QR_DEBUG");
+        const int from_env = (v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0) ? 1 : 0;
+        g_debug.compare_exchange_strong(d, from_env);
+        d = g_debug.load(std::memory_order_relaxed);
+    }
+    return d > 0;
+}
+
 constexpr int64_t kMaxK = 131072;           // INT8 accumulators: k * 127^2 < 2^31
 constexpr int64_t kMaxRows = 2147483647;    // grid dimension limit
 
@@ -76,6 +105,7 @@ qr_status quantize_common(const void *in, qr_dtype in_type, int64_t rows, int64_
     if (!aligned(in, 16) || !aligned(codes, 16)) return fail(QR_ERR_ALIGN, "input and codes must be 16-byte aligned");
     if (!aligned(scales, 4) || (s != nullptr && !aligned(s, 4)))
         return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+    if (inject_launch()) return injected("quantize launch");
     const hipError_t e =
         qr::launch_quantize_rows(in, in_type == QR_BF16, rows, k, s, s == nullptr ? qr::kSNone : s_mode, (int)q,
                                  static_cast<uint8_t *>(codes), scales, static_cast<hipStream_t>(stream),
@@ -115,6 +145,7 @@ qr_status run_linear(const qr::LinearPlan &p, qr_qtype q, int64_t m, int64_t n, 
                 (int)q, (long long)m, (long long)n, (long long)k, p.kind, p.m_tiles, p.waves, p.unroll, p.tiles,
                 p.prefetch ? 1 : 0, p.kind == 0 ? p.ksub : 1, p.gemm.tile, p.gemm.bm, p.kind == 0 ? p.splits : p.gemm.splits,
                 p.kind == 0 ? 0 : p.gemm.dp_tiles, p.ws_bytes);
+    if (inject_launch()) return injected("linear launch");
     const hipError_t e = qr::launch_linear(p, (int)q, m, n, k, static_cast<const uint8_t *>(x_codes), x_scales,
                                            static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
                                            acc_out, workspace, static_cast<hipStream_t>(stream));
@@ -203,6 +234,7 @@ qr_status qr_w8a8_linear_noalloc(qr_qtype q, int64_t m, int64_t n, int64_t k, co
                         "this linear splits K over %zu bytes of partial sums, more than the %zu-byte device scratch "
                         "of qr_w8a8_linear_noalloc; call qr_w8a8_linear with a workspace",
                         p.ws_bytes, (size_t)QR_NOALLOC_SCRATCH_BYTES);
+        if (inject_launch()) return injected("linear launch");
         if ((st = scratch_address(&ws)) != QR_OK) return st;
     }
     return run_linear(p, q, m, n, k, x_codes, x_scales, w_codes, w_scales, y, y_type, acc_out, ws, stream);
@@ -243,6 +275,7 @@ qr_status qr_w8a8_linear_bf16(qr_qtype q, int64_t m, int64_t n, int64_t k, const
                 "ksub=%d ws=%zu\n",
                 (int)q, (long long)m, (long long)n, (long long)k, qr::linear_bf16_fused(p, (int)q, m, k) ? 1 : 0, p.kind,
                 p.m_tiles, p.waves, p.unroll, p.tiles, p.kind == 0 ? p.ksub : 1, need);
+    if (inject_launch()) return injected("linear launch");
     const hipError_t e = qr::launch_linear_bf16(p, (int)q, m, n, k, static_cast<const uint16_t *>(x), s,
                                                 static_cast<const uint8_t *>(w_codes), w_scales, y,
                                                 y_type == QR_BF16, acc_out, workspace,
@@ -278,6 +311,19 @@ qr_status qr_w8a8_grouped_linear(qr_qtype q, int64_t num_experts, int64_t n, int
         (row_ids != nullptr && !aligned(row_ids, 4)))
         return fail(QR_ERR_ALIGN, "scales and index arrays must be 4-byte aligned");
     if (!aligned(y, 16)) return fail(QR_ERR_ALIGN, "y must be 16-byte aligned");
+    if (inject_launch()) return injected("grouped launch");
+    if (debug_on()) {
+        int bits = 0;
+        const hipError_t ce = qr::check_token_lists(expert_offsets, num_experts, row_ids, total_rows, x_rows, &bits,
+                                                    static_cast<hipStream_t>(stream));
+        if (ce != hipSuccess) return hip_status(ce, "token-list check");
+        if (bits != 0)
+            return fail(QR_ERR_ARG, "debug check of the token lists failed:%s%s%s%s",
+                        (bits & 1) ? " expert_offsets[0] != 0;" : "",
+                        (bits & 2) ? " expert_offsets[num_experts] != total_rows;" : "",
+                        (bits & 4) ? " expert_offsets decreases;" : "",
+                        (bits & 8) ? " a row id outside [0, x_rows);" : "");
+    }
     const hipError_t e = qr::launch_grouped((int)q, num_experts, n, k, expert_offsets, row_ids, total_rows, x_rows,
                                             static_cast<const uint8_t *>(x_codes), x_scales,
                                             static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
@@ -298,6 +344,7 @@ qr_status qr_count_code_changes(const void *a, const void *b, int64_t count, qr_
         return fail(QR_ERR_ALIGN, "codes must be 16-byte aligned");
     if ((sa != nullptr && !aligned(sa, 4)) || (sb != nullptr && !aligned(sb, 4)))
         return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    if (inject_launch()) return injected("count launch");
     const hipError_t e = qr::launch_count_changes(static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(b),
                                                   count, (int)q, sa, sb, n_scales, out3,
                                                   static_cast<hipStream_t>(stream));
@@ -333,6 +380,7 @@ qr_status qr_requantize_weights(const void *w, qr_dtype w_type, int64_t n, int64
         if (overlap(prev_codes, w_codes, n * k) || overlap(prev_scales, w_scales, n * 4))
             return fail(QR_ERR_ARG, "previous and new codes (or scales) overlap without being the same buffer");
     }
+    if (inject_launch()) return injected("requantize launch");
     const hipError_t e = qr::launch_requantize(w, w_type == QR_BF16, n, k, s, (int)q,
                                                static_cast<const uint8_t *>(prev_codes), prev_scales,
                                                static_cast<uint8_t *>(w_codes), w_scales, row_counts, out3,
@@ -355,6 +403,7 @@ qr_status qr_quantize_weights_w4(const void *w, qr_dtype w_type, int64_t n, int6
     if (!aligned(w, 16) || !aligned(w_codes, 16) || (s != nullptr && !aligned(s, 16)))
         return fail(QR_ERR_ALIGN, "input, codes and s must be 16-byte aligned");
     if (!aligned(w_scales, 4)) return fail(QR_ERR_ALIGN, "scales must be 4-byte aligned");
+    if (inject_launch()) return injected("w4 quantize launch");
     const hipError_t e = qr::launch_quantize_w4(w, w_type == QR_BF16, n, k, s, static_cast<uint8_t *>(w_codes),
                                                 w_scales, static_cast<hipStream_t>(stream));
     return hip_status(e, "w4 quantize launch");
@@ -382,6 +431,7 @@ qr_status qr_w4a16_linear(int64_t m, int64_t n, int64_t k, const void *x, const 
         fprintf(stderr, "[qr] w4a16 m=%lld n=%lld k=%lld ring=%d tiles=%d waves=%d wk=%d depth=%d xlds=%d\n",
                 (long long)m, (long long)n, (long long)k, p.ring ? 1 : 0, p.tiles, p.waves, p.wk, p.depth,
                 p.x_lds ? 1 : 0);
+    if (inject_launch()) return injected("w4a16 launch");
     const hipError_t e = qr::launch_w4a16(p, m, n, k, static_cast<const uint16_t *>(x),
                                           static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,
                                           static_cast<hipStream_t>(stream));
@@ -409,6 +459,7 @@ qr_status qr_moe_route(const float *logits, int64_t num_tokens, int64_t num_expe
             !aligned(row_weights, 4) || !aligned(pair_rows, 4))
             return fail(QR_ERR_ALIGN, "routing arrays must be 4-byte aligned");
     }
+    if (inject_launch()) return injected("route launch");
     const hipError_t e = qr::launch_moe_route(logits, num_tokens, (int)num_experts, (int)top_k, topk_expert,
                                               topk_weight, expert_offsets, row_ids, row_weights, pair_rows,
                                               static_cast<hipStream_t>(stream));
@@ -428,6 +479,7 @@ qr_status qr_silu_mul_quantize(const void *y_gu, int64_t rows, int64_t inter, co
         return fail(QR_ERR_ALIGN, "y_gu, h_codes and h must be 16-byte aligned");
     if (!aligned(h_scales, 4) || (s != nullptr && !aligned(s, 4)))
         return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+    if (inject_launch()) return injected("silu launch");
     const hipError_t e = qr::launch_silu_mul_quant(static_cast<const uint16_t *>(y_gu), rows, inter, s, (int)q,
                                                    static_cast<uint8_t *>(h_codes), h_scales,
                                                    static_cast<uint16_t *>(h), static_cast<hipStream_t>(stream));
@@ -449,11 +501,14 @@ qr_status qr_moe_combine(const void *y_down, int64_t rows, int64_t hidden, const
         return fail(QR_ERR_ALIGN, "y_down and out must be 16-byte aligned");
     if (!aligned(topk_weight, 4) || !aligned(pair_rows, 4))
         return fail(QR_ERR_ALIGN, "topk_weight and pair_rows must be 4-byte aligned");
+    if (inject_launch()) return injected("combine launch");
     const hipError_t e = qr::launch_moe_combine(static_cast<const uint16_t *>(y_down), rows, topk_weight, pair_rows,
                                                 num_tokens, (int)top_k, hidden, static_cast<uint16_t *>(out),
                                                 static_cast<hipStream_t>(stream));
     return hip_status(e, "combine launch");
 }
+
+void qr_set_debug(int on) { g_debug.store(on ? 1 : 0, std::memory_order_relaxed); }
 
 const char *qr_last_error(void) { return g_err; }
 

@@ -383,4 +383,46 @@ hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t coun
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------------------------------------
+// Token-list check (debug mode): one workgroup reads the offsets and row ids once and writes the OR of the
+// failed conditions (see check_token_lists) to a device word that the host then copies back.
+// ---------------------------------------------------------------------------------------------------------
+__device__ int g_token_list_bits;
+
+__global__ __launch_bounds__(1024) void token_list_check_kernel(const int32_t *__restrict__ offsets, int64_t num_experts,
+                                                                const int32_t *__restrict__ row_ids, int64_t total_rows,
+                                                                int64_t x_rows) {
+    __shared__ int bits_all;
+    const int t = threadIdx.x;
+    if (t == 0) bits_all = 0;
+    __syncthreads();
+    int bits = 0;
+    if (t == 0) {
+        if (offsets[0] != 0) bits |= 1;
+        if ((int64_t)offsets[num_experts] != total_rows) bits |= 2;
+    }
+    for (int64_t e = t; e < num_experts; e += blockDim.x)
+        if (offsets[e + 1] < offsets[e]) bits |= 4;
+    if (row_ids != nullptr)
+        for (int64_t j = t; j < total_rows; j += blockDim.x) {
+            const int32_t r = row_ids[j];
+            if (r < 0 || (int64_t)r >= x_rows) bits |= 8;
+        }
+    if (bits != 0) atomicOr(&bits_all, bits);
+    __syncthreads();
+    if (t == 0) g_token_list_bits = bits_all;
+}
+
+hipError_t check_token_lists(const int32_t *offsets, int64_t num_experts, const int32_t *row_ids, int64_t total_rows,
+                             int64_t x_rows, int *bits, hipStream_t stream) {
+    hipLaunchKernelGGL(token_list_check_kernel, dim3(1), dim3(1024), 0, stream, offsets, num_experts, row_ids,
+                       total_rows, x_rows);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = hipMemcpyFromSymbolAsync(bits, HIP_SYMBOL(g_token_list_bits), sizeof(int), 0, hipMemcpyDeviceToHost, stream);
+    if (err != hipSuccess) return err;
+    return hipStreamSynchronize(stream);
+}
+
 }  // namespace qr

@@ -85,6 +85,12 @@ hipError_t launch_grouped(int qtype, int64_t num_experts, int64_t n, int64_t k, 
 hipError_t launch_count_changes(const uint8_t *a, const uint8_t *b, int64_t count, int qtype, const float *sa,
                                 const float *sb, int64_t n_scales, int64_t *out3, hipStream_t stream);
 
+// Debug check of a grouped call's token lists (one workgroup on the stream, then a wait for its verdict):
+// *bits gets 1 if offsets[0] != 0, 2 if offsets[num_experts] != total_rows, 4 if the offsets decrease
+// somewhere, 8 if a row id lies outside [0, x_rows); 0 when the lists are valid.
+hipError_t check_token_lists(const int32_t *offsets, int64_t num_experts, const int32_t *row_ids, int64_t total_rows,
+                             int64_t x_rows, int *bits, hipStream_t stream);
+
 // W4A16 (qr_w4.hip): group-wise INT4 weights, bfloat16 activations.
 constexpr int64_t kW4Group = 128;  // input channels per INT4 scale group
 struct W4Plan {

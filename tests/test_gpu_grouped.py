@@ -67,6 +67,47 @@ def test_grouped_identity_rows_and_many_rows_per_expert(oq, gq):
     assert_grouped_within_bound(host(y), oq, off, None, xc, xs, wc, ws, "grouped identity")
 
 
+def test_grouped_debug_check_of_token_lists():
+    """Debug mode checks the token lists on the device before the grouped linear runs: valid lists give the
+    same output bits as without the check; each broken condition (first offset, last offset, a decreasing
+    pair, a row id outside [0, x_rows)) is refused with QR_ERR_ARG and its name, and nothing is launched after
+    it (the output buffer keeps its sentinel)."""
+    rng = np.random.default_rng(302)
+    E, n, k, x_rows = 4, 48, 256, 12
+    xc, xs = O.quantize_rows(rng.standard_normal((x_rows, k)).astype(np.float32), O.INT8, s_mode=O.S_MUL_RECIP)
+    wc, ws = _expert_weights(E, n, k, O.INT8, rng)
+    off = np.array([0, 3, 3, 7, 10], np.int32)
+    rows = np.array([0, 5, 11, 2, 2, 9, 4, 1, 7, 3], np.int32)
+    total = int(off[-1])
+    y0 = qr.qr_w8a8_grouped_linear(qr.QR_INT8, dev(off), dev(rows), total, dev(xc), dev(xs), dev(wc), dev(ws))
+    torch.cuda.synchronize()
+    bad_cases = [
+        ("first", np.array([1, 3, 3, 7, 10], np.int32), rows, "expert_offsets[0] != 0"),
+        ("last", np.array([0, 3, 3, 7, 9], np.int32), rows, "expert_offsets[num_experts] != total_rows"),
+        ("decreasing", np.array([0, 5, 3, 7, 10], np.int32), rows, "expert_offsets decreases"),
+        ("row id", off, np.array([0, 5, 11, 2, 12, 9, 4, 1, 7, 3], np.int32), "row id outside"),
+        ("negative row id", off, np.array([0, 5, 11, 2, 2, 9, -1, 1, 7, 3], np.int32), "row id outside"),
+    ]
+    qr.qr_set_debug(True)
+    try:
+        y1 = qr.qr_w8a8_grouped_linear(qr.QR_INT8, dev(off), dev(rows), total, dev(xc), dev(xs), dev(wc), dev(ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y1), host(y0))
+        for what, o, r, text in bad_cases:
+            log("grouped debug check: %s" % what)
+            y = torch.full((total, n), 7.0, dtype=torch.bfloat16, device="cuda")
+            with pytest.raises(qr.QRError) as ei:
+                qr.qr_w8a8_grouped_linear(qr.QR_INT8, dev(o), dev(r), total, dev(xc), dev(xs), dev(wc), dev(ws), y=y)
+            assert ei.value.status == 1 and text in str(ei.value), (what, str(ei.value))
+            torch.cuda.synchronize()
+            assert bool((y == 7.0).all()), what
+    finally:
+        qr.qr_set_debug(False)
+    # debug off again: the lists are trusted (and clamped) as before, no error
+    qr.qr_w8a8_grouped_linear(qr.QR_INT8, dev(bad_cases[2][1]), dev(rows), total, dev(xc), dev(xs), dev(wc), dev(ws))
+    torch.cuda.synchronize()
+
+
 def _assert_rows_within_bound(y, keep, oq, off, rows, xc, xs, wc, ws, what):
     """The element-wise bound on the rows marked in keep (the others are checked by the caller)."""
     acc, bnd, xw = grouped_exact(oq, off, rows, xc, xs, wc, ws)
