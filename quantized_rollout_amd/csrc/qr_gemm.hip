@@ -214,13 +214,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(int64_t m, int64_t n
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Ring-pipelined GEMM: 256 x 256 outputs per workgroup, eight wavefronts (two per SIMD) of 128 x 64 outputs
-// each (4 x 2 fragments of the 32x32 MFMA: v_mfma_i32_32x32x32_i8, or v_mfma_scale_f32_32x32x64_f8f6f4 with
-// E4M3 operands and unit block scales), 128 accumulators per lane. K advances in 64-byte stages through a ring
-// of four LDS buffers filled straight from memory by buffer loads with the LDS flag (no registers in between),
-// up to three stages ahead of the MFMAs. A workgroup's loads are spread over all eight wavefronts: the rate at
-// which one wavefront's memory instructions are served is limited, so more wavefronts issuing them fetch
-// more per CU. Each buffer holds the stage's 256 activation rows then its 256 weight rows, 64 bytes each, with
+// Ring-pipelined GEMM: BM x BN outputs per workgroup (BM = 256 or 128 activation rows, BN = 256, 128 or 64
+// channels), wavefronts of 64 x 64 outputs each (2 x 2 fragments of the 32x32 MFMA: v_mfma_i32_32x32x32_i8,
+// or v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit block scales), 64 accumulators per lane. K
+// advances in 64-byte stages through a ring of four LDS buffers filled straight from memory by buffer loads
+// with the LDS flag (no registers in between), up to three stages ahead of the MFMAs. A workgroup's loads are
+// spread over all its wavefronts: the rate at which one wavefront's memory instructions are served is
+// limited, so more wavefronts issuing them fetch more per CU. Each buffer holds the stage's BM activation rows
+// then its BN weight rows, 64 bytes each, with
 // logical 16-byte piece c of row r stored at physical piece c ^ ring_swizzle(r). The buffer resources bound
 // the rows (rows past m or n load zeros) and the partial last stage points its out-of-range pieces past the
 // end. A 32x32 fragment read gives lane l row (l & 31) and logical pieces (l >> 5) and 2 + (l >> 5) (INT8,
@@ -229,19 +230,24 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(int64_t m, int64_t n
 // (c + 32 (i / 4 mod 2)), register 4 (i / 8) + i mod 4.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kRingK = 64;   // K bytes per stage
-constexpr int kRingN = 256;  // weight rows (output channels) per tile
 
-// Tile of BM activation rows (256, or 128 for small batches) x 256 channels: BM / 16 wavefronts of 64 x 64
-// outputs in a (BM / 64) x 4 arrangement, each loading 16 activation rows and 256 / (BM / 16) weight rows of
-// every stage.
-template <int BM>
+// Tile of BM activation rows x BN channels: BM BN / 4096 wavefronts of 64 x 64 outputs in a (BM / 64) x (BN / 64)
+// arrangement, each loading BM / waves activation rows and BN / waves weight rows (16 per load) of every stage.
+// The narrow tiles are for few-row batches, where 256-channel tiles leave most CUs idle or need many K splits.
+template <int BM, int BN>
 struct Ring {
-    static constexpr int kWaves = BM / 16;
+    static constexpr int kWaves = BM * BN / 4096;
+    static constexpr int kWavesN = BN / 64;  // wavefronts across the channels
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kBuf = (BM + kRingN) * kRingK;  // bytes per ring buffer
-    static constexpr int kRowsB = kRingN / kWaves;       // weight rows loaded per wavefront
+    static constexpr int kBuf = (BM + BN) * kRingK;  // bytes per ring buffer
+    static constexpr int kRowsA = BM / kWaves;       // activation rows loaded per wavefront
+    static constexpr int kRowsB = BN / kWaves;       // weight rows loaded per wavefront
+    static constexpr int kLoadsA = kRowsA / 16;
     static constexpr int kLoadsB = kRowsB / 16;
-    static constexpr int kLoads = 1 + kLoadsB;           // buffer loads per wavefront per stage
+    static constexpr int kLoads = kLoadsA + kLoadsB;  // buffer loads per wavefront per stage
+    static_assert(kRowsA % 16 == 0 && kRowsB % 16 == 0, "16 rows per load");
+    // the bf16 epilogue stages each wavefront's 64 x 64 outputs (8 KiB) in the ring
+    static_assert(kWaves * 8192 <= 4 * kBuf, "epilogue staging fits the ring");
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -263,13 +269,13 @@ struct Acc32<kFp8> {
     typedef float __attribute__((ext_vector_type(16))) type;
 };
 
-template <int QT, int BM>
-__global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
+template <int QT, int BM, int BN>
+__global__ __launch_bounds__((Ring<BM, BN>::kThreads), 1) void gemm_ring_kernel(
     int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq, const float *__restrict__ xs,
     const uint8_t *__restrict__ wq, const float *__restrict__ ws, void *__restrict__ y, int y_bf16,
     void *__restrict__ acc_out, int tiles_m, int tiles_n, int splits, int stages_per_split,
     void *__restrict__ partial, int dp_tiles) {
-    typedef Ring<BM> R;
+    typedef Ring<BM, BN> R;
     typedef typename Acc32<QT>::type acc_t;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * R::kBuf];  // local stage s in buffer s mod 4
 
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
         }
     }
     const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
-    const int64_t n0 = (int64_t)(tile / tiles_m) * kRingN;
+    const int64_t n0 = (int64_t)(tile / tiles_m) * BN;
     const int64_t all_stages = (k + kRingK - 1) / kRingK;
     const int64_t st0 = to_partial ? (int64_t)split * stages_per_split : 0;
     const int64_t stages = to_partial ? std::min<int64_t>(stages_per_split, all_stages - st0)  // >= 1 by construction
@@ -314,17 +320,22 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = wave / 4, wn = wave % 4;
+    const int wm = wave / R::kWavesN, wn = wave % R::kWavesN;
 
     // buffer resources over the whole operands: rows past the end load zeros
     const v4i rsa = make_rsrc(xq, (uint32_t)(m * k));
     const v4i rsb = make_rsrc(wq, (uint32_t)(n * k));
 
     // stage loads, 16 rows per instruction; lane l writes physical piece l & 3 of row l / 4 of the block, which
-    // holds logical piece (l & 3) ^ swz(row). Activation rows 16 wave ..; weight rows kRowsB wave ..
-    const int ra = wave * 16 + (lane >> 2);
-    const int lpa = (lane & 3) ^ ring_swizzle(ra);
-    const uint32_t offa = m0 + ra < m ? (uint32_t)((m0 + ra) * k + 16 * lpa) : kOutOfRange;
+    // holds logical piece (l & 3) ^ swz(row). Activation rows kRowsA wave ..; weight rows kRowsB wave ..
+    uint32_t offa[R::kLoadsA];
+    int lpa[R::kLoadsA];
+#pragma unroll
+    for (int q = 0; q < R::kLoadsA; ++q) {
+        const int r = wave * R::kRowsA + q * 16 + (lane >> 2);
+        lpa[q] = (lane & 3) ^ ring_swizzle(r);
+        offa[q] = m0 + r < m ? (uint32_t)((m0 + r) * k + 16 * lpa[q]) : kOutOfRange;
+    }
     uint32_t offb[R::kLoadsB];
     int lpb[R::kLoadsB];
 #pragma unroll
@@ -336,9 +347,11 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     auto issue = [&](int64_t gst, uint8_t *buf) {  // global stage gst into buffer buf
         const uint32_t k0 = (uint32_t)(gst * kRingK);
         const bool tail = gst >= full;
-        {
-            const bool in = !tail || (int64_t)k0 + 16 * lpa < k;
-            dma16(rsa, lds_addr(buf + (wave * 16) * kRingK), (in && offa != kOutOfRange) ? offa + k0 : kOutOfRange);
+#pragma unroll
+        for (int q = 0; q < R::kLoadsA; ++q) {
+            const bool in = !tail || (int64_t)k0 + 16 * lpa[q] < k;
+            dma16(rsa, lds_addr(buf + (wave * R::kRowsA + q * 16) * kRingK),
+                  (in && offa[q] != kOutOfRange) ? offa[q] + k0 : kOutOfRange);
         }
 #pragma unroll
         for (int q = 0; q < R::kLoadsB; ++q) {
@@ -357,36 +370,31 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     // fragment reads: lane row (l & 31), half h = l >> 5
     const int fr = lane & 31, h = lane >> 5;
     const int p0 = QT == kInt8 ? h : 2 * h, p1 = QT == kInt8 ? 2 + h : 2 * h + 1;
-    uint4 fa[2][2], fb[2][2];
-    auto read_frags = [&](const uint8_t *buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = wm * 64 + i * 32 + fr;
-            const int sw = ring_swizzle(r);
-            fa[i][0] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (p0 ^ sw));
-            fa[i][1] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (p1 ^ sw));
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = wn * 64 + j * 32 + fr;
-            const int sw = ring_swizzle(r);
-            fb[j][0] = *reinterpret_cast<const uint4 *>(buf + (BM + r) * kRingK + 16 * (p0 ^ sw));
-            fb[j][1] = *reinterpret_cast<const uint4 *>(buf + (BM + r) * kRingK + 16 * (p1 ^ sw));
+    struct Frags {
+        uint4 a[2][2], b[2][2];
+    };
+    // read x of a stage (x = 0..7): A fragment x / 2 piece x % 2 for x < 4, then B fragment (x - 4) / 2
+    auto read_one = [&](const uint8_t *buf, Frags &f, auto X) {
+        constexpr int x = decltype(X)::value;
+        if constexpr (x < 4) {
+            const int r = wm * 64 + (x / 2) * 32 + fr;
+            f.a[x / 2][x & 1] = *reinterpret_cast<const uint4 *>(buf + r * kRingK + 16 * (((x & 1) ? p1 : p0) ^ ring_swizzle(r)));
+        } else {
+            const int r = wn * 64 + ((x - 4) / 2) * 32 + fr;
+            f.b[(x - 4) / 2][x & 1] =
+                *reinterpret_cast<const uint4 *>(buf + (BM + r) * kRingK + 16 * (((x & 1) ? p1 : p0) ^ ring_swizzle(r)));
         }
     };
-    auto mfmas = [&]() {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if constexpr (QT == kInt8) {
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(fa[i][0]), v4(fb[j][0]), acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(fa[i][1]), v4(fb[j][1]), acc[i][j], 0, 0, 0);
-                } else {
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        v8(fa[i][0], fa[i][1]), v8(fb[j][0], fb[j][1]), acc[i][j], 0, 0, 0, 127, 0, 127);
-                }
-            }
+    // MFMA tile x (x = 0..3): fragments (x / 2, x % 2)
+    auto mfma_one = [&](const Frags &f, auto X) {
+        constexpr int x = decltype(X)::value, i = x / 2, j = x % 2;
+        if constexpr (QT == kInt8) {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(f.a[i][0]), v4(f.b[j][0]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(f.a[i][1]), v4(f.b[j][1]), acc[i][j], 0, 0, 0);
+        } else {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8(f.a[i][0], f.a[i][1]), v8(f.b[j][0], f.b[j][1]),
+                                                                         acc[i][j], 0, 0, 0, 127, 0, 127);
+        }
     };
     // wait until this wave's loads of a stage have landed (`later` = stages issued after it, 0..2) and its own
     // fragment reads are done; the barrier then makes every wave's loads of the stage visible and tells every
@@ -400,11 +408,12 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
             wait_vmcnt_lgkm0<0>();
         barrier_fenced();
     };
-
+    auto buffer = [&](int64_t s) { return ring + (int)(s & 3) * R::kBuf; };
     // Pipeline: stage s + 3 is loaded while stage s runs. Each step waits for its own stage, refills the buffer
     // of stage s - 1 (which every wave has finished reading before the barrier of step s) with stage s + 3,
-    // reads its fragments and runs its MFMAs; the wavefronts sharing a SIMD cover each other's fragment reads.
-    auto buffer = [&](int64_t s) { return ring + (int)(s & 3) * R::kBuf; };
+    // reads its fragments and runs its MFMAs; other wavefronts on the SIMD (or other workgroups on the CU, for
+    // the small tiles) cover each one's fragment reads.
+    Frags f;
 #pragma unroll
     for (int i = 0; i < 3; ++i)
         if (i < stages) issue(st0 + i, ring + i * R::kBuf);
@@ -412,13 +421,13 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
     for (; s + 3 < stages; ++s) {  // steady: two later stages in flight, one more issued here
         sync_stage(2);
         issue(st0 + s + 3, buffer(s + 3));
-        read_frags(buffer(s));
-        mfmas();
+        unroll<8>([&](auto X) { read_one(buffer(s), f, X); });
+        unroll<4>([&](auto X) { mfma_one(f, X); });
     }
     for (; s < stages; ++s) {  // the last (up to) three stages: nothing more to issue
         sync_stage(stages - s - 1);
-        read_frags(buffer(s));
-        mfmas();
+        unroll<8>([&](auto X) { read_one(buffer(s), f, X); });
+        unroll<4>([&](auto X) { mfma_one(f, X); });
     }
     wait_vmcnt<0>();  // no load may still be writing LDS when the wave ends
 
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
         // split-K: this split's raw accumulators into its slice of the partial sums, [split][m][nb] over the
         // split columns n_lo .. n - 1 (all of n unless whole-K tiles come first)
         typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
-        const int64_t n_lo = dp_tiles == 0 ? 0 : (int64_t)(dp_tiles / tiles_m) * kRingN, nb = n - n_lo;
+        const int64_t n_lo = dp_tiles == 0 ? 0 : (int64_t)(dp_tiles / tiles_m) * BN, nb = n - n_lo;
         part_t *P = static_cast<part_t *>(partial) + (int64_t)split * m * nb;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads, 1) void gemm_ring_kernel(
         sw[j] = ws[col < n ? col : n - 1];
     }
     // uniform over the workgroup (the barrier below is reached by every wavefront or by none)
-    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + kRingN <= n;
+    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + BN <= n;
     if (fast) {
         // bf16 tile through LDS: each wave converts its 64 x 64 outputs into its own 8 KiB of the ring (row
         // stride 128 bytes), then writes 16-byte row pieces with buffer stores (rows past m fall outside the
@@ -882,11 +891,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n
     }
 }
 
-template <int QT, int BM>
+template <int QT, int BM, int BN>
 hipError_t launch_ring(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const uint8_t *xq, const float *xs,
                        const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
                        hipStream_t stream) {
-    const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + kRingN - 1) / kRingN);
+    typedef Ring<BM, BN> R;
+    const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
     int grid;
     if (g.dp_tiles == 0) {
         grid = ((tiles_m * tiles_n * g.splits + 7) / 8) * 8;
@@ -894,7 +904,7 @@ hipError_t launch_ring(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const
         const int pieces = (tiles_m * tiles_n - g.dp_tiles) * g.splits;
         grid = 8 * (g.dp_tiles / 8 + (pieces + 7) / 8);
     }
-    hipLaunchKernelGGL((gemm_ring_kernel<QT, BM>), dim3(grid), dim3(Ring<BM>::kThreads), 0, stream, m, n, k, xq, xs,
+    hipLaunchKernelGGL((gemm_ring_kernel<QT, BM, BN>), dim3(grid), dim3(R::kThreads), 0, stream, m, n, k, xq, xs,
                        wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits, g.stages_per_split,
                        workspace, g.dp_tiles);
     if (g.splits > 1)
@@ -944,9 +954,16 @@ hipError_t launch_q(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const ui
                     hipStream_t stream) {
     switch (g.tile) {
         case kGemmRing:
-            if (g.bm == 128)
-                return launch_ring<QT, 128>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
-            return launch_ring<QT, 256>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
+#define QR_RING(BM_, BN_) launch_ring<QT, BM_, BN_>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream)
+            if (g.bm == 128) {
+                if (g.bn == 64) return QR_RING(128, 64);
+                if (g.bn == 128) return QR_RING(128, 128);
+                return QR_RING(128, 256);
+            }
+            if (g.bn == 64) return QR_RING(256, 64);
+            if (g.bn == 128) return QR_RING(256, 128);
+            return QR_RING(256, 256);
+#undef QR_RING
         case kGemmWide:
             return launch_wide<QT>(g, m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, workspace, stream);
         case 1: return launch_t<QT, 256, 128>(m, n, k, xq, xs, wq, ws, y, y_bf16, acc_out, stream);
@@ -992,30 +1009,50 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
     const int64_t stages = (k + stage_bytes - 1) / stage_bytes;
     const double per64 = (double)stage_bytes / 64.0;
     const int fbm = env_int("QR_GEMM_BM", 0);
+    const int fbn = env_int("QR_GEMM_BN", 0);
     const int fs = env_int("QR_GEMM_SPLITS", 0);
     const int64_t forced_sp = fs >= 1 ? std::min<int64_t>(fs, stages) : 0;
     g.bm = (m <= 128 && g.tile != kGemmWide) ? 128 : 256;
+    g.bn = 256;
     g.stages_per_split = (int)stages;
+    // microseconds per 64 bytes of K of one workgroup, by tile (rows, channels). The narrow ring tiles are
+    // scaled from one-round measurements (MI355X, FP8, one 4096-deep tile per CU: 0.47 / 0.64 / 0.88 us for 128 x
+    // 64 / 128 / 256, 0.56 / 0.85 / 1.16 us for 256 x 64 / 128 / 256) by the ratio of the fitted 256-channel
+    // costs to their one-round figures. They pay where 256-channel tiles leave CUs idle or need many K splits:
+    // the 7B qkv and o at m = 128 (21.9 -> 18.1, 21.0 -> 16.7 us) and m = 512 (29.3 -> 24.8, 27.9 -> 24.4 us).
+    auto stage_us = [&](int bm, int bn) -> double {
+        if (g.tile == kGemmWide) return 0.83;
+        if (bn == 256) return bm == 128 ? 0.65 : 0.83;
+        if (bn == 128) return bm == 128 ? 0.47 : 0.61;
+        return bm == 128 ? 0.35 : 0.40;
+    };
+    auto tile_ok = [&](int bm, int bn) {
+        if ((fbm == 128 || fbm == 256) && fbm != bm) return false;
+        if ((fbn == 64 || fbn == 128 || fbn == 256) && fbn != bn) return false;
+        if (g.tile == kGemmWide) return bm == kWideM && bn == kWideN;
+        return true;
+    };
     double best = 1e30;
-    for (int bm : {128, 256}) {
-        if ((fbm == 128 || fbm == 256) && fbm != bm) continue;
-        if (g.tile == kGemmWide && bm != kWideM) continue;
-        const int64_t tiles = count(bm, kRingN);
-        for (int64_t sp = forced_sp ? forced_sp : 1; sp <= (forced_sp ? forced_sp : 16); ++sp) {
-            if (!forced_sp && sp > 1 && (stages + sp - 1) / sp < min_stages) break;
-            const int64_t sps = (stages + sp - 1) / sp;
-            const int64_t used = (stages + sps - 1) / sps;  // no split without a stage
-            const int64_t rounds = (tiles * used + 255) / 256;
-            double t = (double)rounds * (double)sps * (bm == 128 ? 0.65 : 0.83) * per64;
-            if (used > 1) t += 5.0 + (double)used * (double)m * (double)n * 8.0 / 5.0e6;
-            if (t < best) {
-                best = t;
-                g.bm = bm;
-                g.stages_per_split = (int)sps;
-                g.splits = (int)used;
+    for (int bm : {128, 256})
+        for (int bn : {256, 128, 64}) {
+            if (!tile_ok(bm, bn)) continue;
+            const int64_t tiles = count(bm, bn);
+            for (int64_t sp = forced_sp ? forced_sp : 1; sp <= (forced_sp ? forced_sp : 16); ++sp) {
+                if (!forced_sp && sp > 1 && (stages + sp - 1) / sp < min_stages) break;
+                const int64_t sps = (stages + sp - 1) / sp;
+                const int64_t used = (stages + sps - 1) / sps;  // no split without a stage
+                const int64_t rounds = (tiles * used + 255) / 256;
+                double t = (double)rounds * (double)sps * stage_us(bm, bn) * per64;
+                if (used > 1) t += 5.0 + (double)used * (double)m * (double)n * 8.0 / 5.0e6;
+                if (t < best) {
+                    best = t;
+                    g.bm = bm;
+                    g.bn = bn;
+                    g.stages_per_split = (int)sps;
+                    g.splits = (int)used;
+                }
             }
         }
-    }
     // Whole rounds of tiles over all of K, then the remaining tiles (a band of output columns) split over K
     // so that their pieces fill one more round: for tile counts just past a multiple of the CU count (the 7B
     // gate/up at m = 512: 296 tiles of 256 x 256), where the last round would otherwise run few tiles over all
@@ -1023,24 +1060,25 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
     const int round = std::max(8, env_int("QR_GEMM_ROUND", 256) / 8 * 8);
     const int fh = env_int("QR_GEMM_HYB", -1);  // -1 automatic, 0 never, >= 2 that many splits where possible
     if (fh != 0 && !(fs >= 1)) {
-        for (int bm : {128, 256}) {
-            if ((fbm == 128 || fbm == 256) && fbm != bm) continue;
-            if (g.tile == kGemmWide && bm != kWideM) continue;
-            const int64_t tm = (m + bm - 1) / bm, tiles = count(bm, kRingN);
+        for (int bm : {128, 256})
+            for (int bn : {256, 128, 64}) {
+            if (!tile_ok(bm, bn)) continue;
+            const int64_t tm = (m + bm - 1) / bm, tiles = count(bm, bn);
             if (tiles <= round || round % tm != 0 || tiles % round == 0) continue;
             const int64_t dp = tiles / round * round, rem = tiles - dp;
-            const int64_t n_lo = dp / tm * kRingN;
+            const int64_t n_lo = dp / tm * bn;
             for (int64_t sp = fh >= 2 ? fh : 2; sp <= (fh >= 2 ? fh : 16); ++sp) {
                 const int64_t sps = (stages + sp - 1) / sp;
                 const int64_t used = (stages + sps - 1) / sps;
                 if (used < 2) break;
                 if (fh < 2 && (sps < min_stages || rem * used > round)) continue;
-                const double c = (bm == 128 ? 0.65 : 0.83) * per64;
+                const double c = stage_us(bm, bn) * per64;
                 const double t = (double)(dp / round) * (double)stages * c + (double)((rem * used + round - 1) / round) *
                                  (double)sps * c + 5.0 + (double)used * (double)m * (double)(n - n_lo) * 8.0 / 5.0e6;
                 if (fh >= 2 || t < best) {
                     best = fh >= 2 ? -1.0 : t;
                     g.bm = bm;
+                    g.bn = bn;
                     g.stages_per_split = (int)sps;
                     g.splits = (int)used;
                     g.dp_tiles = (int)dp;

@@ -28,6 +28,7 @@ struct GemmPlan {
     int tile;              // kGemmRing = LDS-ring kernel, kGemmWide = wide-wave kernel (128 x 128 per wavefront);
                            // register-staged 1 = 256x128, 2 = 128x256, 3 = 128x128
     int bm;                // ring: activation rows per tile (128 or 256)
+    int bn;                // ring: channels per tile (256, 128 or 64); the wide kernel: 256
     int splits;            // ring: K splits (1 = none; else partial sums in the workspace + a reduction)
     int stages_per_split;  // ring / wide: K stages per split (64 bytes each for the ring, 128 for the wide kernel)
     int dp_tiles;          // ring: > 0: the first dp_tiles tiles (whole CU rounds) run over all of K and only the

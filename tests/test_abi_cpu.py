@@ -233,7 +233,9 @@ def test_workspace_sizes(monkeypatch):
         # few tiles: the planner's cost model splits K (runs of at least 4 stages of 64 bytes); the partial sums
         # take splits x m x n x 4 bytes
         assert B.qr_workspace_bytes(q, 512, 3584, 18944) == 9 * 512 * 3584 * 4    # 28 tiles of 256 x 256
-        assert B.qr_workspace_bytes(q, 128, 4608, 3584) == 7 * 128 * 4608 * 4     # 18 tiles of 128 x 256
+        assert B.qr_workspace_bytes(q, 128, 4608, 3584) == 3 * 128 * 4608 * 4     # 72 tiles of 128 x 64
+        assert B.qr_workspace_bytes(q, 128, 3584, 18944) == 9 * 128 * 3584 * 4    # 28 tiles of 128 x 128
+        assert B.qr_workspace_bytes(q, 512, 3584, 3584) == 0                       # 224 tiles of 128 x 64
         assert B.qr_workspace_bytes(q, 2048, 3584, 18944) == 2 * 2048 * 3584 * 4  # 112 tiles, 296 stages
         # forced split counts never leave a split without a stage: 17 stages in 16 requested splits -> 9
         monkeypatch.setenv("QR_GEMM_SPLITS", "3")

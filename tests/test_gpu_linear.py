@@ -245,31 +245,39 @@ GEMM_SHAPES = [(65, 264, 16), (300, 512, 1040), (257, 520, 176), (130, 333, 4160
                (100, 1000, 1552)]
 WIDE_SHAPES = [(65, 264, 128), (300, 512, 1024), (257, 520, 256), (130, 333, 4096), (512, 768, 2048),
                (100, 1000, 1536), (300, 520, 1040)]
-GEMM_CASES = [(0, None, None), (0, 1, 128), (0, 1, 256), (0, 3, 128), (0, 3, 256), (0, 64, 256), (4, None, None),
-              (4, 1, 256), (4, 3, 256), (4, 64, 256), (1, None, None), (2, None, None), (3, None, None)]
+# (kernel, K splits, activation rows per tile, channels per tile): the ring kernel also with its narrow
+# channel tiles (64 and 128 channels, 2 to 8 wavefronts per workgroup)
+GEMM_CASES = [(0, None, None, None), (0, 1, 128, 256), (0, 1, 256, 256), (0, 3, 128, 256), (0, 3, 256, 256),
+              (0, 64, 256, 256), (0, 1, 128, 64), (0, 3, 128, 128), (0, None, 256, 64), (0, 2, 256, 128),
+              (4, None, None, None), (4, 1, 256, None), (4, 3, 256, None), (4, 64, 256, None),
+              (1, None, None, None), (2, None, None, None), (3, None, None, None)]
 STAGE_BYTES = {0: 64, 4: 128}
 
 
-@pytest.mark.parametrize("tile,splits,bm", GEMM_CASES)
-def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
+@pytest.mark.parametrize("tile,splits,bm,bn", GEMM_CASES)
+def test_every_gemm_tile(tile, splits, bm, bn, monkeypatch, capfd):
     monkeypatch.setenv("QR_GEMM_TILE", str(tile))
     if splits is not None:
         monkeypatch.setenv("QR_GEMM_SPLITS", str(splits))
     if bm is not None:
         monkeypatch.setenv("QR_GEMM_BM", str(bm))
+    if bn is not None:
+        monkeypatch.setenv("QR_GEMM_BN", str(bn))
     monkeypatch.setenv("QR_TRACE", "1")
     wsp = qr.Workspace()
     for i, (m, n, k) in enumerate(WIDE_SHAPES if tile == 4 else GEMM_SHAPES):
         ran = tile if tile != 4 or k % 128 == 0 else 0
         for oq in (O.INT8, O.FP8):
             xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1300 + 10 * i + oq)
-            what = "gemm tile=%s splits=%s bm=%s %s m=%d n=%d k=%d" % (tile, splits, bm, oq, m, n, k)
+            what = "gemm tile=%s splits=%s bm=%s bn=%s %s m=%d n=%d k=%d" % (tile, splits, bm, bn, oq, m, n, k)
             log(what)
             _check(oq, xc, xs, wc, ws, what)
             err = capfd.readouterr().err
             assert "kind=1" in err and "gemm=%d" % ran in err, err
             if bm is not None:
                 assert "bm=%d" % bm in err, err
+            if bn is not None and ran == 0:
+                assert "bn=%d" % bn in err, err
             if splits is not None:
                 stages = -(-k // STAGE_BYTES[ran])
                 sps = -(-stages // min(splits, stages))
@@ -287,19 +295,23 @@ def test_every_gemm_tile(tile, splits, bm, monkeypatch, capfd):
 
 # Whole rounds of tiles over all of K first, then the remaining band of output columns split over K: the planner's
 # choice for tile counts just past a whole number of CU rounds, forced here with a round of 8 tiles.
-# (m, n, k, rows per tile, splits, whole-K tiles): 2 x 11 tiles with a ragged 3-tile band and a partial last
-# stage (wide kernel: a shorter last split); 2 x 9 tiles with a one-tile band of 253 columns (element-wise
-# reduction) and a one-stage last split; 1 x 9 tiles with 13 (wide kernel: 16) splits
-HYB_CASES = [(0, 300, 2600, 1040, 256, 3, 16), (0, 512, 2301, 1040, 256, 5, 16), (0, 100, 2304, 4160, 128, 16, 8),
-             (4, 300, 2600, 1024, 256, 3, 16), (4, 512, 2301, 1024, 256, 5, 16), (4, 200, 2304, 4096, 256, 16, 8)]
+# (m, n, k, rows per tile, channels per tile, splits, whole-K tiles): 2 x 11 tiles with a ragged 3-tile band and
+# a partial last stage (wide kernel: a shorter last split); 2 x 9 tiles with a one-tile band of 253 columns
+# (element-wise reduction) and a one-stage last split; 1 x 9 tiles with 13 (wide kernel: 16) splits; 2 x 41 tiles
+# of 64 channels with a one-column band of 40 channels
+HYB_CASES = [(0, 300, 2600, 1040, 256, 256, 3, 16), (0, 512, 2301, 1040, 256, 256, 5, 16),
+             (0, 100, 2304, 4160, 128, 256, 16, 8), (0, 300, 2600, 1040, 256, 64, 3, 80),
+             (4, 300, 2600, 1024, 256, 256, 3, 16), (4, 512, 2301, 1024, 256, 256, 5, 16),
+             (4, 200, 2304, 4096, 256, 256, 16, 8)]
 
 
-@pytest.mark.parametrize("tile,m,n,k,bm,splits,dp", HYB_CASES)
-def test_gemm_whole_tiles_then_split_band(tile, m, n, k, bm, splits, dp, monkeypatch, capfd):
+@pytest.mark.parametrize("tile,m,n,k,bm,bn,splits,dp", HYB_CASES)
+def test_gemm_whole_tiles_then_split_band(tile, m, n, k, bm, bn, splits, dp, monkeypatch, capfd):
     monkeypatch.setenv("QR_GEMM_TILE", str(tile))
     monkeypatch.setenv("QR_GEMM_ROUND", "8")
     monkeypatch.setenv("QR_GEMM_HYB", str(splits))
     monkeypatch.setenv("QR_GEMM_BM", str(bm))
+    monkeypatch.setenv("QR_GEMM_BN", str(bn))
     monkeypatch.setenv("QR_TRACE", "1")
     stages = -(-k // STAGE_BYTES[tile])
     sps = -(-stages // splits)
@@ -307,11 +319,12 @@ def test_gemm_whole_tiles_then_split_band(tile, m, n, k, bm, splits, dp, monkeyp
     wsp = qr.Workspace()
     for oq in (O.INT8, O.FP8):
         xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1700 + m + oq)
-        what = "gemm band split tile=%d %s m=%d n=%d k=%d bm=%d splits=%d" % (tile, oq, m, n, k, bm, splits)
+        what = "gemm band split tile=%d %s m=%d n=%d k=%d bm=%d bn=%d splits=%d" % (tile, oq, m, n, k, bm, bn, splits)
         log(what)
         _check(oq, xc, xs, wc, ws, what)
         err = capfd.readouterr().err
         assert "kind=1" in err and "gemm=%d bm=%d splits=%d dp=%d " % (tile, bm, used, dp) in err, err
+        assert "bn=%d" % bn in err, err
         y_acc, _ = _run(oq, xc, xs, wc, ws)
         for rep in range(2):  # one workspace object, called again: the same bytes
             y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
