@@ -58,6 +58,8 @@ DOMINANT = ("gate_up", 2048)  # the kernel that dominates the step: the FP8 gate
 PROFILE_KERNELS = {
     "a3_fp8_gate_up_m2048": ("fp8", 2048, 37888, 3584),
     "a3_fp8_gate_up_m512": ("fp8", 512, 37888, 3584),
+    "a3_fp8_gate_up_m128": ("fp8", 128, 37888, 3584),
+    "a3_fp8_qkv_m128": ("fp8", 128, 4608, 3584),
     "a3_fp8_gate_up_m1": ("fp8", 1, 37888, 3584),
     "a3_fp8_gate_up_m16": ("fp8", 16, 37888, 3584),
     "a3_fp8_down_m1": ("fp8", 1, 3584, 18944),

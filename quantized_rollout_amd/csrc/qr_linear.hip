@@ -722,9 +722,10 @@ bool linear_bf16_fused(const LinearPlan &p, int qtype, int64_t m, int64_t k) {
     // at m = 2 or 4.
     const int64_t max_m = env_int("QR_FUSE_MAX_M", 1);
     if (qtype == kFp8 && k > env_int("QR_FUSE_MAX_K_FP8", 8192)) return false;
+    if (p.kind != 0 || p.m_tiles != 1 || p.splits != 1 || p.unroll != 4 || p.tiles < 1) return false;  // GEMV only
     const int64_t blocks = (p.n_tiles + p.tiles - 1) / p.tiles;
-    return p.kind == 0 && p.m_tiles == 1 && p.splits == 1 && p.unroll == 4 && blocks < env_int("QR_FUSE_MAX_BLOCKS", 1024) &&
-           m <= std::min<int64_t>(max_m, kFuseRows) && gemv_fused_lds_bytes(p, m, k) <= 65536;
+    return blocks < env_int("QR_FUSE_MAX_BLOCKS", 1024) && m <= std::min<int64_t>(max_m, kFuseRows) &&
+           gemv_fused_lds_bytes(p, m, k) <= 65536;
 }
 
 size_t linear_bf16_workspace_bytes(const LinearPlan &p, int qtype, int64_t m, int64_t k) {

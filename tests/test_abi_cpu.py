@@ -212,6 +212,18 @@ def test_linear_bf16_validation_and_workspace(monkeypatch):
     assert call(m=16, n=2048, k=1536) == B.QR_ERR_WORKSPACE
 
 
+def test_linear_bf16_workspace_every_batch():
+    """The bf16 entry point's workspace query for decode (GEMV) and large (GEMM) plans alike: no fused form past one
+    token tile, so the activation codes and scales come first, then the linear's own workspace."""
+    up = lambda b: (b + 255) // 256 * 256
+    for q in (B.QR_INT8, B.QR_FP8_E4M3):
+        for n, k in ((4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944), (2048, 1536), (1536, 8960)):
+            for m in (1, 2, 16, 17, 64, 65, 128, 512, 2048, 4096):
+                need = B.qr_w8a8_linear_bf16_workspace_bytes(q, m, n, k)
+                if m > 16:
+                    assert need == up(m * k) + up(4 * m) + B.qr_workspace_bytes(q, m, n, k), (q, m, n, k)
+
+
 def test_workspace_sizes(monkeypatch):
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
         # GEMV plans with enough blocks, and GEMM plans with a tile for at least half the CUs, reduce inside

@@ -37,9 +37,9 @@ def _case(m, n, k, q, seed, with_s):
 
 # decode shapes (the 1.5B down and gate/up, ragged n and a k with a partial last 256-byte slice) and batches
 # on both sides of the fusion threshold (the 17920-channel gate/up, 1120 workgroups, above the workgroup limit of
-# the fused form, at two batches to keep the oracle quick)
-SHAPES = [(1536, 8960, (1, 3, 4, 5, 16, 64)), (17920, 1536, (1, 4)), (200, 1040, (1, 3, 4, 5, 16, 64)),
-          (37, 272, (1, 3, 4, 5, 16, 64))]
+# the fused form, at two batches to keep the oracle quick; batches past 64 run the quantizer and then a GEMM plan)
+SHAPES = [(1536, 8960, (1, 3, 4, 5, 16, 64)), (17920, 1536, (1, 4)), (200, 1040, (1, 3, 4, 5, 16, 64, 65, 130)),
+          (37, 272, (1, 3, 4, 5, 16, 64, 300))]
 
 
 @pytest.mark.parametrize("q", [O.INT8, O.FP8])
