@@ -7,6 +7,7 @@ Learning with Quantized Rollout", section 3, Eq. (2), with 4 exponent and 3 mant
 no infinity, 0x7F/0xFF NaN). Nothing here calls the C oracle; tests compare the two.
 """
 from fractions import Fraction
+import math
 import struct
 
 QMAX = {0: 127, 1: 448}  # INT8, FP8
@@ -38,6 +39,34 @@ def round_f32(q: Fraction) -> Fraction:
     quantum = Fraction(2) ** (e - 23)
     n = round(a / quantum)  # Fraction.__round__ rounds half to even
     return sign * n * quantum
+
+
+def round_bf16_signed_sqrt(sign: int, v2: Fraction) -> Fraction:
+    """The bfloat16 value nearest to sign * sqrt(v2) for a rational v2 >= 0, ties to even (8-bit significand,
+    smallest normal 2^-126, subnormal quantum 2^-133), decided by exact comparisons of squares, so no square
+    root is ever rounded. Overflow is not modelled."""
+    if v2 == 0:
+        return Fraction(0)
+    e = max(_floor_log2(v2) // 2, -126)  # 2^(2e) <= v2 < 2^(2e + 2): the binade of sqrt(v2)
+    quantum = Fraction(2) ** (e - 7)
+    t = v2 / quantum ** 2  # (sqrt(v2) / quantum)^2
+    n = math.isqrt(t.numerator // t.denominator)  # floor(sqrt(t))
+    mid2 = Fraction(2 * n + 1, 2) ** 2
+    if t > mid2 or (t == mid2 and n % 2 == 1):
+        n += 1
+    return sign * n * quantum
+
+
+def rmsnorm_row(x, gamma, eps):
+    """RMSNorm of one row, exactly rounded: bf16(x_j gamma_j / sqrt(sum x^2 / K + eps)) for Python floats that
+    hold bfloat16 (x) and fp32 (gamma, eps) values; 0 where x_j gamma_j = 0 or the radicand is 0."""
+    xs = [f32_value(v) for v in x]
+    D = sum(v * v for v in xs) / len(xs) + f32_value(eps)
+    out = []
+    for v, g in zip(xs, gamma):
+        p = v * f32_value(g)
+        out.append(Fraction(0) if p == 0 or D == 0 else round_bf16_signed_sqrt(1 if p > 0 else -1, p * p / D))
+    return out
 
 
 def neg_zero_sign(x: float) -> bool:

@@ -66,6 +66,8 @@ def lib():
         L.or_silu_mul.restype = None
         L.or_moe_combine.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp]
         L.or_moe_combine.restype = None
+        L.or_rmsnorm.argtypes = [vp, i64, i64, vp, ctypes.c_float, vp]
+        L.or_rmsnorm.restype = None
         L.or_quantize_w4.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp]
         L.or_quantize_w4.restype = None
         L.or_w4a16_linear.argtypes = [i64, i64, i64, vp, vp, vp, i64, i32, vp, vp]
@@ -311,6 +313,27 @@ def moe_combine(y_down, topk_weight, pair_rows):
     out = np.empty((T, H), np.uint16)
     lib().or_moe_combine(_p(y_down), R, _p(topk_weight), _p(pair_rows), T, k, H, _p(out))
     return out
+
+
+# ---- next row: the producer of a linear's quantized input ---------------------------------------------
+def rmsnorm(x, gamma, eps):
+    """h [R, K] = bf16(x q gamma), q = 1 / sqrt(mean(x^2) + eps) per row (0 for a zero radicand), in double;
+    x bfloat16 bits [R, K], gamma fp32 [K], eps a float32 value. Returns bfloat16 bits."""
+    x = _c(x, np.uint16)
+    gamma = _c(gamma, np.float32)
+    R, K = x.shape
+    assert gamma.shape == (K,)
+    h = np.empty((R, K), np.uint16)
+    lib().or_rmsnorm(_p(x), R, K, _p(gamma), float(np.float32(eps)), _p(h))
+    return h
+
+
+def rmsnorm_quantize(x, gamma, eps, qtype, s=None):
+    """The producer's outputs: h = rmsnorm(x, gamma, eps), then the token-wise quantizer of h (with h diag(1/s)
+    when s is given). Returns (codes, scales, h)."""
+    h = rmsnorm(x, gamma, eps)
+    codes, scales = quantize_rows(h, qtype, s=s, s_mode=S_MUL_RECIP if s is not None else S_NONE, in_type=BF16)
+    return codes, scales, h
 
 
 # ---- next row: requantize + diff -----------------------------------------------------------------------

@@ -14,7 +14,9 @@
  *    kernels, so that codes and scales can be compared bit for bit;
  *  - accumulators are exact (64-bit integers);
  *  - the dequantized output is computed in fp64 from the exact accumulator and rounded once to fp32 or
- *    bfloat16.
+ *    bfloat16;
+ *  - the producers of a linear's input (the SiLU-gated product, RMSNorm) are computed in fp64 and rounded
+ *    once to bfloat16, the precision the next quantizer reads.
  */
 #include "qr_oracle.h"
 
@@ -502,6 +504,31 @@ void or_moe_combine(const uint16_t *y_down, int64_t R, const float *topk_weight,
             }
             out[t * H + c] = or_round_to_bf16(acc);
         }
+}
+
+/* ------------------------------------------------------------------------------------------------------
+ * next row: the producer of a linear's quantized input (RMSNorm, then the token-wise quantizer)
+ * ---------------------------------------------------------------------------------------------------- */
+
+/* h[r][j] = bf16(x[r][j] * q[r] * gamma[j]), q[r] = 1 / sqrt(sum_j x[r][j]^2 / K + eps), in double, the products
+ * taken left to right and rounded once to bfloat16; q[r] = 0 where the radicand is 0 (an all-zero row with
+ * eps = 0). The pages give no normalization: reading, the RMSNorm ahead of each attention and MLP block of the
+ * Qwen decoders they quantize, whose output is the activation X that [QuRL] 4.3 rescales (W X = (W / s)(s X))
+ * and [QuRL] 5 quantizes token-wise. The squares of bfloat16 values are exact in double and are summed in
+ * order j = 0 .. K-1. */
+void or_rmsnorm(const uint16_t *x, int64_t R, int64_t K, const float *gamma, float eps, uint16_t *h) {
+    int64_t r, j;
+    for (r = 0; r < R; ++r) {
+        const uint16_t *xr = x + r * K;
+        double ss = 0.0, d, q;
+        for (j = 0; j < K; ++j) {
+            const double v = or_bf16_to_f32(xr[j]);
+            ss += v * v;
+        }
+        d = ss / (double)K + (double)eps;
+        q = d > 0.0 ? 1.0 / sqrt(d) : 0.0;
+        for (j = 0; j < K; ++j) h[r * K + j] = or_round_to_bf16((double)or_bf16_to_f32(xr[j]) * q * (double)gamma[j]);
+    }
 }
 
 /* ------------------------------------------------------------------------------------------------------

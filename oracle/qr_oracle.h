@@ -94,6 +94,11 @@ void or_silu_mul(const uint16_t *y_gu, int64_t R, int64_t I, uint16_t *h);
 void or_moe_combine(const uint16_t *y_down, int64_t R, const float *topk_weight, const int32_t *pair_rows,
                     int64_t T, int64_t k, int64_t H, uint16_t *out);
 
+/* next row: the producer form of the fused activation quantization. h = bf16(x q gamma) per row with
+ * q = 1 / sqrt(mean(x^2) + eps) (0 for a zero radicand), in double; the codes of h are those of
+ * or_quantize_rows on h. */
+void or_rmsnorm(const uint16_t *x, int64_t R, int64_t K, const float *gamma, float eps, uint16_t *h);
+
 /* next row: one publish of W + dW: the a1 quantizer, then per row the a5 triple against the previous
  * publish (row_counts [rows][3]: bytes, values, scale changed) and its sums in out3 */
 void or_requantize_weights(const void *in, int in_type, int64_t rows, int64_t k, const float *s, int qtype,

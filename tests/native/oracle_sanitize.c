@@ -136,6 +136,21 @@ static void run_w4_case(void) {
     free(w), free(s), free(sc), free(yf), free(codes), free(x), free(yb), free(yd);
 }
 
+static void run_rmsnorm_case(int qtype) {
+    const int64_t R = 3, K = 40;
+    uint16_t *x = malloc((size_t)(R * K) * 2), *h = malloc((size_t)(R * K) * 2);
+    float *g = malloc((size_t)K * 4), *s = malloc((size_t)K * 4), *sc = malloc((size_t)R * 4);
+    uint8_t *c = malloc((size_t)(R * K));
+    int64_t i;
+    for (i = 0; i < R * K; ++i) x[i] = i < K ? 0 : to_bf16(frand() * 3.0f); /* row 0 all zero */
+    for (i = 0; i < K; ++i) g[i] = 0.5f + frand() * 0.25f, s[i] = 1.0f + 0.5f * (float)(i % 2);
+    or_rmsnorm(x, R, K, g, 0.0f, h);
+    for (i = 0; i < K; ++i) CHECK(h[i] == 0 || h[i] == 0x8000); /* a zero row stays zero (no 0 * inf) */
+    or_rmsnorm(x, R, K, g, 1e-6f, h);
+    or_quantize_rows(h, OR_BF16, R, K, s, OR_S_MUL_RECIP, qtype, c, sc);
+    free(x), free(h), free(g), free(s), free(sc), free(c);
+}
+
 int main(void) {
     static const float probes[] = {0.0f, -0.0f, 1.0f, -448.0f, 448.0f, 1e-9f, 0.0009765625f, 3.14159f, -240.5f};
     uint8_t enc[9], enc2[9];
@@ -166,6 +181,8 @@ int main(void) {
     run_publish_case(OR_INT8, 0);
     run_publish_case(OR_FP8, 1);
     run_w4_case();
+    run_rmsnorm_case(OR_INT8);
+    run_rmsnorm_case(OR_FP8);
     printf("ok\n");
     return 0;
 }
