@@ -22,7 +22,8 @@ HBM traffic when profiles/ holds a FETCH_SIZE / WRITE_SIZE summary taken on the 
 decode layer's HBM fraction at M <= 16, and the CPU oracle timed on a bounded sample of the same step (one
 thread and all host cores). Unless --quick, `extra` holds the other workloads: the publish between RL steps on
 the 7B linears (fp32 masters, INT8 and FP8, with and without s; changed-code counts), the grouped MoE FFN, the
-1.5B-shaped INT8 linears, and W4A16.
+1.5B-shaped INT8 linears, W4A16, and the RMSNorm producer that quantizes a linear's input in the normalization's
+own pass.
 
 Counter runs for the traffic figure (each counter in a run of its own):
   rocprofv3 --pmc FETCH_SIZE -d DIR_F -o t --output-format csv -- python3 bench.py --profile-kernel NAME
@@ -656,6 +657,50 @@ ROW_SOURCES = {"a1": ["qr_quantize.hip"], "a2": ["qr_quantize.hip"], "a5": ["qr_
 SHARED_SOURCES = ["qr_device.hpp", "qr_internal.hpp", "qr_abi.hip"]
 
 
+def measure_rmsnorm_producer(dev, reps):
+    """The RMSNorm producer of a linear's FP8 input on the 7B hidden size (3584) at every batch of the step, eps
+    1e-6, with the invariant scale: the fused call against the two launches it replaces (the library RMSNorm of
+    PyTorch on bf16, then the activation quantizer), and the quantizer alone. A 7B decoder layer has two such
+    producers (ahead of qkv and of gate/up)."""
+    import torch
+
+    import quantized_rollout_amd as qr
+    from quantized_rollout_amd import synth
+
+    K, INNER = 3584, 20
+    out = {}
+    for m in BATCHES_7B:
+        inp = synth.make_norm_inputs(m, K, seed=5)
+        x = torch.from_numpy(inp.x.view("int16")).view(torch.bfloat16).to(dev)
+        g, s = torch.from_numpy(inp.gamma).to(dev), torch.from_numpy(inp.s).to(dev)
+        gb = g.to(torch.bfloat16)
+        c = torch.empty((m, K), dtype=torch.uint8, device=dev)
+        sc = torch.empty((m,), dtype=torch.float32, device=dev)
+
+        def fused():
+            for _ in range(INNER):
+                qr.qr_rmsnorm_quantize(x, g, 1e-6, qr.QR_FP8_E4M3, s=s, codes=c, scales=sc)
+
+        def pair():
+            for _ in range(INNER):
+                hn = torch.nn.functional.rms_norm(x, (K,), gb, 1e-6)
+                qr.qr_quantize_acts(hn, qr.QR_FP8_E4M3, s=s, codes=c, scales=sc)
+
+        def quant():
+            for _ in range(INNER):
+                qr.qr_quantize_acts(x, qr.QR_FP8_E4M3, s=s, codes=c, scales=sc)
+
+        t = {name: TimedGraph(fn, INNER).time_ms(reps) * 1e3 / INNER
+             for name, fn in (("fused", fused), ("norm_then_quantize", pair), ("quantize_alone", quant))}
+        out["m%d" % m] = {"us_fused": round(t["fused"], 2), "us_norm_then_quantize": round(t["norm_then_quantize"], 2),
+                          "us_quantize_alone": round(t["quantize_alone"], 2),
+                          "saved_us_per_layer": round(2 * (t["norm_then_quantize"] - t["fused"]), 2),
+                          "GB/s": round(m * K * 3 / t["fused"] / 1e3, 1)}
+        log("rmsnorm producer m=%d: fused %.2f us, norm + quantize %.2f us, quantize alone %.2f us"
+            % (m, t["fused"], t["norm_then_quantize"], t["quantize_alone"]))
+    return out
+
+
 def sources_digest(name):
     """sha256 over the library sources of `name`'s kernels: a traffic figure is only reported for the sources it
     was measured on."""
@@ -901,6 +946,8 @@ def main():
         extra["int8_1p5b_linears"] = measure_int8_1p5b(dev, r)
         log("W4A16 7B-shaped linears")
         extra["w4a16_7b_linears"] = measure_w4a16_7b(dev, r)
+        log("RMSNorm producer of the FP8 linears' input (7B hidden size)")
+        extra["rmsnorm_producer_7b"] = measure_rmsnorm_producer(dev, r)
 
     cpu = None
     if not args.no_cpu_baseline:

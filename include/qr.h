@@ -132,6 +132,25 @@ qr_status qr_w8a8_linear_noalloc(qr_qtype q, int64_t m, int64_t n, int64_t k, co
                                  qr_dtype y_type, void *acc_out, void *stream);
 
 /*
+ * RMSNorm fused with the per-token activation quantization of the next linear's input (next row: the activation
+ * quantization fused into its producer; [QuRL] 4.3: the X side of W X = (W / s)(s X), here h diag(1/s); [QuRL] 5:
+ * token-wise activation scales). The pages give no normalization; this is the RMSNorm ahead of the attention and
+ * MLP blocks of the Qwen decoders they quantize, whose output is the next linear's activation X:
+ *   h[r, j] = bf16(x[r, j] * q_r * gamma[j]), q_r = 1 / sqrt(sum_j x[r, j]^2 / k + eps) (q_r = 0 when the
+ *             radicand is 0), evaluated in fp64 with the products taken left to right, rounded once to
+ *             bfloat16 (nearest even);
+ *   h_codes [rows, k], h_scales [rows]: exactly qr_quantize_acts(h, QR_BF16, rows, k, s, q, ...),
+ * so the fused call gives the same bits as the normalization followed by the quantizer, in one pass over x.
+ * x: device bfloat16 [rows, k]; gamma: device fp32 [k] (the norm weight; bfloat16 weights convert exactly);
+ * eps: finite and >= 0; s: device fp32 [k] or NULL; h: device bfloat16 [rows, k] or NULL (the normalized
+ * activation itself, when wanted). x, gamma, h_codes and h 16-byte aligned; s and h_scales 4-byte aligned.
+ * k: a positive multiple of 16. rows == 0: nothing is launched. Errors: QR_ERR_ARG (negative rows, a null
+ * pointer, eps negative or not finite), QR_ERR_UNSUPPORTED (k, rows), QR_ERR_ALIGN.
+ */
+qr_status qr_rmsnorm_quantize(const void *x, int64_t rows, int64_t k, const float *gamma, float eps, const float *s,
+                              qr_qtype q, void *h_codes, float *h_scales, void *h, void *stream);
+
+/*
  * The W8A8 linear on bfloat16 activations (next row: the activation quantization fused with the linear):
  * the same result, bit for bit, as qr_quantize_acts(x, QR_BF16, m, k, s, q, ...) followed by qr_w8a8_linear on
  * its codes and scales (including acc_out). For single-token decode (m = 1; with FP8 for k <= 8192) the

@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "QR_OK", 1: "QR_ERR_ARG", 2: "QR_ERR_UNSUPPORTED", 3: "QR_ERR
 EXPORTS = ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
            "qr_count_code_changes", "qr_workspace_bytes", "qr_last_error", "qr_version", "qr_quantize_weights_w4",
            "qr_w4a16_linear", "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_w8a8_linear_bf16_workspace_bytes",
-           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine", "qr_w8a8_linear_noalloc", "qr_set_debug")
+           "qr_moe_route", "qr_silu_mul_quantize", "qr_moe_combine", "qr_w8a8_linear_noalloc", "qr_set_debug",
+           "qr_rmsnorm_quantize")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # QR_NOALLOC_SCRATCH_BYTES
 W4_GROUP = 128  # QR_W4_GROUP: input channels per INT4 scale group
 
@@ -68,11 +69,12 @@ def lib():
                 L.qr_w8a8_linear_bf16_workspace_bytes.restype = sz
                 L.qr_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
                 L.qr_silu_mul_quantize.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, vp]
+                L.qr_rmsnorm_quantize.argtypes = [vp, i64, i64, vp, ctypes.c_float, vp, i32, vp, vp, vp, vp]
                 L.qr_moe_combine.argtypes = [vp, i64, i64, vp, vp, i64, i64, vp, vp]
                 for f in ("qr_quantize_weights", "qr_quantize_acts", "qr_w8a8_linear", "qr_w8a8_grouped_linear",
                           "qr_count_code_changes", "qr_quantize_weights_w4", "qr_w4a16_linear",
                           "qr_requantize_weights", "qr_w8a8_linear_bf16", "qr_moe_route", "qr_silu_mul_quantize",
-                          "qr_moe_combine", "qr_w8a8_linear_noalloc"):
+                          "qr_moe_combine", "qr_w8a8_linear_noalloc", "qr_rmsnorm_quantize"):
                     getattr(L, f).restype = ctypes.c_int
                 L.qr_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
                 L.qr_workspace_bytes.restype = sz
@@ -418,6 +420,33 @@ def qr_silu_mul_quantize(y_gu, qtype, s=None, codes=None, scales=None, h=None, w
         _need(h.dtype == torch.bfloat16 and tuple(h.shape) == (rows, inter) and h.is_contiguous(), "bad h")
     _check(lib().qr_silu_mul_quantize(_ptr(y_gu), rows, inter, _ptr(s), int(qtype), _ptr(codes), _ptr(scales), _ptr(h),
                                       _stream(stream)))
+    return (codes, scales, h) if h is not None else (codes, scales)
+
+
+def qr_rmsnorm_quantize(x, gamma, eps, qtype, s=None, codes=None, scales=None, h=None, want_h=False, stream=None):
+    """h = bf16(x q gamma) per row of x [rows, k] (bfloat16), q = 1 / sqrt(mean(x^2) + eps) in fp64, and its
+    per-row codes [rows, k] and scales [rows] (as qr_quantize_acts of h, with h diag(1/s) when s is given).
+    gamma: float32 [k]. Returns (codes, scales) or, with want_h / h given, (codes, scales, h)."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous(),
+          "x must be a contiguous bfloat16 [rows, k] CUDA tensor")
+    rows, k = x.shape
+    dev = x.device
+    _need(gamma.is_cuda and gamma.dtype == torch.float32 and gamma.numel() == k and gamma.is_contiguous(),
+          "gamma must be a contiguous float32 [k] CUDA tensor")
+    if codes is None:
+        codes = torch.empty((rows, k), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if h is None and want_h:
+        h = torch.empty((rows, k), dtype=torch.bfloat16, device=dev)
+    if s is not None:
+        _need(s.is_cuda and s.dtype == torch.float32 and s.numel() == k and s.is_contiguous(), "s must be float32 [k]")
+    _need(codes.dtype == torch.uint8 and tuple(codes.shape) == (rows, k) and codes.is_contiguous(), "bad codes")
+    _need(scales.dtype == torch.float32 and scales.numel() == rows, "bad scales")
+    if h is not None:
+        _need(h.dtype == torch.bfloat16 and tuple(h.shape) == (rows, k) and h.is_contiguous(), "bad h")
+    _check(lib().qr_rmsnorm_quantize(_ptr(x), rows, k, _ptr(gamma), float(eps), _ptr(s), int(qtype), _ptr(codes),
+                                     _ptr(scales), _ptr(h), _stream(stream)))
     return (codes, scales, h) if h is not None else (codes, scales)
 
 

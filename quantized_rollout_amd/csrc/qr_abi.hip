@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "qr_internal.hpp"
@@ -464,6 +465,28 @@ qr_status qr_moe_route(const float *logits, int64_t num_tokens, int64_t num_expe
                                               topk_weight, expert_offsets, row_ids, row_weights, pair_rows,
                                               static_cast<hipStream_t>(stream));
     return hip_status(e, "route launch");
+}
+
+qr_status qr_rmsnorm_quantize(const void *x, int64_t rows, int64_t k, const float *gamma, float eps, const float *s,
+                              qr_qtype q, void *h_codes, float *h_scales, void *h, void *stream) {
+    qr_status st;
+    if ((st = check_q(q)) != QR_OK) return st;
+    if (rows < 0) return fail(QR_ERR_ARG, "negative row count %lld", (long long)rows);
+    if (rows > kMaxRows) return fail(QR_ERR_UNSUPPORTED, "row count %lld too large", (long long)rows);
+    if ((st = check_k(k)) != QR_OK) return st;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QR_ERR_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
+    if (rows == 0) return ok();
+    if (x == nullptr || gamma == nullptr || h_codes == nullptr || h_scales == nullptr)
+        return fail(QR_ERR_ARG, "null pointer");
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(h_codes, 16) || (h != nullptr && !aligned(h, 16)))
+        return fail(QR_ERR_ALIGN, "x, gamma, h_codes and h must be 16-byte aligned");
+    if (!aligned(h_scales, 4) || (s != nullptr && !aligned(s, 4)))
+        return fail(QR_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+    if (inject_launch()) return injected("rmsnorm launch");
+    const hipError_t e = qr::launch_rmsnorm_quant(static_cast<const uint16_t *>(x), rows, k, gamma, eps, s, (int)q,
+                                                  static_cast<uint8_t *>(h_codes), h_scales,
+                                                  static_cast<uint16_t *>(h), static_cast<hipStream_t>(stream));
+    return hip_status(e, "rmsnorm launch");
 }
 
 qr_status qr_silu_mul_quantize(const void *y_gu, int64_t rows, int64_t inter, const float *s, qr_qtype q,

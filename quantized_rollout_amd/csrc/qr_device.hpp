@@ -29,6 +29,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// double -> bfloat16 bits with one rounding (nearest even). The conversion to fp32 is made round-to-odd
+// (truncate, then set the last bit when inexact); rounding that 24-bit value to nearest even at 8 bits then
+// equals the direct rounding because 24 >= 8 + 2 (S. Boldo, G. Melquiond, "Emulation of FMA and correctly
+// rounded sums: proved algorithms using rounding to odd", IEEE Trans. Computers 57(4), 2008).
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+    float f = (float)d;
+    if ((double)f != d) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(d)) u -= 1u;  // the neighbour toward zero (sign and magnitude bits)
+        f = __uint_as_float(u | 1u);
+    }
+    return f32_to_bf16(f);
+}
+
 // ---------------------------------------------------------------------------------------------------------
 // Correctly rounded w / S for a whole row with one reciprocal.
 //
@@ -107,6 +121,12 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;

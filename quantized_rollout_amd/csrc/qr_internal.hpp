@@ -14,6 +14,10 @@ enum SMode { kSNone = 0, kSMul = 1, kSMulRecip = 2 };
 // and stores of the codes (weights, read and written once); activations keep their codes cached for the linear.
 hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int s_mode,
                                 int qtype, uint8_t *codes, float *scales, hipStream_t stream, bool streaming = false);
+// The RMSNorm producer of a linear's quantized input: bf16 x [rows, k] (k % 16 == 0), fp32 gamma [k].
+hipError_t launch_rmsnorm_quant(const uint16_t *x, int64_t rows, int64_t k, const float *gamma, float eps,
+                                const float *s, int qtype, uint8_t *codes, float *scales, uint16_t *h_out,
+                                hipStream_t stream);
 // the weight quantizer with the changed-code triple of every row against the previous publish (which may be
 // the output itself), then out3 = the triples' sums
 hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int qtype,

@@ -18,23 +18,6 @@
 namespace qr {
 namespace {
 
-// ---------------------------------------------------------------------------------------------------------
-// fp64 helpers
-// ---------------------------------------------------------------------------------------------------------
-// double -> bfloat16 bits with one rounding (nearest even). The conversion to fp32 is made round-to-odd
-// (truncate, then set the last bit when inexact); rounding that 24-bit value to nearest even at 8 bits then
-// equals the direct rounding because 24 >= 8 + 2 (S. Boldo, G. Melquiond, "Emulation of FMA and correctly
-// rounded sums: proved algorithms using rounding to odd", IEEE Trans. Computers 57(4), 2008).
-__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
-    float f = (float)d;
-    if ((double)f != d) {
-        uint32_t u = __float_as_uint(f);
-        if (fabs((double)f) > fabs(d)) u -= 1u;  // the neighbour toward zero (sign and magnitude bits)
-        f = __uint_as_float(u | 1u);
-    }
-    return f32_to_bf16(f);
-}
-
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {

@@ -255,6 +255,164 @@ __global__ __launch_bounds__(1024) void sum_row_counts_kernel(const int32_t *__r
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// RMSNorm producer of a linear's quantized input: h = bf16(x q gamma) per row, q = 1 / sqrt(mean(x^2) + eps)
+// (0 for a zero radicand), in fp64 and rounded once, then the token-wise quantizer of h (h diag(1/s) with s).
+// The same teams as the quantizer: the x chunks held in registers are replaced by their h chunks after the
+// sum of squares, so the row is read from HBM once; chunks past the register budget are re-read (from L2) and
+// their h recomputed, bit for bit the same. The squares of bfloat16 values are exact in fp64; their sum is
+// taken per lane, then over the wavefront and the team in a fixed order.
+// ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint4 rms_chunk(const uint4 &xc, const float *__restrict__ gamma, int64_t c, double q) {
+    const float4 g0 = *reinterpret_cast<const float4 *>(gamma + 8 * c);
+    const float4 g1 = *reinterpret_cast<const float4 *>(gamma + 8 * c + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const uint32_t p[4] = {xc.x, xc.y, xc.z, xc.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = f64_to_bf16((double)bf16_lo(p[i]) * q * (double)g[2 * i]);
+        const uint32_t hi = f64_to_bf16((double)bf16_hi(p[i]) * q * (double)g[2 * i + 1]);
+        o[i] = lo | (hi << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ double sum_sq_chunk(const uint4 &xc) {
+    const uint32_t p[4] = {xc.x, xc.y, xc.z, xc.w};
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double lo = bf16_lo(p[i]), hi = bf16_hi(p[i]);
+        a += lo * lo;
+        a += hi * hi;
+    }
+    return a;
+}
+
+template <int QT, int SMODE, int THREADS, int RPB>
+__global__ __launch_bounds__(THREADS * RPB) void rmsnorm_quant_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                                      int64_t k, const float *__restrict__ gamma,
+                                                                      float eps, const float *__restrict__ s,
+                                                                      uint8_t *__restrict__ codes,
+                                                                      float *__restrict__ scales,
+                                                                      uint16_t *__restrict__ h_out) {
+    static_assert(RPB == 1 || THREADS == 64, "several rows per workgroup only with one-wavefront rows");
+    constexpr int E = 8, kC = kCMax;
+    constexpr float qmax = QMax<QT>::value;
+    const int64_t row = (int64_t)blockIdx.x * RPB + (RPB > 1 ? (int)(threadIdx.x >> 6) : 0);
+    if (row >= rows) return;  // whole wavefronts only (RPB > 1 implies one wavefront per row)
+    const int t = RPB > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    const int64_t nch = k / E;
+    const uint4 *__restrict__ src = reinterpret_cast<const uint4 *>(x + row * k);
+    uint4 *__restrict__ hdst = h_out != nullptr ? reinterpret_cast<uint4 *>(h_out + row * k) : nullptr;
+
+    uint4 keep[kC];
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+        const int64_t c = t + (int64_t)i * THREADS;
+        if (c < nch) {
+            keep[i] = src[c];
+            ss += sum_sq_chunk(keep[i]);
+        }
+    }
+    for (int64_t c = t + (int64_t)kC * THREADS; c < nch; c += THREADS) ss += sum_sq_chunk(src[c]);
+    ss = wave_sum_f64(ss);
+    if constexpr (THREADS > 64) {
+        __shared__ double red_ss[THREADS / 64];
+        if ((t & 63) == 0) red_ss[t >> 6] = ss;
+        __syncthreads();
+        ss = red_ss[0];
+#pragma unroll
+        for (int i = 1; i < THREADS / 64; ++i) ss += red_ss[i];
+    }
+    const double d = ss / (double)k + (double)eps;
+    const double q = d > 0.0 ? 1.0 / sqrt(d) : 0.0;
+
+    float amax = 0.0f;
+    auto absmax_of = [&](const uint4 &hc, int64_t c) {
+        float w[E];
+        expand_chunk<true, SMODE>(hc, s, c * E, w);
+#pragma unroll
+        for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(w[j]));
+    };
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+        const int64_t c = t + (int64_t)i * THREADS;
+        if (c < nch) {
+            keep[i] = rms_chunk(keep[i], gamma, c, q);
+            if (hdst != nullptr) hdst[c] = keep[i];
+            absmax_of(keep[i], c);
+        }
+    }
+    for (int64_t c = t + (int64_t)kC * THREADS; c < nch; c += THREADS) {
+        const uint4 hc = rms_chunk(src[c], gamma, c, q);
+        if (hdst != nullptr) hdst[c] = hc;
+        absmax_of(hc, c);
+    }
+    amax = wave_max(amax);
+    if constexpr (THREADS > 64) {
+        __shared__ float red[THREADS / 64];
+        if ((t & 63) == 0) red[t >> 6] = amax;
+        __syncthreads();
+        amax = red[0];
+#pragma unroll
+        for (int i = 1; i < THREADS / 64; ++i) amax = fmaxf(amax, red[i]);
+    }
+
+    float S = amax / qmax;  // IEEE division
+    if (!(S > 0.0f)) S = 1.0f;  // all-zero row, or a scale that underflows to zero
+    const float r = 1.0f / S;
+    const bool fast = S >= 0x1p-90f;
+    if (t == 0) scales[row] = S;
+
+    uint8_t *dst = codes + row * k;
+    auto emit = [&](const uint4 &hc, int64_t c) {
+        float w[E];
+        expand_chunk<true, SMODE>(hc, s, c * E, w);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const float v = fast ? div_by_scale(w[j], S, r) : w[j] / S;
+            w[j] = fminf(fmaxf(v, -qmax), qmax);
+        }
+        uint2 o;
+        o.x = encode_code4<QT>(w);
+        o.y = encode_code4<QT>(w + 4);
+        *reinterpret_cast<uint2 *>(dst + c * 8) = o;
+    };
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+        const int64_t c = t + (int64_t)i * THREADS;
+        if (c < nch) emit(keep[i], c);
+    }
+    for (int64_t c = t + (int64_t)kC * THREADS; c < nch; c += THREADS) emit(rms_chunk(src[c], gamma, c, q), c);
+}
+
+// Lanes per row. Weights (many rows, streamed once): the smallest power of two of at least half the row's
+// chunks (64..1024), halved while the launch exceeds 2^20 threads. Activations (few to a few thousand rows whose
+// latency the next linear waits for): one chunk per lane (up to 1024 lanes), halved while rows x lanes exceeds
+// 2^18. Both at least what holds every chunk in kC registers per lane; a row of one wavefront shares its
+// workgroup with three others. Measured on MI355X (graph replay, bf16 to FP8; quantizer alone / with RMSNorm):
+// K = 3584 at 1 and 16 rows 2.6 / 3.8 us with 512 lanes against 2.9 / 4.2 us with 256, at 2048 rows 5.6 / 10.5
+// us with 128 against 6.0 / 11.8 with 256; K = 1536 at 2048 rows 4.0 / 6.6 us with 128; K = 18944 at 512 and
+// 2048 rows 6.9 / 13.5 and 22.6 / 40.5 us with 512 lanes against 7.6 / 16.1 and 23.2 / 44.4 with 1024.
+int team_lanes(int64_t rows, int64_t nch, int kC, bool acts) {
+    int lanes = 64;
+    if (acts) {
+        while (lanes < 1024 && lanes < nch) lanes *= 2;
+        while (lanes > 64 && rows * lanes > ((int64_t)1 << 18)) lanes /= 2;
+    } else {
+        while (lanes < 1024 && 2 * lanes < nch) lanes *= 2;
+        while (lanes > 64 && rows * lanes > ((int64_t)1 << 20)) lanes /= 2;
+    }
+    const int minimum = nch <= 64 * kC ? 64 : nch <= 128 * kC ? 128 : nch <= 256 * kC ? 256 : nch <= 512 * kC ? 512 : 1024;
+    if (lanes < minimum) lanes = minimum;  // the register budget: at most kC chunks per lane held
+    const int forced = env_int("QR_QUANT_THREADS", 0);  // tuning sweeps
+    if (forced == 64 || forced == 128 || forced == 256 || forced == 512 || forced == 1024) lanes = forced;
+    return lanes;
+}
+
 struct DiffArgs {
     const uint8_t *prev_codes;
     const float *prev_scales;
@@ -271,19 +429,7 @@ hipError_t launch_t(const void *in, int64_t rows, int64_t k, const float *s, uin
 #define QR_QROWS(T, R, G)                                                                                      \
     hipLaunchKernelGGL((quantize_rows_kernel<BF16, QT, SMODE, T, R, DIFF, NT>), G, dim3(T * R), 0, stream, in, rows, \
                        k, s, codes, scales, d.prev_codes, d.prev_scales, d.row_counts)
-    // Lanes per row: the smallest power of two of at least half the row's chunks (64..1024), halved while the
-    // launch exceeds 2^20 threads; a row of one wavefront shares its workgroup with three others. Rows are
-    // latency-bound when few (a lane encodes its chunks one after the other), so few long rows (activations) get
-    // wide teams and many rows (weights) one wavefront each. Measured on MI355X (bf16 to FP8, graph replay):
-    // K = 3584 at 1..512 rows 7.1 -> 4.0-4.9 us with 512 lanes, at 2048 rows 11.2 -> 9.8 us with 256; K = 18944
-    // at 1..128 rows 6.2-7.6 -> 5.7-6.8 us with 1024, at 2048 rows 32.9 -> 31.2 us with 512.
-    int lanes = 64;
-    while (lanes < 1024 && 2 * lanes < nch) lanes *= 2;
-    while (lanes > 64 && rows * lanes > ((int64_t)1 << 20)) lanes /= 2;
-    const int minimum = nch <= 64 * kC ? 64 : nch <= 128 * kC ? 128 : nch <= 256 * kC ? 256 : nch <= 512 * kC ? 512 : 1024;
-    if (lanes < minimum) lanes = minimum;  // the register budget: at most kC chunks per lane held
-    const int forced = env_int("QR_QUANT_THREADS", 0);  // tuning sweeps
-    if (forced == 64 || forced == 128 || forced == 256 || forced == 512 || forced == 1024) lanes = forced;
+    const int lanes = team_lanes(rows, nch, kC, !NT && !DIFF);  // weights stream (NT), activations do not
     if (lanes == 64) {
         constexpr int kRows = 4;
         QR_QROWS(64, kRows, dim3((unsigned)((rows + kRows - 1) / kRows)));
@@ -332,6 +478,38 @@ hipError_t launch_quantize_rows(const void *in, bool in_bf16, int64_t rows, int6
                                 int qtype, uint8_t *codes, float *scales, hipStream_t stream, bool streaming) {
     return launch_q<false>(in, in_bf16, rows, k, s, s_mode, streaming, qtype, codes, scales,
                            DiffArgs{nullptr, nullptr, nullptr}, stream);
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t *x, int64_t rows, int64_t k, const float *gamma, float eps,
+                                const float *s, int qtype, uint8_t *codes, float *scales, uint16_t *h_out,
+                                hipStream_t stream) {
+    const int64_t nch = k / 8;
+    const int lanes = team_lanes(rows, nch, kCMax, true);
+    const dim3 grid((unsigned)rows);
+#define QR_RMS(QT, SM, T, R, G)                                                                                  \
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<QT, SM, T, R>), G, dim3(T * R), 0, stream, x, rows, k, gamma, eps, s, \
+                       codes, scales, h_out)
+#define QR_RMS_T(QT, SM)                                                                                         \
+    do {                                                                                                         \
+        if (lanes == 64)                                                                                         \
+            QR_RMS(QT, SM, 64, 4, dim3((unsigned)((rows + 3) / 4)));                                             \
+        else if (lanes == 128)                                                                                   \
+            QR_RMS(QT, SM, 128, 1, grid);                                                                        \
+        else if (lanes == 256)                                                                                   \
+            QR_RMS(QT, SM, 256, 1, grid);                                                                        \
+        else if (lanes == 512)                                                                                   \
+            QR_RMS(QT, SM, 512, 1, grid);                                                                        \
+        else                                                                                                     \
+            QR_RMS(QT, SM, 1024, 1, grid);                                                                       \
+    } while (0)
+    if (qtype == kInt8) {
+        if (s != nullptr) QR_RMS_T(kInt8, kSMulRecip); else QR_RMS_T(kInt8, kSNone);
+    } else {
+        if (s != nullptr) QR_RMS_T(kFp8, kSMulRecip); else QR_RMS_T(kFp8, kSNone);
+    }
+#undef QR_RMS_T
+#undef QR_RMS
+    return hipGetLastError();
 }
 
 hipError_t launch_requantize(const void *in, bool in_bf16, int64_t rows, int64_t k, const float *s, int qtype,

@@ -10,7 +10,10 @@ this module is the only thing they share. Recipe, per workload:
   * draw order: every weight matrix in the listed order, then the weight updates, then the invariant
     scales, then per linear the activations followed by their 4 outlier input channels
     (``rng.choice(K, 4, replace=False)``, those columns multiplied by 20 in fp32), then router logits;
-  * activations are drawn once at the largest batch; smaller batches take row prefixes.
+  * activations are drawn once at the largest batch; smaller batches take row prefixes;
+  * the RMSNorm producer's inputs (``make_norm_inputs``): hidden states N(0, 1) with the 4 outlier channels, each
+    row multiplied by 10^u, u ~ U(-1, 2) (the residual stream's token-to-token magnitude spread), then the norm
+    weight gamma = |N(1, 0.3)| rounded to bfloat16 (held as fp32), then the invariant scale s ~ U(0.5, 2).
 
 Shapes follow the pages' models: a 1.5B-class dense decoder layer (QuRL section 5.1, the DeepScaleR
 model), a 7B-class layer (QuRL sections 5.1 and 5.2) and the Qwen3-30B-A3B mixture-of-experts layer (QaRL
@@ -212,3 +215,20 @@ def make_moe(wl: MoEWorkload = QWEN3_MOE, experts: Optional[int] = None) -> MoEI
     h = f32_to_bf16_bits(_activations(rng, wl.tokens * wl.top_k, wl.inter))
     offsets, row_ids = route_top_k(logits, wl.top_k)
     return MoEInputs(wl, wgu, wd, x, logits, h, offsets, row_ids)
+
+
+@dataclass
+class NormInputs:
+    x: np.ndarray  # hidden states [rows, k], bfloat16 bits
+    gamma: np.ndarray  # norm weight [k], fp32 holding bfloat16 values
+    s: np.ndarray  # invariant scale [k], fp32
+
+
+def make_norm_inputs(rows: int, k: int, seed: int = 0) -> NormInputs:
+    """Inputs of the RMSNorm producer of a linear's quantized input, at the hidden size k of the pages' models."""
+    rng = np.random.default_rng(seed)
+    x = _activations(rng, rows, k)
+    x *= (10.0 ** rng.uniform(-1.0, 2.0, (rows, 1))).astype(np.float32)
+    gamma = bf16_bits_to_f32(f32_to_bf16_bits(np.abs(1.0 + 0.3 * rng.standard_normal(k)).astype(np.float32)))
+    s = rng.uniform(0.5, 2.0, k).astype(np.float32)
+    return NormInputs(f32_to_bf16_bits(x), gamma, s)

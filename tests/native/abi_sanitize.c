@@ -77,6 +77,12 @@ static void validation(void) {
     CHECK(qr_moe_route(NULL, 64, 16, 4, NULL, NULL, (int32_t *)PTR(12), NULL, NULL, NULL, NULL) != QR_OK);
     CHECK(qr_silu_mul_quantize(x, 32, 250, NULL, QR_INT8, y, (float *)xs, NULL, NULL) != QR_OK);
     CHECK(qr_moe_combine(x, 256, 512, NULL, (int32_t *)PTR(13), 64, 4, y, NULL) == QR_ERR_ARG);
+    CHECK(qr_rmsnorm_quantize(x, 16, 3584, (const float *)xs, -1.0f, NULL, QR_FP8_E4M3, y, (float *)xs, NULL, NULL) ==
+          QR_ERR_ARG);
+    CHECK(qr_rmsnorm_quantize(x, 16, 3580, (const float *)xs, 1e-6f, NULL, QR_INT8, y, (float *)xs, NULL, NULL) ==
+          QR_ERR_UNSUPPORTED);
+    CHECK(qr_rmsnorm_quantize(x, 16, 3584, (const float *)xs, 1e-6f, NULL, (qr_qtype)7, y, (float *)xs, NULL, NULL) ==
+          QR_ERR_ARG);
     /* sizes: no overflow in the workspace arithmetic over large shapes */
     CHECK(qr_workspace_bytes(QR_INT8, 1, 1536, 8960, 1) < BIG);
     CHECK(qr_workspace_bytes(QR_FP8_E4M3, 65536, 37888, 3584, 1) > 0 || 1);
@@ -113,6 +119,8 @@ static void injected_launches(void) {
                                 (int32_t *)PTR(11), (float *)PTR(12), (int32_t *)PTR(13), NULL)));
     CHECK(injected(qr_silu_mul_quantize(x, 32, 256, NULL, QR_INT8, y, (float *)xs, NULL, NULL)));
     CHECK(injected(qr_moe_combine(x, 256, 512, (const float *)xs, (const int32_t *)PTR(13), 64, 4, y, NULL)));
+    CHECK(injected(qr_rmsnorm_quantize(x, 16, 3584, (const float *)xs, 1e-6f, NULL, QR_INT8, y, (float *)xs, NULL,
+                                       NULL)));
     /* validation still comes first */
     CHECK(qr_w8a8_linear(QR_INT8, 16, 1536, 1530, x, xs, w, wsc, y, QR_BF16, NULL, ws, BIG, NULL) ==
           QR_ERR_UNSUPPORTED);

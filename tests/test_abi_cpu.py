@@ -300,3 +300,23 @@ def test_moe_glue_validation():
     assert combine(T=0, out=NULL) == B.QR_OK
     assert combine(out=NULL) == B.QR_ERR_ARG
     assert combine(out=MIS) == B.QR_ERR_ALIGN and combine(yd=MIS) == B.QR_ERR_ALIGN
+
+
+def test_rmsnorm_quantize_validation():
+    L = B.lib()
+
+    def rms(rows=16, k=3584, q=1, x=P, g=P2, eps=1e-6, s=NULL, codes=P, sc=P, h=NULL):
+        return L.qr_rmsnorm_quantize(x, rows, k, g, eps, s, q, codes, sc, h, S0)
+
+    assert rms(k=3576) == B.QR_ERR_UNSUPPORTED and "multiple of 16" in _err()
+    assert rms(k=0) == B.QR_ERR_ARG
+    assert rms(q=2) == B.QR_ERR_ARG
+    assert rms(rows=-1) == B.QR_ERR_ARG
+    assert rms(eps=-1e-6) == B.QR_ERR_ARG and "eps" in _err()
+    assert rms(eps=float("nan")) == B.QR_ERR_ARG and rms(eps=float("inf")) == B.QR_ERR_ARG
+    assert rms(rows=0, x=NULL, g=NULL) == B.QR_OK  # nothing to do
+    assert rms(x=NULL) == B.QR_ERR_ARG and rms(g=NULL) == B.QR_ERR_ARG and rms(sc=NULL) == B.QR_ERR_ARG
+    assert rms(x=MIS) == B.QR_ERR_ALIGN and rms(g=MIS) == B.QR_ERR_ALIGN and rms(h=MIS) == B.QR_ERR_ALIGN
+    assert rms(codes=MIS) == B.QR_ERR_ALIGN
+    assert rms(sc=ctypes.c_void_p(0x7F0000000002)) == B.QR_ERR_ALIGN
+    assert rms(s=ctypes.c_void_p(0x7F0000000002)) == B.QR_ERR_ALIGN
