@@ -644,7 +644,7 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
     // Chosen at m = 1 from measurements on MI355X (graph replay, weights past the caches):
     //  - codes in: 8 parts below 512 tiles with k <= 8960 (1.5B down 8.8 -> 5.8 us, o 4.3 -> 3.4, 7B qkv
     //    7.6 -> 5.8, o 6.0 -> 5.2), 2 or 4 on many tiles (1.5B gate/up 8.2 -> 7.9 with k < 2048, 7B gate/up
-    //    26.8 -> 24.5), none for the 7B down (k = 18944: slower with any split);
+    //    26.8 -> 24.5); one wavefront per workgroup with 8 parts on 128..511 tiles (below);
     //  - activation quantization inside the kernel (every workgroup repeats it): 2 parts below 256 tiles (1.5B
     //    qkv 6.4 -> 5.6 us, o 6.3 -> 5.5, down 11.4 -> 9.3; 7B o 9.2 -> 8.2), none otherwise.
     // QR_GEMV_KSUB forces S; other GEMV overrides turn the automatic choice off.
@@ -657,10 +657,19 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
         if (fk == 2 || fk == 4 || fk == 8) {
             ks = fk;
         } else if (fk == 0 && !overrides && m == 1) {
-            if (fused_quant)
+            if (fused_quant) {
                 ks = p.n_tiles < 256 ? 2 : 1;
-            else if (k <= 8960)
+            } else if (p.n_tiles >= 128 && p.n_tiles < 512) {
+                // 8 parts with one wavefront per workgroup on 256-byte slices (measured on MI355X, the same box:
+                // 7B down, k = 18944, 16.1 -> 14.7 us, qkv 6.07 -> 5.87, o 5.7 -> 5.44, the layer at m = 1 with
+                // a2 65.6 -> 64.6 us; 1.5B qkv 4.0 -> 3.7; the fewest-tile 1.5B down is slower this way, and the
+                // 7B gate/up with 8 parts on one wavefront was not faster on every box)
+                ks = 8;
+                u = 4;
+                wave_cap = 1;
+            } else if (k <= 8960) {
                 ks = p.n_tiles < 512 ? 8 : (k >= 2048 ? 4 : 2);
+            }
         } else if (fk == 0 && !overrides && !fused_quant && m > 8 && p.n_tiles < 160 && k <= 8960) {
             // two token blocks of 8 tokens, K in 2 parts: the weights are read twice (the second time mostly
             // from cache), which pays only on the fewest tiles (1.5B o at m = 16: 4.8 -> 4.1 us, down 10.2 ->
