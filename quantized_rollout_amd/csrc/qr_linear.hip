@@ -602,13 +602,16 @@ LinearPlan plan_linear(int qtype, int64_t m, int64_t n, int64_t k, int max_unrol
         const bool few = p.n_tiles < 128;
         if (k >= 1536 && !few) u = 8;
         wave_cap = few ? 8 : 4;
-        // past half a token tile, on very many tiles, two weight tiles per block share each activation slice,
-        // and one wavefront streams all of K for them: no partial sums through LDS, and the most blocks resident
-        // per CU (measured on MI355X: 7B gate/up at m = 16 from 34.4 to 32.3 us with two tiles, then 31.7 ->
-        // 29.0 us and at m = 9 30.9 -> 28.9 us with one wavefront; the 1.5B gate/up, 1120 tiles, is slower with
-        // two tiles)
+        // past half a token tile, on many tiles, one wavefront streams all of K for its block: no partial sums
+        // through LDS, and the most blocks resident per CU; on very many tiles two weight tiles per block also
+        // share each activation slice (measured on MI355X, 7B gate/up, 2368 tiles, at m = 16: 34.4 us with one
+        // tile on four wavefronts, 31.7 with two tiles, 29.0 with two tiles on one wavefront, 29.0-31.5 with one
+        // tile on one wavefront; the 1.5B gate/up, 1120 tiles, at m = 16 with one tile on one wavefront: INT8
+        // 9.2 -> 8.6 us, FP8 10.0 -> 8.4, at m = 9 INT8 8.5 -> 8.2; two tiles are slower there)
         if (m > 8 && p.n_tiles >= 2048 && gemv_variant_waves(1, u, 2) > 0) {
             tb = 2;
+            wave_cap = 1;
+        } else if (m > 8 && p.n_tiles >= 1024) {
             wave_cap = 1;
         }
     } else {
