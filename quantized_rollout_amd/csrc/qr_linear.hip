@@ -733,15 +733,15 @@ LinearPlan plan_linear_bf16(int qtype, int64_t m, int64_t n, int64_t k) {
 bool linear_bf16_fused(const LinearPlan &p, int qtype, int64_t m, int64_t k) {
     // Every workgroup quantizes the token rows itself, so the prologue is repeated per workgroup and only its
     // own latency is hidden by other workgroups. Measured on MI355X (graph replay, weights past the caches,
-    // against the activation quantizer with wide per-row teams and the hardware E4M3 conversion, about 4 us):
-    // at m = 1 it pays on few workgroups (7B FP8 o 9.6 -> 8.9 us, qkv even) but not on the many of the 7B FP8
-    // gate/up (2368: 29.2 -> 31.4 us), nor on the 7B FP8 down (k = 18944, a long row in every workgroup), nor
-    // at m = 2 or 4.
+    // against the activation quantizer, about 3.6 us, followed by the linear on codes): at m = 1 it pays on at
+    // most 256 workgroups (1.5B qkv, 256: 6.3 -> 5.8 us, o, 192: 6.1 -> 5.7), not on the 7B qkv (288: 8.4 against
+    // 9.4 us) and o (448: 7.9 against 8.0), nor on the many of the 7B gate/up (2368), nor on the 7B down
+    // (k = 18944, a long row in every workgroup), nor at m = 2 or 4.
     const int64_t max_m = env_int("QR_FUSE_MAX_M", 1);
     if (qtype == kFp8 && k > env_int("QR_FUSE_MAX_K_FP8", 8192)) return false;
     if (p.kind != 0 || p.m_tiles != 1 || p.splits != 1 || p.unroll != 4 || p.tiles < 1) return false;  // GEMV only
     const int64_t blocks = (p.n_tiles + p.tiles - 1) / p.tiles;
-    return blocks < env_int("QR_FUSE_MAX_BLOCKS", 1024) && m <= std::min<int64_t>(max_m, kFuseRows) &&
+    return blocks <= env_int("QR_FUSE_MAX_BLOCKS", 256) && m <= std::min<int64_t>(max_m, kFuseRows) &&
            gemv_fused_lds_bytes(p, m, k) <= 65536;
 }
 

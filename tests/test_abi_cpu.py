@@ -197,7 +197,8 @@ def test_linear_bf16_validation_and_workspace(monkeypatch):
     for q in (B.QR_INT8, B.QR_FP8_E4M3):
         # m = 1: the activation quantization runs inside the linear, no workspace (FP8: for k <= 8192), on plans
         # of fewer than 1024 workgroups; the 1120 workgroups of n = 17920 quantize into the workspace first
-        assert ws(q, 1, 3584, 3584) == 0
+        assert ws(q, 1, 2048, 1536) == 0  # in-kernel quantization: at most 256 workgroups
+        assert ws(q, 1, 3584, 3584) == 3584 + 256  # 448 workgroups: the quantizer, then the linear
         assert ws(q, 1, 17920, 1536) == 1536 + 256
         assert ws(q, 1, 1536, 8960) == (0 if q == B.QR_INT8 else 8960 + 256)
         # larger batches: the activation codes (m k bytes) and scales (4 m), each rounded up to 256 bytes,

@@ -165,6 +165,7 @@ def test_gemv_k_parts(ks, monkeypatch, capfd):
     the tolerance, at m = 1 up to 16 / ks tokens, with channels not a multiple of the tile, K parts with a partial
     last slice, and the bfloat16-activation entry point (the activation quantization inside the kernel)."""
     monkeypatch.setenv("QR_GEMV_KSUB", str(ks))
+    monkeypatch.setenv("QR_FUSE_MAX_BLOCKS", "1024")  # the in-kernel quantization also on 8 x 96 workgroups
     monkeypatch.setenv("QR_TRACE", "1")
     shapes = [(1, 1536, 8960), (1, 70, 1664), (min(4, 16 // ks), 100, 2048), (16 // ks, 37, 3584), (1, 3, 128 * ks)]
     for i, (m, n, k) in enumerate(shapes):

@@ -72,7 +72,7 @@ def test_linear_bf16_parity(q, with_s, fuse_max, monkeypatch, capfd):
             assert_y_within_bound(host(y), acc_f, xs, ws, bound, what)
             assert_y_close(host(y), y_ref, what)
             err = capfd.readouterr().err
-            # the in-kernel quantization: one token tile, FP8 rows up to k = 8192, fewer than 1024 workgroups
+            # the in-kernel quantization: one token tile, FP8 rows up to k = 8192, at most 256 workgroups
             fused = m <= limit and (q == O.INT8 or k <= 8192) and n < 16384
             assert ("fused=%d" % fused) in err or m > 16, (what, err)
 
