@@ -38,8 +38,8 @@ def test_oracle_under_asan_ubsan(tmp_path):
 
 def test_abi_host_side_under_asan_ubsan(tmp_path):
     """qr_abi.hip and qr_linear.hip (validation, plans, launch set-up) compiled with host sanitizers (the device
-    code is compiled as usual), linked with the other objects of the in-tree build into a library the driver
-    program loads."""
+    code is compiled as usual), linked with the other objects of the in-tree build into a library that the C
+    test program tests/native/abi_sanitize.c loads."""
     from quantized_rollout_amd import build as B
     objdir = os.path.join(ROOT, "quantized_rollout_amd", "_build")
     rest = [os.path.join(objdir, os.path.basename(s) + ".o") for s in B.sources()
