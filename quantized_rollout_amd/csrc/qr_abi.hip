@@ -142,10 +142,11 @@ qr_status run_linear(const qr::LinearPlan &p, qr_qtype q, int64_t m, int64_t n, 
                      void *acc_out, void *workspace, void *stream) {
     if (qr::trace_enabled())
         fprintf(stderr, "[qr] linear q=%d m=%lld n=%lld k=%lld kind=%d mt=%d waves=%d unroll=%d tiles=%d pf=%d ksub=%d gemm=%d "
-                "bm=%d splits=%d dp=%d ws=%zu bn=%d\n",
+                "bm=%d splits=%d dp=%d ws=%zu bn=%d band=%lld\n",
                 (int)q, (long long)m, (long long)n, (long long)k, p.kind, p.m_tiles, p.waves, p.unroll, p.tiles,
                 p.prefetch ? 1 : 0, p.kind == 0 ? p.ksub : 1, p.gemm.tile, p.gemm.bm, p.kind == 0 ? p.splits : p.gemm.splits,
-                p.kind == 0 ? 0 : p.gemm.dp_tiles, p.ws_bytes, p.gemm.bn);
+                p.kind == 0 ? 0 : p.gemm.dp_tiles, p.ws_bytes, p.gemm.bn,
+                p.kind == 1 && p.gemm.band ? (long long)p.gemm.band_n0 : -1LL);
     if (inject_launch()) return injected("linear launch");
     const hipError_t e = qr::launch_linear(p, (int)q, m, n, k, static_cast<const uint8_t *>(x_codes), x_scales,
                                            static_cast<const uint8_t *>(w_codes), w_scales, y, y_type == QR_BF16,

@@ -550,6 +550,7 @@ __global__ __launch_bounds__((Ring<BM, BN>::kThreads), 1) void gemm_ring_kernel(
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kWideK = 128;     // K bytes per stage
 constexpr int kWideN = 256;     // weight rows (output channels) per tile
+constexpr int kWideBandN = 160; // output channels per tile of the band after whole rounds of 256-wide tiles
 constexpr int kWideM = 256;     // activation rows per tile
 constexpr int kWideThreads = 256;
 constexpr int kWideBuf = (kWideM + kWideN) * kWideK;  // bytes per LDS stage buffer (64 KiB)
@@ -558,13 +559,22 @@ constexpr int kWideChunks = kWideM * kWideK / 16 / kWideThreads;  // 16-byte pie
 
 __device__ __forceinline__ int wide_swizzle(int r) { return (r >> 1) & 7; }
 
-template <int QT>
+template <int QT, int BN>
 __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     int64_t m, int64_t n, int64_t k, const uint8_t *__restrict__ xq, const float *__restrict__ xs,
     const uint8_t *__restrict__ wq, const float *__restrict__ ws, void *__restrict__ y, int y_bf16,
     void *__restrict__ acc_out, int tiles_m, int tiles_n, int splits, int stages_per_split,
-    void *__restrict__ partial, int dp_tiles) {
+    void *__restrict__ partial, int dp_tiles, int64_t n_base) {
     typedef typename Acc32<QT>::type acc_t;
+    // BN = 256: 2 x 2 wavefronts of 128 x 128 outputs; BN = 160 (a band of columns after whole rounds of 256-wide
+    // tiles): 4 x 1 wavefronts of 64 x 160
+    constexpr int WM = BN == kWideN ? 2 : 4, WN = 4 / WM;
+    constexpr int WR = kWideM / WM, WC = BN / WN;               // outputs per wavefront
+    constexpr int IA = WR / 32, JB = WC / 32;                   // 32 x 32 fragments per wavefront
+    constexpr int CB = BN * kWideK / 16 / kWideThreads;         // weight staging pieces per thread
+    constexpr int NS = kWideChunks + CB, NR = 2 * (IA + JB), NM = IA * JB;
+    constexpr int NX = NS > NR ? (NS > NM ? NS : NM) : (NR > NM ? NR : NM);
+    static_assert(WC % 32 == 0 && (BN * kWideK) % (16 * kWideThreads) == 0 && BN <= kWideN, "tile shape");
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];  // two stage buffers of kWideBuf bytes
 
     // work item: the same order as the ring kernel (each XCD a contiguous run; whole-K tiles first)
@@ -595,14 +605,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
         }
     }
     const int64_t m0 = (int64_t)(tile % tiles_m) * kWideM;
-    const int64_t n0 = (int64_t)(tile / tiles_m) * kWideN;
+    const int64_t n0 = n_base + (int64_t)(tile / tiles_m) * BN;
     const int64_t all_stages = (k + kWideK - 1) / kWideK;
     const int64_t st0 = to_partial ? (int64_t)split * stages_per_split : 0;
     const int64_t stages = to_partial ? std::min<int64_t>(stages_per_split, all_stages - st0) : all_stages;
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     // LDS: stage buffer b holds its activation rows at b * kWideHalf and its weight rows at kWideBuf + b * kWideHalf,
     // so that every access below is a register plus an immediate offset, and moving to the other buffer flips one
@@ -617,13 +627,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     const int lds0 = srow * kWideK + 16 * (spiece ^ wide_swizzle(srow));
     const int64_t rows_a = m - m0 - srow, rows_b = n - n0 - srow;  // piece i is in range while 32 i < rows
     // byte offsets of the pieces at K = 0, or kOutOfRange (past every operand) for rows outside the operand
-    uint32_t va[kWideChunks], vb[kWideChunks];
+    uint32_t va[kWideChunks], vb[CB];
 #pragma unroll
-    for (int i = 0; i < kWideChunks; ++i) {
+    for (int i = 0; i < kWideChunks; ++i)
         va[i] = 32 * i < rows_a ? (uint32_t)((m0 + srow + 32 * i) * k + 16 * spiece) : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
         vb[i] = 32 * i < rows_b ? (uint32_t)((n0 + srow + 32 * i) * k + 16 * spiece) : kOutOfRange;
-    }
-    v4i ra[kWideChunks], rb[kWideChunks];
+    v4i ra[kWideChunks], rb[CB];
     // staging piece x of global stage gst (x < 8: activations, else weights). K is a whole number of stages here,
     // so the stage's K offset goes in the scalar offset, with no per-lane arithmetic; a row outside the operand
     // stays out of range with or without it.
@@ -644,11 +655,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
             *reinterpret_cast<v4i *>(lds + wb + 4096 * (x - 8)) = rb[x - 8];
     };
 
-    acc_t acc[4][4];
+    acc_t acc[IA][JB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{};
+        for (int j = 0; j < JB; ++j) acc[i][j] = acc_t{};
 
     // one 64-byte step u of a stage: 16 fragment reads (lane row (l & 31), half h = l >> 5), 16 MFMA tiles; both
     // split into single instructions so that the pipeline below can interleave them with other memory operations
@@ -656,25 +667,25 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     const int q0 = QT == kInt8 ? h : 2 * h, q1 = QT == kInt8 ? 2 + h : 2 * h + 1;
     const int swz = wide_swizzle(fr);  // rows wm 128 + 32 i + fr and 128 wn + 32 j + fr share it
     // the lane's fragment addresses in buffer 0 for step u and piece parity p (the first or second 16 bytes)
-    auto frag_a = [&](int u, int p) { return (wm * 128 + fr) * kWideK + 16 * ((4 * u + (p ? q1 : q0)) ^ swz); };
+    auto frag_a = [&](int u, int p) { return (wm * WR + fr) * kWideK + 16 * ((4 * u + (p ? q1 : q0)) ^ swz); };
     auto frag_b = [&](int u, int p) {
-        return kWideBuf + (wn * 128 + fr) * kWideK + 16 * ((4 * u + (p ? q1 : q0)) ^ swz);
+        return kWideBuf + (wn * WC + fr) * kWideK + 16 * ((4 * u + (p ? q1 : q0)) ^ swz);
     };
     struct Frags {
-        uint4 a[4][2], b[4][2];
+        uint4 a[IA][2], b[JB][2];
     };
     // read x (x = 0..15) at fragment addresses fa, fb: A fragment x / 2 piece x % 2 for x < 8, then B fragment
     // (x - 8) / 2 piece x % 2
     auto read_one = [&](const int (&fa)[2], const int (&fb)[2], Frags &f, auto X) {
         constexpr int x = decltype(X)::value;
-        if constexpr (x < 8)
+        if constexpr (x < 2 * IA)
             f.a[x / 2][x & 1] = *reinterpret_cast<const uint4 *>(lds + fa[x & 1] + (x / 2) * 4096);
         else
-            f.b[(x - 8) / 2][x & 1] = *reinterpret_cast<const uint4 *>(lds + fb[x & 1] + ((x - 8) / 2) * 4096);
+            f.b[(x - 2 * IA) / 2][x & 1] = *reinterpret_cast<const uint4 *>(lds + fb[x & 1] + ((x - 2 * IA) / 2) * 4096);
     };
     // MFMA tile x of a step: fragments (x / 4, x % 4)
     auto mfma_one = [&](const Frags &f, auto X) {
-        constexpr int x = decltype(X)::value, i = x / 4, j = x % 4;
+        constexpr int x = decltype(X)::value, i = x / JB, j = x % JB;
         if constexpr (QT == kInt8) {
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(f.a[i][0]), v4(f.b[j][0]), acc[i][j], 0, 0, 0);
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4(f.a[i][1]), v4(f.b[j][1]), acc[i][j], 0, 0, 0);
@@ -719,28 +730,30 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     auto run_stage = [&](int64_t s, auto store_c, auto load_c, auto next_c) {
         constexpr bool kStore = decltype(store_c)::value, kLoad = decltype(load_c)::value,
                        kNext = decltype(next_c)::value;
-        unroll<16>([&](auto X) {
-            mfma_one(f0, X);
-            read_one(c1a, c1b, f1, X);
-            if constexpr (kStore) store_one(wa, wb, X);
-            if constexpr (kLoad) load_one(st0 + s + 2, X);
+        unroll<NX>([&](auto X) {
+            constexpr int x = decltype(X)::value;
+            if constexpr (x < NM) mfma_one(f0, X);
+            if constexpr (x < NR) read_one(c1a, c1b, f1, X);
+            if constexpr (kStore && x < NS) store_one(wa, wb, X);
+            if constexpr (kLoad && x < NS) load_one(st0 + s + 2, X);
             __builtin_amdgcn_sched_barrier(0);
         });
         __syncthreads();
-        unroll<16>([&](auto X) {
-            mfma_one(f1, X);
-            if constexpr (kNext) read_one(n0a, n0b, f0, X);
+        unroll<NX>([&](auto X) {
+            constexpr int x = decltype(X)::value;
+            if constexpr (x < NM) mfma_one(f1, X);
+            if constexpr (kNext && x < NR) read_one(n0a, n0b, f0, X);
             __builtin_amdgcn_sched_barrier(0);
         });
         flip();
     };
-    unroll<16>([&](auto X) { load_one(st0, X); });
-    unroll<16>([&](auto X) { store_one(lds0, kWideBuf + lds0, X); });
-    if (stages > 1) unroll<16>([&](auto X) { load_one(st0 + 1, X); });
+    unroll<NS>([&](auto X) { load_one(st0, X); });
+    unroll<NS>([&](auto X) { store_one(lds0, kWideBuf + lds0, X); });
+    if (stages > 1) unroll<NS>([&](auto X) { load_one(st0 + 1, X); });
     __syncthreads();
     {
         const int fa[2] = {frag_a(0, 0), frag_a(0, 1)}, fb[2] = {frag_b(0, 0), frag_b(0, 1)};
-        unroll<16>([&](auto X) { read_one(fa, fb, f0, X); });
+        unroll<NR>([&](auto X) { read_one(fa, fb, f0, X); });
     }
     int64_t s = 0;
     for (; s + 2 < stages; ++s) run_stage(s, yes{}, yes{}, yes{});  // steady state: stage s + 2 exists
@@ -751,15 +764,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     run_stage(s, no{}, no{}, no{});  // the last stage
     __syncthreads();  // every fragment read is retired before the epilogue reuses the LDS
 
-    const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
+    const int64_t wrow0 = m0 + wm * WR, wcol0 = n0 + wn * WC;
     if (to_partial) {
         typedef typename std::conditional<QT == kInt8, int32_t, float>::type part_t;
-        const int64_t n_lo = dp_tiles == 0 ? 0 : (int64_t)(dp_tiles / tiles_m) * kWideN, nb = n - n_lo;
+        const int64_t n_lo = dp_tiles == 0 ? 0 : (int64_t)(dp_tiles / tiles_m) * BN, nb = n - n_lo;
         part_t *P = static_cast<part_t *>(partial) + (int64_t)split * m * nb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < IA; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JB; ++j) {
                 const int64_t col = wcol0 + j * 32 + fr;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -771,20 +784,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
     }
 
     // epilogue: y = acc * x_scale[row] * w_scale[col]
-    float sw[4];
+    float sw[JB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JB; ++j) {
         const int64_t col = wcol0 + j * 32 + fr;
         sw[j] = ws[col < n ? col : n - 1];
     }
-    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + kWideN <= n;  // uniform per workgroup
+    const bool fast = y_bf16 && acc_out == nullptr && (n % 8) == 0 && n0 + BN <= n;  // uniform per workgroup
     if (fast) {
-        // the wavefront's 128 x 128 bf16 outputs go through its own 32 KiB of LDS (row stride 256 bytes; the last
-        // barrier of the loop has retired every fragment read), then out as 16-byte row pieces with buffer stores
-        // (rows past m fall outside the buffer and are dropped); a wavefront reads back only what it wrote
-        constexpr int kStride = 256;
-        uint8_t *stage = lds + wave * (128 * kStride);
-        unroll<4>([&](auto I) {
+        // the wavefront's WR x WC bf16 outputs go through its own WR x 2 WC bytes of LDS (the last barrier of the
+        // loop has retired every fragment read), then out as 16-byte row pieces with buffer stores (rows past m
+        // fall outside the buffer and are dropped); a wavefront reads back only what it wrote
+        constexpr int kStride = 2 * WC, kPieces = WC / 8;  // bytes and 16-byte pieces per staged row
+        uint8_t *stage = lds + wave * (WR * kStride);
+        unroll<IA>([&](auto I) {
             constexpr int i = decltype(I)::value;
             float sx[16];
 #pragma unroll
@@ -792,7 +805,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
                 const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
                 sx[e] = xs[row < m ? row : m - 1];
             }
-            unroll<4>([&](auto J) {
+            unroll<JB>([&](auto J) {
                 constexpr int j = decltype(J)::value;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -805,9 +818,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
         const __amdgpu_buffer_rsrc_t ry =
             __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)(m * n * 2), kBufferFlags);
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int c = lane + 64 * q;  // 16-byte piece: row c / 16, columns 8 (c % 16) ..
-            const int r = c >> 4, c8 = (c & 15) * 8;
+        for (int q = 0; q < WR * kPieces / 64; ++q) {
+            const int c = lane + 64 * q;  // 16-byte piece: row c / kPieces, columns 8 (c % kPieces) ..
+            const int r = c / kPieces, c8 = (c % kPieces) * 8;
             const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kStride + c8 * 2);
             const int64_t row = wrow0 + r;
             const uint32_t off = row < m ? (uint32_t)((row * n + wcol0 + c8) * 2) : kOutOfRange;
@@ -815,7 +828,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
         }
         return;
     }
-    unroll<4>([&](auto I) {
+    unroll<IA>([&](auto I) {
         constexpr int i = decltype(I)::value;
         float sx[16];
 #pragma unroll
@@ -823,7 +836,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
             const int64_t row = wrow0 + i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
             sx[e] = xs[row < m ? row : m - 1];
         }
-        unroll<4>([&](auto J) {
+        unroll<JB>([&](auto J) {
             constexpr int j = decltype(J)::value;
             const int64_t col = wcol0 + j * 32 + fr;
 #pragma unroll
@@ -917,21 +930,37 @@ hipError_t launch_wide(const GemmPlan &g, int64_t m, int64_t n, int64_t k, const
                        const uint8_t *wq, const float *ws, void *y, bool y_bf16, void *acc_out, void *workspace,
                        hipStream_t stream) {
     // more than 64 KiB of dynamic LDS per workgroup is opted into once per kernel
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wide_kernel<QT>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wide_kernel<QT, kWideN>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kWideBuf);
+    static const hipError_t attr_b = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemm_wide_kernel<QT, kWideBandN>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        2 * kWideBuf);
     if (attr != hipSuccess) return attr;
+    if (attr_b != hipSuccess) return attr_b;
     if (k % kWideK != 0) return hipErrorInvalidValue;  // the kernel's loads take whole 128-byte stages
-    const int tiles_m = (int)((m + kWideM - 1) / kWideM), tiles_n = (int)((n + kWideN - 1) / kWideN);
-    int grid;
-    if (g.dp_tiles == 0) {
-        grid = ((tiles_m * tiles_n * g.splits + 7) / 8) * 8;
-    } else {
-        const int pieces = (tiles_m * tiles_n - g.dp_tiles) * g.splits;
-        grid = 8 * (g.dp_tiles / 8 + (pieces + 7) / 8);
+    const int tiles_m = (int)((m + kWideM - 1) / kWideM);
+    const int64_t n_main = g.band ? g.band_n0 : n;  // columns of the 256-wide tiles
+    if (g.band && (g.splits != 1 || g.dp_tiles != 0 || n_main % kWideN != 0)) return hipErrorInvalidValue;
+    const int tiles_n = (int)((n_main + kWideN - 1) / kWideN);
+    if (tiles_n > 0) {
+        int grid;
+        if (g.dp_tiles == 0) {
+            grid = ((tiles_m * tiles_n * g.splits + 7) / 8) * 8;
+        } else {
+            const int pieces = (tiles_m * tiles_n - g.dp_tiles) * g.splits;
+            grid = 8 * (g.dp_tiles / 8 + (pieces + 7) / 8);
+        }
+        hipLaunchKernelGGL((gemm_wide_kernel<QT, kWideN>), dim3(grid), dim3(kWideThreads), 2 * kWideBuf, stream, m, n,
+                           k, xq, xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits,
+                           g.stages_per_split, workspace, g.dp_tiles, (int64_t)0);
     }
-    hipLaunchKernelGGL((gemm_wide_kernel<QT>), dim3(grid), dim3(kWideThreads), 2 * kWideBuf, stream, m, n, k, xq,
-                       xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_n, g.splits, g.stages_per_split,
-                       workspace, g.dp_tiles);
+    if (g.band) {  // the remaining columns as one round of 256 x kWideBandN tiles over all of K
+        const int tiles_b = (int)((n - n_main + kWideBandN - 1) / kWideBandN);
+        const int grid = ((tiles_m * tiles_b + 7) / 8) * 8;
+        hipLaunchKernelGGL((gemm_wide_kernel<QT, kWideBandN>), dim3(grid), dim3(kWideThreads), 2 * kWideBuf, stream,
+                           m, n, k, xq, xs, wq, ws, y, y_bf16 ? 1 : 0, acc_out, tiles_m, tiles_b, 1,
+                           (int)((k + kWideK - 1) / kWideK), workspace, 0, n_main);
+    }
     if (g.splits > 1)
         launch_splitk_reduce(QT, m, n, g.splits, workspace, xs, ws, y, y_bf16, acc_out, stream, g.n_lo);
     return hipGetLastError();
@@ -1084,6 +1113,34 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
                     g.dp_tiles = (int)dp;
                     g.n_lo = n_lo;
                 }
+            }
+        }
+    }
+    // The wide kernel over all of K in whole rounds of 256-wide tiles, then the remaining columns as one round of
+    // 256 x 160 tiles in a second launch (the columns from band_n0). The cost model takes a band round at 0.7 of
+    // a full one, fitted on MI355X (7B FP8, graph replay, weights past the caches: gate/up at m = 2048 254 ->
+    // 251 us, qkv 42.0 -> 40.5, o 36.2 (ring) -> 32.9, gate/up at m = 512 90.7 (split band) -> 87.2; the
+    // deep-K down and the few-tile qkv and o at m = 512 stay on their plans).
+    const int fband = env_int("QR_GEMM_BAND", -1);  // -1 by the cost model, 0 never, 1 wherever it applies
+    const bool band_forced_off = fband == 0 || fs > 1 || fh >= 2 || (forced >= 0 && forced != kGemmWide) ||
+                                 (fbn != 0 && fbn != kWideN) || (fbm != 0 && fbm != kWideM);
+    if (!band_forced_off && (m > 128 || fband == 1) && k % kWideK == 0) {
+        const int64_t tm = (m + kWideM - 1) / kWideM, tiles = count(kWideM, kWideN);
+        if (tiles % round != 0 && round % tm == 0) {
+            const int64_t n0b = tiles / round * round / tm * kWideN;
+            const int64_t band_tiles = tm * ((n - n0b + kWideBandN - 1) / kWideBandN);
+            const int64_t wstages = (k + kWideK - 1) / kWideK;
+            const double c = 0.83 * (double)kWideK / 64.0 * (double)wstages;  // one round of 256-wide tiles
+            const double t = (double)(tiles / round) * c + 0.7 * c;
+            if (n0b < n && band_tiles <= round && (fband == 1 || t < best)) {
+                g = GemmPlan{};
+                g.tile = kGemmWide;
+                g.bm = kWideM;
+                g.bn = kWideN;
+                g.splits = 1;
+                g.stages_per_split = (int)wstages;
+                g.band = true;
+                g.band_n0 = n0b;
             }
         }
     }

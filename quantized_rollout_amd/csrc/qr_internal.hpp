@@ -38,6 +38,8 @@ struct GemmPlan {
     int dp_tiles;          // ring: > 0: the first dp_tiles tiles (whole CU rounds) run over all of K and only the
                            // remaining tiles, a band of output columns from n_lo, are split; 0: every tile alike
     int64_t n_lo;          // ring: first column of the split band (0 unless dp_tiles > 0)
+    bool band;             // wide kernel over all of K: columns from band_n0 run as 256 x 160 tiles, a second launch
+    int64_t band_n0;
     size_t ws_bytes;       // splits x m x (n - n_lo) x 4 when split, else 0
 };
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k);

@@ -333,6 +333,39 @@ def test_gemm_whole_tiles_then_split_band(tile, m, n, k, bm, bn, splits, dp, mon
             assert np.array_equal(host(y), y_acc), (what, rep)
 
 
+# The wide kernel over all of K with the columns past whole rounds of 256-wide tiles run as a band of 256 x 160
+# tiles in a second launch, forced on with a round of 8 tiles: (m, n, k, first band column or -1 for none).
+# 2 x 11 tiles: two rounds, then a band of 552 columns (a partial last band tile); 1 x 2 and 2 x 2 tiles: the band
+# alone (ragged rows, 512 = 3 x 160 + 32 columns, a one-stage K); 1 x 2 tiles with a deep K and 333 columns
+# (the element-wise epilogue); 2 x 3 tiles, whose band would need 10 tiles: none.
+BAND_CASES = [(300, 2600, 1024, 2048), (65, 264, 128, 0), (300, 512, 1024, 0), (130, 333, 4096, 0),
+              (512, 768, 2048, -1)]
+
+
+@pytest.mark.parametrize("m,n,k,band", BAND_CASES)
+def test_wide_kernel_band_of_narrow_tiles(m, n, k, band, monkeypatch, capfd):
+    monkeypatch.setenv("QR_GEMM_TILE", "4")
+    monkeypatch.setenv("QR_GEMM_SPLITS", "1")
+    monkeypatch.setenv("QR_GEMM_BAND", "1")
+    monkeypatch.setenv("QR_GEMM_ROUND", "8")
+    monkeypatch.setenv("QR_TRACE", "1")
+    wsp = qr.Workspace()
+    for oq in (O.INT8, O.FP8):
+        xc, xs, wc, ws = _quantized_operands(m, n, k, oq, seed=1900 + m + n + oq)
+        what = "wide band %s m=%d n=%d k=%d" % (oq, m, n, k)
+        log(what)
+        _check(oq, xc, xs, wc, ws, what)
+        err = capfd.readouterr().err
+        assert "gemm=4 " in err and "band=%d\n" % band in err, err
+        y_ref, _, _ = O.linear(oq, xc, xs, wc, ws, O.BF16)
+        y_acc, _ = _run(oq, xc, xs, wc, ws)
+        y = qr.qr_w8a8_linear(GQ[oq], dev(xc), dev(xs), dev(wc), dev(ws), workspace=wsp)
+        torch.cuda.synchronize()
+        y = host(y)
+        assert_y_close(y, y_ref, what + " (no accumulators)")
+        assert np.array_equal(y, y_acc), what
+
+
 def test_workspace_reuse_across_plans():
     """One workspace object serves a sequence of differently planned shapes: every call stays bit-exact (INT8)
     or within tolerance (FP8)."""
