@@ -536,7 +536,8 @@ __global__ __launch_bounds__((Ring<BM, BN>::kThreads), 1) void gemm_ring_kernel(
 // outputs each (4 x 4 fragments of the 32x32 MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit
 // block scales, or two v_mfma_i32_32x32x32_i8), 256 accumulators per lane. A wavefront's fragments of one
 // 64-byte K step are 8 reads of 2 KiB for 16 MFMAs, half of what the ring kernel's 64 x 64 wavefronts read per
-// MFMA, so the LDS carries less per operation.
+// MFMA, so the LDS carries less per operation. A second form (BN = 160, four wavefronts of 64 x 160 outputs) runs
+// the columns past whole CU rounds of 256-wide tiles as one more round of narrower tiles, in a second launch.
 // K (a multiple of 128 bytes) advances in 128-byte stages through two LDS buffers. Every thread loads its
 // 16-byte pieces of stage s + 1 into registers (raw buffer loads: rows past m or n read as zero) while the MFMAs
 // of stage s run, and writes them to the other buffer before the stage's barrier. A buffer holds the stage's 256
