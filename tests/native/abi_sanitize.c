@@ -101,7 +101,9 @@ static void injected_launches(void) {
     CHECK(injected(qr_w8a8_linear(QR_INT8, 2048, 37888, 3584, x, xs, w, wsc, y, QR_BF16, o, ws, BIG, NULL)));
     CHECK(injected(qr_w8a8_linear_noalloc(QR_INT8, 16, 1536, 1536, x, xs, w, wsc, y, QR_BF16, NULL, NULL)));
     CHECK(injected(qr_w8a8_linear_noalloc(QR_INT8, 512, 3584, 18944, x, xs, w, wsc, y, QR_BF16, NULL, NULL)));
-    CHECK(injected(qr_w8a8_linear_bf16(QR_INT8, 1, 3584, 3584, x, NULL, w, wsc, y, QR_BF16, NULL, NULL, 0, NULL)));
+    /* one launch with the quantization inside the GEMV (few workgroups: no workspace), then the two-launch form */
+    CHECK(injected(qr_w8a8_linear_bf16(QR_INT8, 1, 2048, 1536, x, NULL, w, wsc, y, QR_BF16, NULL, NULL, 0, NULL)));
+    CHECK(injected(qr_w8a8_linear_bf16(QR_INT8, 1, 3584, 3584, x, NULL, w, wsc, y, QR_BF16, NULL, ws, BIG, NULL)));
     CHECK(injected(qr_w8a8_linear_bf16(QR_FP8_E4M3, 64, 1536, 8960, x, NULL, w, wsc, y, QR_F32, NULL, ws, BIG, NULL)));
     CHECK(injected(qr_w8a8_grouped_linear(QR_FP8_E4M3, 8, 256, 512, (const int32_t *)PTR(7), (const int32_t *)PTR(8),
                                           64, 32, x, xs, w, wsc, y, QR_BF16, ws, BIG, NULL)));
