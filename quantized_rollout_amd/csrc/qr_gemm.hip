@@ -879,11 +879,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n
     for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC; base < total; base += stride) {
         part_t a[VEC];
         if constexpr (VEC == 4) {
-            typedef typename std::conditional<QT == kInt8, int4, float4>::type vec_t;
-            vec_t v = *reinterpret_cast<const vec_t *>(P + base);
+            typedef part_t vec_t __attribute__((ext_vector_type(4)));
+            auto ld = [&](int sp) {  // read once: non-temporal
+                return __builtin_nontemporal_load(reinterpret_cast<const vec_t *>(P + (int64_t)sp * total + base));
+            };
+            vec_t v = ld(0);
             a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
-            for (int sp = 1; sp < splits; ++sp) {
-                v = *reinterpret_cast<const vec_t *>(P + (int64_t)sp * total + base);
+            int sp = 1;
+            for (; sp + 4 <= splits; sp += 4) {  // four loads in flight, then added in split order
+                const vec_t v1 = ld(sp), v2 = ld(sp + 1), v3 = ld(sp + 2), v4 = ld(sp + 3);
+                a[0] += v1.x; a[1] += v1.y; a[2] += v1.z; a[3] += v1.w;
+                a[0] += v2.x; a[1] += v2.y; a[2] += v2.z; a[3] += v2.w;
+                a[0] += v3.x; a[1] += v3.y; a[2] += v3.z; a[3] += v3.w;
+                a[0] += v4.x; a[1] += v4.y; a[2] += v4.z; a[3] += v4.w;
+            }
+            for (; sp < splits; ++sp) {
+                v = ld(sp);
                 a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
             }
         } else {
@@ -892,15 +903,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n
         }
         const int64_t row = base / nb, col = n_lo + (base - row * nb);
         const float sx = xs[row];
+        float v[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int64_t idx = row * n + col + e;
-            const float v = acc_to_f32(a[e]) * sx * ws[col + e];
+        for (int e = 0; e < VEC; ++e) v[e] = acc_to_f32(a[e]) * sx * ws[col + e];
+        const int64_t idx = row * n + col;
+        if constexpr (VEC == 4) {
+            // n and col are multiples of 4 here (nb and n_lo are), so one 8- or 16-byte store per output type
+            if (y_bf16) {
+                const uint2 o = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                 (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + idx) = o;
+            } else {
+                *reinterpret_cast<float4 *>(static_cast<float *>(y) + idx) = float4{v[0], v[1], v[2], v[3]};
+            }
+            if (acc_out != nullptr) {
+                typedef part_t vec_t __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<vec_t *>(static_cast<part_t *>(acc_out) + idx) = vec_t{a[0], a[1], a[2], a[3]};
+            }
+        } else {
             if (y_bf16)
-                static_cast<uint16_t *>(y)[idx] = f32_to_bf16(v);
+                static_cast<uint16_t *>(y)[idx] = f32_to_bf16(v[0]);
             else
-                static_cast<float *>(y)[idx] = v;
-            if (acc_out != nullptr) static_cast<part_t *>(acc_out)[idx] = a[e];
+                static_cast<float *>(y)[idx] = v[0];
+            if (acc_out != nullptr) static_cast<part_t *>(acc_out)[idx] = a[0];
         }
     }
 }
@@ -1154,7 +1179,7 @@ void launch_splitk_reduce(int qtype, int64_t m, int64_t n, int splits, const voi
     const int64_t total_out = m * (n - n_lo);
     const bool vec = ((n - n_lo) % 4) == 0;
     const int64_t items = vec ? total_out / 4 : total_out;
-    const int blocks = (int)std::min<int64_t>((items + 255) / 256, 4096);
+    const int blocks = (int)std::min<int64_t>((items + 255) / 256, 65536);  // about one item per thread
 #define QR_REDUCE(QT, V)                                                                                       \
     hipLaunchKernelGGL((splitk_reduce_kernel<QT, V>), dim3(blocks), dim3(256), 0, stream, m, n, n_lo, splits, partial, \
                        xs, ws, y, y_bf16 ? 1 : 0, acc_out)
