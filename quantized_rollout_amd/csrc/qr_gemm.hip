@@ -1147,10 +1147,14 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
     // a full one, fitted on MI355X (7B FP8, graph replay, weights past the caches: gate/up at m = 2048 254 ->
     // 251 us, qkv 42.0 -> 40.5, o 36.2 (ring) -> 32.9, gate/up at m = 512 90.7 (split band) -> 87.2; the
     // deep-K down and the few-tile qkv and o at m = 512 stay on their plans).
+    // At 64 < m <= 128 (one token tile, the ring kernel's 128-row tiles otherwise) only a band that fills at
+    // least three quarters of a round over a K of at least 2048 bytes, where the cost model's factor does not
+    // hold (7B gate/up at m = 128, FP8: 45.2 -> 41.4 us, INT8 47 -> 44; the 1.5B gate/up, 112 band tiles over
+    // K = 1536: 15.1 -> 18.6, not taken).
     const int fband = env_int("QR_GEMM_BAND", -1);  // -1 by the cost model, 0 never, 1 wherever it applies
     const bool band_forced_off = fband == 0 || fs > 1 || fh >= 2 || (forced >= 0 && forced != kGemmWide) ||
                                  (fbn != 0 && fbn != kWideN) || (fbm != 0 && fbm != kWideM);
-    if (!band_forced_off && (m > 128 || fband == 1) && k % kWideK == 0) {
+    if (!band_forced_off && (m > 64 || fband == 1) && k % kWideK == 0) {
         const int64_t tm = (m + kWideM - 1) / kWideM, tiles = count(kWideM, kWideN);
         if (tiles % round != 0 && round % tm == 0) {
             const int64_t n0b = tiles / round * round / tm * kWideN;
@@ -1158,7 +1162,8 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
             const int64_t wstages = (k + kWideK - 1) / kWideK;
             const double c = 0.83 * (double)kWideK / 64.0 * (double)wstages;  // one round of 256-wide tiles
             const double t = (double)(tiles / round) * c + 0.7 * c;
-            if (n0b < n && band_tiles <= round && (fband == 1 || t < best)) {
+            const bool small_ok = m > 128 || (4 * band_tiles >= 3 * round && k >= 2048);
+            if (n0b < n && band_tiles <= round && (fband == 1 || (small_ok && t < best))) {
                 g = GemmPlan{};
                 g.tile = kGemmWide;
                 g.bm = kWideM;

@@ -366,6 +366,28 @@ def test_wide_kernel_band_of_narrow_tiles(m, n, k, band, monkeypatch, capfd):
         assert np.array_equal(y, y_acc), what
 
 
+# The planner's band at one token tile (64 < m <= 128): taken only where the 256 x 160 tiles fill at least three
+# quarters of a round over a K of at least 2048 bytes (the 7B gate/up: 237 tiles), not for the 1.5B gate/up
+# (112 tiles, K = 1536) or the 7B down (23 tiles); (m, n, k, first band column or -1).
+@pytest.mark.parametrize("m,n,k,band", [(128, 37888, 3584, 0), (96, 37888, 3584, 0), (128, 17920, 1536, -1),
+                                        (128, 3584, 18944, -1)])
+def test_band_plan_at_one_token_tile(m, n, k, band, monkeypatch, capfd):
+    monkeypatch.setenv("QR_TRACE", "1")
+    q = qr.QR_FP8_E4M3
+    log("band plan m=%d n=%d k=%d" % (m, n, k))
+    x = torch.zeros((m, k), dtype=torch.uint8, device="cuda")  # zero codes: only the plan is checked here
+    xs = torch.ones(m, device="cuda")
+    w = torch.zeros((n, k), dtype=torch.uint8, device="cuda")
+    wsc = torch.ones(n, device="cuda")
+    y = qr.qr_w8a8_linear(q, x, xs, w, wsc)
+    torch.cuda.synchronize()
+    assert not bool(y.float().abs().max() > 0)
+    err = capfd.readouterr().err
+    assert "kind=1" in err and ("band=%d\n" % band) in err, err
+    if band >= 0:
+        assert "gemm=4 " in err, err
+
+
 def test_workspace_reuse_across_plans():
     """One workspace object serves a sequence of differently planned shapes: every call stays bit-exact (INT8)
     or within tolerance (FP8)."""
