@@ -29,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> bfloat16 bits in one hardware conversion (v_cvt_pk_bf16_f32: round to nearest even, the same bits
+// as f32_to_bf16 for finite values): a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, b2_t));
+}
+
 // double -> bfloat16 bits with one rounding (nearest even). The conversion to fp32 is made round-to-odd
 // (truncate, then set the last bit when inexact); rounding that 24-bit value to nearest even at 8 bits then
 // equals the direct rounding because 24 >= 8 + 2 (S. Boldo, G. Melquiond, "Emulation of FMA and correctly

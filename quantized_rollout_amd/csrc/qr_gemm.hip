@@ -479,10 +479,13 @@ __global__ __launch_bounds__((Ring<BM, BN>::kThreads), 1) void gemm_ring_kernel(
             unroll<2>([&](auto J) {
                 constexpr int j = decltype(J)::value;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
+                for (int e = 0; e < 16; e += 2) {  // rows r and r + 1 of the lane's column, one conversion
                     const int r = i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
-                    const float v = acc_to_f32(acc[i][j][e]) * sx[e] * sw[j];
-                    *reinterpret_cast<uint16_t *>(stage + r * kStride + (j * 32 + fr) * 2) = f32_to_bf16(v);
+                    const uint32_t p = f32x2_to_bf16x2(acc_to_f32(acc[i][j][e]) * sx[e] * sw[j],
+                                                       acc_to_f32(acc[i][j][e + 1]) * sx[e + 1] * sw[j]);
+                    uint8_t *q = stage + r * kStride + (j * 32 + fr) * 2;
+                    *reinterpret_cast<uint16_t *>(q) = (uint16_t)p;
+                    *reinterpret_cast<uint16_t *>(q + kStride) = (uint16_t)(p >> 16);
                 }
             });
         });
@@ -809,10 +812,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void gemm_wide_kernel(
             unroll<JB>([&](auto J) {
                 constexpr int j = decltype(J)::value;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
+                for (int e = 0; e < 16; e += 2) {  // rows r and r + 1 of the lane's column, one conversion
                     const int r = i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
-                    const float v = acc_to_f32(acc[i][j][e]) * sx[e] * sw[j];
-                    *reinterpret_cast<uint16_t *>(stage + r * kStride + (j * 32 + fr) * 2) = f32_to_bf16(v);
+                    const uint32_t p = f32x2_to_bf16x2(acc_to_f32(acc[i][j][e]) * sx[e] * sw[j],
+                                                       acc_to_f32(acc[i][j][e + 1]) * sx[e + 1] * sw[j]);
+                    uint8_t *q = stage + r * kStride + (j * 32 + fr) * 2;
+                    *reinterpret_cast<uint16_t *>(q) = (uint16_t)p;
+                    *reinterpret_cast<uint16_t *>(q + kStride) = (uint16_t)(p >> 16);
                 }
             });
         });
@@ -910,8 +916,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t m, int64_t n
         if constexpr (VEC == 4) {
             // n and col are multiples of 4 here (nb and n_lo are), so one 8- or 16-byte store per output type
             if (y_bf16) {
-                const uint2 o = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                                 (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+                const uint2 o = {f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])};
                 *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + idx) = o;
             } else {
                 *reinterpret_cast<float4 *>(static_cast<float *>(y) + idx) = float4{v[0], v[1], v[2], v[3]};
