@@ -857,12 +857,19 @@ def main():
     ap.add_argument("--profile-reps", type=int, default=3)
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the markdown summary of the two counter runs of --profile-kernel NAME and exit")
-    ap.add_argument("--traffic-command", default="", help="the command lines recorded in that summary")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command lines recorded in that summary (default: the two counter runs and this one, "
+                    "with the given directories)")
     args = ap.parse_args()
 
     if args.traffic_summary:
-        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.profile_kernel,
-                              args.profile_reps, args.traffic_command))
+        fdir, wdir = args.traffic_summary
+        run = "python3 bench.py --profile-kernel %s --profile-reps %d" % (args.profile_kernel, args.profile_reps)
+        command = args.traffic_command or "\n".join([
+            "rocprofv3 --pmc FETCH_SIZE -d %s -o t --output-format csv -- %s" % (fdir, run),
+            "rocprofv3 --pmc WRITE_SIZE -d %s -o t --output-format csv -- %s" % (wdir, run),
+            "%s --traffic-summary %s %s" % (run, fdir, wdir)])
+        print(traffic_summary(fdir, wdir, args.profile_kernel, args.profile_reps, command))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
