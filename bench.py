@@ -65,6 +65,7 @@ PROFILE_KERNELS = {
     "a3_fp8_gate_up_m16": ("fp8", 16, 37888, 3584),
     "a3_fp8_down_m1": ("fp8", 1, 3584, 18944),
     "a3_fp8_down_m16": ("fp8", 16, 3584, 18944),
+    "a3_int8_gate_up_1p5b_m64": ("int8", 64, 17920, 1536),
 }
 
 
